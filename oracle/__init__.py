@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for the selective-scan hot path -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The GPU library never calls it and shares no
+code with it.  The arithmetic lives in ``oracle.c`` (plain sequential C, fp64);
+this module only builds it with gcc and marshals numpy arrays through ctypes.
+
+Every function here takes and returns float64 numpy arrays in the layouts
+documented in ``oracle.c``:
+  x, dt, z, y [B, D, L];  Bm, Cm [B, L, N];  A [D, N];  dt_bias, Dskip [D];
+  h0, h_last [B, D, N];  conv w [D, K].
+Parity status: every function is pinned by tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+
+def compile_oracle(src: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile an oracle C source with gcc (IEEE fp64, no fast-math)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+         "-o", tmp, src, "-lm", "-lpthread"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(LIBRARY):
+        compile_oracle()
+    return LIBRARY
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_softplus.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_zoh.restype = None
+        lib.oracle_zoh.argtypes = [ctypes.c_double, ctypes.c_double, P, P]
+        lib.oracle_selective_scan_fwd.restype = ctypes.c_int
+        lib.oracle_selective_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int]
+        lib.oracle_conv1d_silu.restype = ctypes.c_int
+        lib.oracle_conv1d_silu.argtypes = [P] * 4 + [I64] * 4 + [ctypes.c_int]
+        lib.oracle_state_update.restype = ctypes.c_int
+        lib.oracle_state_update.argtypes = [P] * 10 + [I64] * 3
+        self.lib = lib
+        self.path = path
+
+    def softplus(self, v: float) -> float:
+        return self.lib.oracle_softplus(float(v))
+
+    def silu(self, v: float) -> float:
+        return self.lib.oracle_silu(float(v))
+
+    def zoh(self, delta: float, a: float):
+        """Return (Abar, bcoef) with Bbar = bcoef * B for one diagonal entry."""
+        ab = ctypes.c_double()
+        bc = ctypes.c_double()
+        self.lib.oracle_zoh(float(delta), float(a), ctypes.byref(ab), ctypes.byref(bc))
+        return ab.value, bc.value
+
+    def selective_scan(self, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+                       nthreads: int = 1):
+        """Selective scan forward.  Returns (y [B,D,L], h_last [B,D,N])."""
+        x, dt, A, Bm, Cm = map(_f64, (x, dt, A, Bm, Cm))
+        dt_bias, Dskip, z, h0 = map(_f64, (dt_bias, Dskip, z, h0))
+        Bsz, D, L = x.shape
+        N = A.shape[1]
+        assert dt.shape == x.shape and A.shape == (D, N)
+        assert Bm.shape == (Bsz, L, N) and Cm.shape == (Bsz, L, N)
+        assert z is None or z.shape == x.shape
+        assert h0 is None or h0.shape == (Bsz, D, N)
+        assert dt_bias is None or dt_bias.shape == (D,)
+        assert Dskip is None or Dskip.shape == (D,)
+        y = np.empty((Bsz, D, L), dtype=np.float64)
+        h_last = np.empty((Bsz, D, N), dtype=np.float64)
+        rc = self.lib.oracle_selective_scan_fwd(
+            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+            _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), Bsz, D, L, N, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_selective_scan_fwd rejected its arguments")
+        return y, h_last
+
+    def conv1d_silu(self, x, w, bias=None, apply_silu: bool = True):
+        """Causal depthwise conv1d (+ SiLU).  x [B,D,L], w [D,K] -> [B,D,L]."""
+        x, w, bias = _f64(x), _f64(w), _f64(bias)
+        Bsz, D, L = x.shape
+        K = w.shape[1]
+        assert w.shape[0] == D and (bias is None or bias.shape == (D,))
+        out = np.empty_like(x)
+        rc = self.lib.oracle_conv1d_silu(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), Bsz, D, L,
+                                         K, 1 if apply_silu else 0)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_silu rejected its arguments")
+        return out
+
+    def state_update(self, h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None):
+        """One decode step.  h [B,D,N] (not modified), x/dt/z [B,D], Bm/Cm [B,N].
+        Returns (y [B,D], h_new [B,D,N])."""
+        h = np.array(h, dtype=np.float64, copy=True, order="C")
+        x, dt, A, Bm, Cm = map(_f64, (x, dt, A, Bm, Cm))
+        dt_bias, Dskip, z = map(_f64, (dt_bias, Dskip, z))
+        Bsz, D, N = h.shape
+        assert x.shape == (Bsz, D) and dt.shape == (Bsz, D) and A.shape == (D, N)
+        assert Bm.shape == (Bsz, N) and Cm.shape == (Bsz, N)
+        y = np.empty((Bsz, D), dtype=np.float64)
+        rc = self.lib.oracle_state_update(_ptr(h), _ptr(x), _ptr(dt), _ptr(dt_bias),
+                                          _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+                                          _ptr(y), Bsz, D, N)
+        if rc != 0:
+            raise ValueError("oracle_state_update rejected its arguments")
+        return y, h
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The oracle built from oracle.c (compiled on first use if missing)."""
+    global _default
+    if _default is None:
+        build(force=False)
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def softplus(v):
+    return get().softplus(v)
+
+
+def silu(v):
+    return get().silu(v)
+
+
+def zoh(delta, a):
+    return get().zoh(delta, a)
+
+
+def selective_scan(*args, **kw):
+    return get().selective_scan(*args, **kw)
+
+
+def conv1d_silu(*args, **kw):
+    return get().conv1d_silu(*args, **kw)
+
+
+def state_update(*args, **kw):
+    return get().state_update(*args, **kw)

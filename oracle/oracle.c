@@ -1,0 +1,229 @@
+/*
+ * Reference oracle for the selective state-space hot path — TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, sequential fp64 C.  It exists only to check the HIP library:
+ * only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load or run it.  It shares no code, header, table or constant with the
+ * GPU library, and the GPU library never calls it.
+ *
+ * What it computes, and where each step comes from (sources are the web
+ * pages this project is built from, cited by title and section):
+ *
+ *  - Continuous SSM  h'(t) = A h(t) + B u(t),  y(t) = C h(t) + D u(t)
+ *      ["Mamba: Linear-Time Sequence Modeling with Selective SSMs", section
+ *       "连续与离散SSM"; "Mamba架构与SSM模型：高效序列建模技术解析", §2.1].
+ *  - Zero-order-hold discretisation with step Δ:
+ *      Abar = exp(Δ A),   Bbar = (Δ A)^-1 (exp(Δ A) - I) Δ B
+ *      ["Mamba架构与SSM模型：高效序列建模技术解析", §2.1].
+ *    A is diagonal here (one scalar a per state n), so per state
+ *      Abar_n = exp(Δ a_n),  Bbar_n = expm1(Δ a_n) / a_n * B_n,
+ *    and at a_n = 0 the limit Bbar_n = Δ B_n.
+ *  - Input-dependent step  Δ = softplus(dt + dt_bias)
+ *      ["Mamba架构与SSM模型：高效序列建模技术解析", §2.2].
+ *  - Selective (time-varying) recurrence  h_t = Abar_t h_{t-1} + Bbar_t x_t,
+ *    readout  y_t = <C_t, h_t>  taken AFTER x_t has entered the state
+ *      ["Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式",
+ *       §2.1 (selective SSM pseudo-code, where Δ, B and C depend on the token)].
+ *  - Skip D x_t and the multiplicative SiLU gate of the block:
+ *      out_t = (y_t + D x_t) * z_t * sigmoid(z_t)
+ *      [same page, §3.1 block diagram: SiLU activation with multiplicative
+ *       gating around the selective SSM].
+ *  - Causal depthwise conv1d (kernel 4) + SiLU in front of the SSM
+ *      [same page, §3.1 (causal Conv1D); "Mamba架构与SSM模型：高效序列建模技术解析",
+ *       §3.2 (d_conv=4)].  Taps follow the usual cross-correlation order:
+ *      pre_t = bias + sum_{k<K} w[k] x[t-(K-1)+k], with x[t<0] = 0.
+ *  - Decode: one step of the same recurrence on a stored state
+ *      ["Mamba架构深度剖析：如何以线性时间重塑序列建模", §3: fixed-size state,
+ *       step-by-step prediction at inference].
+ *
+ * Layouts (all row-major, fp64):
+ *   x, dt, z, y : [B, D, L]      (L fastest)
+ *   Bm, Cm      : [B, L, N]      (shared by every channel d of batch b)
+ *   A           : [D, N];  dt_bias, Dskip : [D];  h0, h_last : [B, D, N]
+ *   conv w      : [D, K];  conv bias : [D]
+ *   decode      : h [B, D, N] in/out, x/dt/z/y [B, D], Bm/Cm [B, N]
+ * NULL for dt_bias / Dskip / z / h0 / h_last / conv bias means "absent"
+ * (zero bias, no skip, no gate, zero initial state, state not returned).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* softplus(v) = log(1 + e^v), evaluated without overflow. */
+double oracle_softplus(double v)
+{
+    if (v > 0.0)
+        return v + log1p(exp(-v));
+    return log1p(exp(v));
+}
+
+/* z * sigmoid(z) */
+double oracle_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* ZOH for one diagonal entry a with step delta:
+ *   *abar = exp(delta a),  *bcoef = (exp(delta a) - 1) / a  (so Bbar = bcoef * B),
+ * with the a = 0 limit bcoef = delta. */
+void oracle_zoh(double delta, double a, double *abar, double *bcoef)
+{
+    *abar = exp(delta * a);
+    if (a == 0.0)
+        *bcoef = delta;
+    else
+        *bcoef = expm1(delta * a) / a;
+}
+
+/* One time step for one channel: h (length N) is updated in place and the
+ * gated output is returned.  Bt, Ct point at this step's N values. */
+static double step(int64_t N, double *h, double xv, double dtv, double bias,
+                   const double *A, const double *Bt, const double *Ct,
+                   double Dv, const double *zv)
+{
+    double delta = oracle_softplus(dtv + bias);
+    double y = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double abar, bcoef;
+        oracle_zoh(delta, A[n], &abar, &bcoef);
+        h[n] = abar * h[n] + bcoef * Bt[n] * xv;
+    }
+    for (int64_t n = 0; n < N; ++n)
+        y += Ct[n] * h[n];
+    y += Dv * xv;
+    if (zv)
+        y *= oracle_silu(*zv);
+    return y;
+}
+
+/* Scan of one channel over L steps.
+ * x, dt, z, y: L values with unit stride.  Bm, Cm: L rows of N values with
+ * row stride ldbc.  A, h0, h_last: N values. */
+void oracle_scan_channel(int64_t L, int64_t N, const double *x, const double *dt,
+                         double dt_bias, const double *A, const double *Bm,
+                         const double *Cm, int64_t ldbc, double Dv, const double *z,
+                         const double *h0, double *y, double *h_last)
+{
+    double h[64];
+    for (int64_t n = 0; n < N; ++n)
+        h[n] = h0 ? h0[n] : 0.0;
+    for (int64_t t = 0; t < L; ++t)
+        y[t] = step(N, h, x[t], dt[t], dt_bias, A, Bm + t * ldbc, Cm + t * ldbc, Dv,
+                    z ? z + t : NULL);
+    if (h_last)
+        for (int64_t n = 0; n < N; ++n)
+            h_last[n] = h[n];
+}
+
+typedef struct {
+    const double *x, *dt, *dt_bias, *A, *Bm, *Cm, *Dskip, *z, *h0;
+    double *y, *h_last;
+    int64_t B, D, L, N;
+    int64_t first, last; /* channel range [first, last) over b*D + d */
+} scan_job;
+
+static void *scan_worker(void *arg)
+{
+    const scan_job *j = (const scan_job *)arg;
+    for (int64_t c = j->first; c < j->last; ++c) {
+        int64_t b = c / j->D, d = c % j->D;
+        size_t row = (size_t)c * (size_t)j->L;
+        oracle_scan_channel(j->L, j->N, j->x + row, j->dt + row,
+                            j->dt_bias ? j->dt_bias[d] : 0.0, j->A + d * j->N,
+                            j->Bm + (size_t)b * j->L * j->N, j->Cm + (size_t)b * j->L * j->N,
+                            j->N, j->Dskip ? j->Dskip[d] : 0.0, j->z ? j->z + row : NULL,
+                            j->h0 ? j->h0 + (size_t)c * j->N : NULL, j->y + row,
+                            j->h_last ? j->h_last + (size_t)c * j->N : NULL);
+    }
+    return NULL;
+}
+
+/* Whole-tensor selective scan.  Channels are independent sequences, so they
+ * may be spread over nthreads POSIX threads; the arithmetic of each channel is
+ * the same sequential loop either way.  Returns 0, or -1 on bad arguments. */
+int oracle_selective_scan_fwd(const double *x, const double *dt, const double *dt_bias,
+                              const double *A, const double *Bm, const double *Cm,
+                              const double *Dskip, const double *z, const double *h0,
+                              double *y, double *h_last, int64_t B, int64_t D, int64_t L,
+                              int64_t N, int nthreads)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !y || B < 0 || D < 0 || L < 0 || N < 1 || N > 64)
+        return -1;
+    int64_t nch = B * D;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nch < nthreads)
+        nthreads = nch > 0 ? (int)nch : 1;
+    scan_job jobs[256];
+    pthread_t tids[256];
+    for (int i = 0; i < nthreads; ++i) {
+        scan_job j = {x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, h_last, B, D, L, N,
+                      nch * i / nthreads, nch * (i + 1) / nthreads};
+        jobs[i] = j;
+    }
+    if (nthreads == 1) {
+        scan_worker(&jobs[0]);
+        return 0;
+    }
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tids[i], NULL, scan_worker, &jobs[i]) != 0) {
+            scan_worker(&jobs[i]);
+            tids[i] = 0;
+        } else {
+            started++;
+        }
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (tids[i])
+            pthread_join(tids[i], NULL);
+    (void)started;
+    return 0;
+}
+
+/* Causal depthwise conv1d over L with K taps, optional bias, then SiLU
+ * (apply_silu != 0) or identity. */
+int oracle_conv1d_silu(const double *x, const double *w, const double *bias, double *out,
+                       int64_t B, int64_t D, int64_t L, int64_t K, int apply_silu)
+{
+    if (!x || !w || !out || B < 0 || D < 0 || L < 0 || K < 1)
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            const double *xr = x + ((size_t)b * D + d) * L;
+            double *orow = out + ((size_t)b * D + d) * L;
+            for (int64_t t = 0; t < L; ++t) {
+                double acc = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    int64_t s = t - (K - 1) + k;
+                    if (s >= 0)
+                        acc += w[d * K + k] * xr[s];
+                }
+                orow[t] = apply_silu ? oracle_silu(acc) : acc;
+            }
+        }
+    return 0;
+}
+
+/* Single-token decode step on a stored state h [B, D, N] (updated in place).
+ * x, dt, z, y: [B, D];  Bm, Cm: [B, N]. */
+int oracle_state_update(double *h, const double *x, const double *dt, const double *dt_bias,
+                        const double *A, const double *Bm, const double *Cm,
+                        const double *Dskip, const double *z, double *y, int64_t B,
+                        int64_t D, int64_t N)
+{
+    if (!h || !x || !dt || !A || !Bm || !Cm || !y || B < 0 || D < 0 || N < 1 || N > 64)
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            size_t c = (size_t)b * D + d;
+            y[c] = step(N, h + c * N, x[c], dt[c], dt_bias ? dt_bias[d] : 0.0, A + d * N,
+                        Bm + (size_t)b * N, Cm + (size_t)b * N, Dskip ? Dskip[d] : 0.0,
+                        z ? z + c : NULL);
+        }
+    return 0;
+}

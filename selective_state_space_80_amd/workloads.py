@@ -1,0 +1,148 @@
+"""Seeded synthetic workloads for the selective-scan hot path.
+
+This module only draws random inputs; it contains none of the method's
+arithmetic and is shared by the GPU tests, the oracle checks and the
+benchmark so that both sides consume bit-identical tensors.
+
+Recipe (every distribution is drawn with ``numpy.random.default_rng``):
+  x, z           ~ N(0, 1)                       [B, D, L]
+  dt             ~ N(0, 0.25)  (0.25 = std)      [B, D, L]
+  u_d            log-uniform in [1e-3, 1e-1]     per channel d
+  dt_bias_d      = log(expm1(u_d))  (so a zero dt gives step u_d)
+  A[d, n]        = -(n + 1)
+  Bm, Cm         ~ N(0, 1)                       [B, L, N]  (shared over d)
+  Dskip          = 1
+  block config:  x is replaced by x_raw ~ N(0, 1) that feeds the causal
+                 depthwise conv, whose weights are conv_w ~ N(0, 0.5) [D, 4]
+  decode config: h0 ~ N(0, 1) [B, D, N] fp32; every step draws fresh
+                 x, z, dt [B, D] and Bm, Cm [B, N] from its own stream.
+Draw order: x (or x_raw), z, dt, u, Bm, Cm, conv_w.  bf16 tensors are drawn in
+fp32 and rounded to bf16 (round-to-nearest-even); the arrays returned here
+hold those rounded values in float32, so they convert to bf16 exactly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class ScanWorkload:
+    name: str
+    B: int
+    D: int
+    L: int
+    N: int
+    io: str            # "f32" or "bf16"
+    conv: bool = False  # causal conv1d(k=4)+SiLU front end feeds the scan
+    seed: int = 0
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.D * self.L
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    D: int
+    N: int
+    io: str
+    steps: int
+    check_every: int
+    seed: int = 0
+
+
+WORKLOADS = {
+    0: ScanWorkload("scan_b1_d64_l256_n16_f32", 1, 64, 256, 16, "f32", False, 1000),
+    1: ScanWorkload("block_dmodel768_b2_d1536_l8192_n16_f32_conv4", 2, 1536, 8192, 16,
+                    "f32", True, 1001),
+    2: ScanWorkload("scan_b8_d5120_l2048_n16_bf16", 8, 5120, 2048, 16, "bf16", False, 1002),
+    3: ScanWorkload("scan_b1_d1536_l131072_n16_bf16", 1, 1536, 131072, 16, "bf16", False,
+                    1003),
+    4: DecodeWorkload("decode_b256_d5120_n16_bf16_x1024", 256, 5120, 16, "bf16", 1024, 128,
+                      1004),
+}
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); return float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32)
+    # NaN stays NaN (not produced by these generators, kept for completeness)
+    return np.where(np.isnan(a), a, out)
+
+
+def _normal(rng, shape, std=1.0):
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        v *= np.float32(std)
+    return v
+
+
+def _channel_params(rng, D: int, N: int, u_range=(1e-3, 1e-1)):
+    lo, hi = np.log(u_range[0]), np.log(u_range[1])
+    u = np.exp(rng.uniform(lo, hi, size=D))
+    dt_bias = np.log(np.expm1(u)).astype(np.float32)
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float32), (D, 1))
+    Dskip = np.ones(D, dtype=np.float32)
+    return dt_bias, A, Dskip
+
+
+def make_scan_inputs(B: int, D: int, L: int, N: int, io: str = "f32", seed: int = 0,
+                     conv: bool = False, dt_std: float = 0.25, u_range=(1e-3, 1e-1)):
+    """Draw one scan problem.  Returns a dict of float32 numpy arrays:
+    x (or x_raw + conv_w when conv), z, dt, dt_bias, A, Bm, Cm, Dskip."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    first = _normal(rng, (B, D, L))
+    out["z"] = _normal(rng, (B, D, L))
+    out["dt"] = _normal(rng, (B, D, L), dt_std)
+    out["dt_bias"], out["A"], out["Dskip"] = _channel_params(rng, D, N, u_range)
+    out["Bm"] = _normal(rng, (B, L, N))
+    out["Cm"] = _normal(rng, (B, L, N))
+    if conv:
+        out["x_raw"] = first
+        out["conv_w"] = _normal(rng, (D, 4), 0.5)
+    else:
+        out["x"] = first
+    if io == "bf16":
+        for k in ("x", "x_raw", "z", "dt", "Bm", "Cm"):
+            if k in out:
+                out[k] = round_bf16(out[k])
+    elif io != "f32":
+        raise ValueError("io must be 'f32' or 'bf16'")
+    return out
+
+
+def scan_inputs(wl: ScanWorkload, seed: int | None = None):
+    return make_scan_inputs(wl.B, wl.D, wl.L, wl.N, wl.io,
+                            wl.seed if seed is None else seed, wl.conv)
+
+
+def decode_initial(wl: DecodeWorkload, seed: int | None = None):
+    """h0 [B,D,N] fp32 and the per-channel parameters of a decode run."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    h0 = _normal(rng, (wl.B, wl.D, wl.N))
+    dt_bias, A, Dskip = _channel_params(rng, wl.D, wl.N)
+    return {"h0": h0, "dt_bias": dt_bias, "A": A, "Dskip": Dskip}
+
+
+def decode_step_inputs(wl: DecodeWorkload, step: int, seed: int | None = None):
+    """Fresh token inputs of decode step `step`: x, z, dt [B,D]; Bm, Cm [B,N]."""
+    rng = np.random.default_rng([wl.seed if seed is None else seed, 1 + step])
+    out = {
+        "x": _normal(rng, (wl.B, wl.D)),
+        "z": _normal(rng, (wl.B, wl.D)),
+        "dt": _normal(rng, (wl.B, wl.D), 0.25),
+        "Bm": _normal(rng, (wl.B, wl.N)),
+        "Cm": _normal(rng, (wl.B, wl.N)),
+    }
+    if wl.io == "bf16":
+        out = {k: round_bf16(v) for k, v in out.items()}
+    return out

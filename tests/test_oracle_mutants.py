@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in copies of oracle.c (on the CPU) and check that
+the pins catch every one of them.  This is what makes the pins trustworthy:
+a dropped term, a wrong sign or index, a transposed operand each fail at
+least one pin."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+with open(oracle.SOURCE) as _f:
+    _SRC = _f.read()
+
+# (name, text to find, replacement); each must occur in oracle.c
+MUTANTS = [
+    ("euler_bbar", "*bcoef = expm1(delta * a) / a;", "*bcoef = delta;"),
+    ("bbar_missing_delta", "*bcoef = expm1(delta * a) / a;",
+     "*bcoef = expm1(delta * a) / (delta * a);"),
+    ("abar_sign", "*abar = exp(delta * a);", "*abar = exp(-delta * a);"),
+    ("no_softplus", "double delta = oracle_softplus(dtv + bias);",
+     "double delta = exp(dtv + bias);"),
+    ("bias_dropped", "oracle_softplus(dtv + bias)", "oracle_softplus(dtv)"),
+    ("b_c_swapped", "bcoef * Bt[n] * xv;", "bcoef * Ct[n] * xv;"),
+    ("readout_before_update",
+     "        h[n] = abar * h[n] + bcoef * Bt[n] * xv;\n    }\n    for (int64_t n = 0; n < N; ++n)\n        y += Ct[n] * h[n];",
+     "        y += Ct[n] * h[n];\n        h[n] = abar * h[n] + bcoef * Bt[n] * xv;\n    }"),
+    ("gate_excludes_skip", "    y += Dv * xv;\n    if (zv)\n        y *= oracle_silu(*zv);",
+     "    if (zv)\n        y *= oracle_silu(*zv);\n    y += Dv * xv;"),
+    ("silu_is_sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("h0_ignored", "h[n] = h0 ? h0[n] : 0.0;", "h[n] = 0.0;"),
+    ("conv_taps_reversed", "acc += w[d * K + k] * xr[s];",
+     "acc += w[d * K + (K - 1 - k)] * xr[s];"),
+    ("conv_off_by_one", "int64_t s = t - (K - 1) + k;", "int64_t s = t - K + k;"),
+    ("conv_bias_dropped", "double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
+    ("dskip_channel_index", "j->Dskip ? j->Dskip[d] : 0.0", "j->Dskip ? j->Dskip[0] : 0.0"),
+    ("a_row_index", "j->A + d * j->N,", "j->A,"),
+]
+
+
+@pytest.mark.parametrize("name,find,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, find, repl):
+    assert _SRC.count(find) >= 1, f"mutation site for {name} not found in oracle.c"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(_SRC.replace(find, repl))
+    lib = oracle.compile_oracle(str(src), str(tmp_path / f"lib_{name}.so"))
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects the planted mistake {name}"
+    os.remove(lib)

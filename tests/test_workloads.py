@@ -1,0 +1,64 @@
+"""The seeded input generators: determinism, shapes, distributions, bf16 rounding."""
+import hashlib
+
+import numpy as np
+import torch
+
+from selective_state_space_80_amd import workloads as W
+
+
+def _digest(d):
+    h = hashlib.sha256()
+    for k in sorted(d):
+        h.update(k.encode())
+        h.update(np.ascontiguousarray(d[k]).tobytes())
+    return h.hexdigest()
+
+
+def test_same_seed_same_inputs():
+    a = W.make_scan_inputs(2, 8, 64, 16, "bf16", seed=5)
+    b = W.make_scan_inputs(2, 8, 64, 16, "bf16", seed=5)
+    c = W.make_scan_inputs(2, 8, 64, 16, "bf16", seed=6)
+    assert _digest(a) == _digest(b) != _digest(c)
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 7,
+                        np.array([0.0, -0.0, 1e-40, 3.0e38, -2.5, 1.00390625,
+                                  1.01171875], np.float32)])
+    want = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(W.round_bf16(v), want)
+
+
+def test_scan_recipe():
+    wl = W.WORKLOADS[0]
+    p = W.scan_inputs(wl)
+    assert p["x"].shape == (1, 64, 256) and p["Bm"].shape == (1, 256, 16)
+    assert np.array_equal(p["A"], -np.tile(np.arange(1, 17, dtype=np.float32), (64, 1)))
+    assert np.all(p["Dskip"] == 1)
+    u = np.logaddexp(0.0, p["dt_bias"].astype(np.float64))   # step at dt = 0
+    assert np.all((u > 0.99e-3) & (u < 1.01e-1))
+    assert abs(np.std(p["dt"]) - 0.25) < 0.01
+    assert all(v.dtype == np.float32 for v in p.values())
+
+
+def test_bf16_inputs_are_representable():
+    p = W.make_scan_inputs(1, 4, 32, 16, "bf16", seed=1)
+    for k in ("x", "z", "dt", "Bm", "Cm"):
+        assert np.array_equal(W.round_bf16(p[k]), p[k])
+
+
+def test_block_recipe_has_conv():
+    p = W.make_scan_inputs(1, 4, 32, 16, "f32", seed=2, conv=True)
+    assert "x_raw" in p and p["conv_w"].shape == (4, 4) and "x" not in p
+
+
+def test_decode_recipe():
+    wl = W.DecodeWorkload("t", 3, 5, 16, "bf16", 4, 2, 9)
+    h = W.decode_initial(wl)
+    s0 = W.decode_step_inputs(wl, 0)
+    s1 = W.decode_step_inputs(wl, 1)
+    assert h["h0"].shape == (3, 5, 16) and s0["x"].shape == (3, 5)
+    assert s0["Bm"].shape == (3, 16) and not np.array_equal(s0["x"], s1["x"])
+    assert np.array_equal(W.decode_step_inputs(wl, 1)["x"], s1["x"])
