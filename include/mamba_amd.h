@@ -1,0 +1,150 @@
+/*
+ * mamba_amd.h -- C ABI of the MI355X (gfx950) selective state-space library.
+ *
+ * Three operations make up the data-parallel hot path of a Mamba block:
+ *   mamba_conv1d_silu            causal depthwise conv1d + SiLU front end
+ *   mamba_selective_scan_fwd     fused selective-scan forward (prefill)
+ *   mamba_selective_state_update single-token recurrent step (decode)
+ * plus workspace sizing and status helpers.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
+ *     row-major in the layout stated at the call; the library never frees or
+ *     keeps it.  Optional inputs may be NULL where stated.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream).  They allocate no memory.
+ *   - Arguments are validated on the host before any HIP call; on a bad
+ *     argument the call returns a status other than MAMBA_OK and launches
+ *     nothing.  A failure to launch returns MAMBA_ERR_LAUNCH.  Faults inside a
+ *     kernel surface at the caller's next synchronisation, as usual for HIP.
+ *   - Outputs must not overlap inputs (only the decode state is in/out).
+ *   - Element types: MAMBA_F32 = float, MAMBA_BF16 = bfloat16 (stored as
+ *     uint16, round-to-nearest-even on output).  Parameters (A, dt_bias, D,
+ *     conv weights, states) are always float.
+ *   - Arithmetic is fp32 throughout, including the recurrent state.
+ *   - Thread safety: calls may be issued from several host threads; calls
+ *     that share a workspace must be ordered on one stream.
+ *
+ * Notation: B batch, D channels (d_inner), L sequence length, N state size
+ * (1..16), K conv taps.  The model is the selective SSM of the Mamba papers:
+ *   Δ_t   = softplus(dt_t + dt_bias)                       (input-dependent step)
+ *   Ā_t   = exp(Δ_t A),  B̄_t = (Δ_t A)^-1 (exp(Δ_t A) - I) Δ_t B_t   (zero-order hold)
+ *   h_t   = Ā_t h_{t-1} + B̄_t x_t,   y_t = <C_t, h_t> + D x_t
+ *   out_t = y_t * SiLU(z_t)
+ * with A diagonal (one value per channel d and state n).
+ */
+#ifndef MAMBA_AMD_H
+#define MAMBA_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA_AMD_ABI_VERSION 1
+#define MAMBA_MAX_STATE 16
+#define MAMBA_MAX_CONV_TAPS 8
+
+typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_dtype;
+
+typedef enum {
+    MAMBA_OK = 0,
+    MAMBA_ERR_NULL = 1,        /* a required pointer is NULL                  */
+    MAMBA_ERR_SHAPE = 2,       /* a size is negative or the product too large */
+    MAMBA_ERR_DTYPE = 3,       /* dtype is not MAMBA_F32 / MAMBA_BF16         */
+    MAMBA_ERR_UNSUPPORTED = 4, /* N outside 1..16, K outside 1..8             */
+    MAMBA_ERR_ALIGN = 5,       /* pointer not aligned to its element size     */
+    MAMBA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+    MAMBA_ERR_WORKSPACE = 7,   /* workspace missing, misaligned or too small  */
+    MAMBA_ERR_LAUNCH = 8,      /* HIP reported an error when launching        */
+    MAMBA_ERR_DEVICE = 9       /* no HIP device, or not a gfx950 device       */
+} mamba_status;
+
+/* Static, human-readable name of a status value (never NULL). */
+const char *mamba_status_string(int status);
+
+/* MAMBA_AMD_ABI_VERSION of the compiled library. */
+int mamba_abi_version(void);
+
+/*
+ * Causal depthwise conv1d over time, then SiLU (the block's front end:
+ * "Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式", §3.1, causal
+ * Conv1D before the selective SSM; kernel size d_conv = 4 in
+ * "Mamba架构与SSM模型：高效序列建模技术解析", §3.2):
+ *   out[b,d,t] = SiLU( bias[d] + sum_{k<K} w[d,k] * x[b,d,t-(K-1)+k] ),  x[t<0] = 0.
+ *   x, out : [B, D, L] of `dtype`;  w : [D, K] float;  bias : [D] float or NULL.
+ * out must not overlap x.  K in 1..8.
+ */
+mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias, void *out,
+                               int64_t B, int64_t D, int64_t L, int64_t K, mamba_dtype dtype,
+                               void *stream);
+
+/*
+ * Bytes of device workspace mamba_selective_scan_fwd needs for this shape
+ * (0 only for an empty problem).  The workspace is scratch owned by the
+ * caller: it needs no initialisation, holds nothing between calls, and must
+ * be 256-byte aligned.
+ */
+size_t mamba_selective_scan_fwd_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                               mamba_dtype io);
+
+/*
+ * Fused selective-scan forward: softplus step, zero-order-hold discretisation
+ * ("Mamba架构与SSM模型：高效序列建模技术解析", §2.1-2.2), the selective
+ * recurrence with readout after the update ("Mamba状态空间模型深度解析：
+ * 挑战Transformer的下一代序列建模范式", §2.1), the D skip and the SiLU(z) gate
+ * (same page, §3.1), for every (b, d) sequence, in one pass over the inputs.
+ * Long sequences are cut into chunks whose end states are carried across
+ * chunks ("Mamba: Linear-Time Sequence Modeling with Selective SSMs", section
+ * on the block-wise selective scan with a prefix state passed forward).
+ *
+ *   x, dt, z, y : [B, D, L] of `io`            (z NULL = no gate)
+ *   dt_bias     : [D] float or NULL (= 0)      Dskip : [D] float or NULL (= 0)
+ *   A           : [D, N] float (diagonal state matrix, one row per channel)
+ *   Bm, Cm      : [B, L, N] of `io`, shared by every channel of batch b
+ *   h0          : [B, D, N] float or NULL (= zero initial state)
+ *   h_last      : [B, D, N] float or NULL (= not returned): state after step L-1
+ *   workspace   : >= mamba_selective_scan_fwd_workspace_size(...) bytes
+ * h0/h_last let a long sequence be scanned in several calls or handed to the
+ * decode step.  y and h_last must not overlap any input, each other or the
+ * workspace.
+ */
+mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float *dt_bias,
+                                      const float *A, const void *Bm, const void *Cm,
+                                      const float *Dskip, const void *z, const float *h0,
+                                      void *y, float *h_last, void *workspace,
+                                      size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
+                                      int64_t N, mamba_dtype io, void *stream);
+
+/*
+ * Single-token decode step (the recurrent, fixed-size-state mode used at
+ * inference: "Mamba架构深度剖析：如何以线性时间重塑序列建模", §3): for every
+ * (b, d), one step of the recurrence above on the stored state h, updated in
+ * place, and the gated output of that token.
+ *   h           : [B, D, N] float, read and overwritten
+ *   x, dt, z, y : [B, D] of `io`  (z NULL = no gate)
+ *   Bm, Cm      : [B, N] of `io`
+ *   A [D, N], dt_bias [D] or NULL, Dskip [D] or NULL : float
+ * y must not overlap h or any input.
+ */
+mamba_status mamba_selective_state_update(float *h, const void *x, const void *dt,
+                                          const float *dt_bias, const float *A,
+                                          const void *Bm, const void *Cm, const float *Dskip,
+                                          const void *z, void *y, int64_t B, int64_t D,
+                                          int64_t N, mamba_dtype io, void *stream);
+
+/*
+ * Profiling hook.  When both are non-NULL hipEvent_t handles (passed as
+ * void*), later calls made from this host thread record `start` right before
+ * and `stop` right after the main scan kernel of mamba_selective_scan_fwd, on
+ * the call's stream.  Pass NULL, NULL to turn it off.
+ */
+void mamba_set_scan_timing_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_AMD_H */

@@ -1,0 +1,219 @@
+"""MI355X (gfx950) selective state-space hot path: Python binding.
+
+Thin ctypes marshalling over the C ABI of ``libmamba_amd.so`` (declared in
+``include/mamba_amd.h``).  Every step of the computation runs in the HIP
+kernels of that library; this module only checks tensor metadata, takes
+device pointers and the current HIP stream, and raises on a non-OK status.
+There is no CPU fallback: if the library is missing, calls raise.
+
+Entry points (same names as the C ABI, without the ``mamba_`` prefix):
+  conv1d_silu(x, w, bias=None, out=None)
+  selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+                     return_last_state=False, out=None, workspace=None)
+  selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, out=None)
+  selective_scan_fwd_workspace_size(B, D, L, N, dtype)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libmamba_amd.so")
+
+MAMBA_F32 = 0
+MAMBA_BF16 = 1
+
+STATUS_NAMES = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ERR_DTYPE",
+                4: "MAMBA_ERR_UNSUPPORTED", 5: "MAMBA_ERR_ALIGN", 6: "MAMBA_ERR_ALIAS",
+                7: "MAMBA_ERR_WORKSPACE", 8: "MAMBA_ERR_LAUNCH", 9: "MAMBA_ERR_DEVICE"}
+
+# every symbol include/mamba_amd.h declares
+EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
+            "mamba_selective_scan_fwd_workspace_size", "mamba_selective_scan_fwd",
+            "mamba_selective_state_update", "mamba_set_scan_timing_events"]
+
+_lib = None
+
+
+class MambaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load_library(path: str = LIBRARY):
+    """Load libmamba_amd.so and declare its signatures (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m selective_state_space_80_amd.build`"
+                           " (the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.mamba_status_string.restype = ctypes.c_char_p
+    lib.mamba_status_string.argtypes = [I32]
+    lib.mamba_abi_version.restype = I32
+    lib.mamba_abi_version.argtypes = []
+    lib.mamba_conv1d_silu.restype = I32
+    lib.mamba_conv1d_silu.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, P]
+    lib.mamba_selective_scan_fwd_workspace_size.restype = SZ
+    lib.mamba_selective_scan_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I32]
+    lib.mamba_selective_scan_fwd.restype = I32
+    lib.mamba_selective_scan_fwd.argtypes = [P] * 12 + [SZ, I64, I64, I64, I64, I32, P]
+    lib.mamba_selective_state_update.restype = I32
+    lib.mamba_selective_state_update.argtypes = [P] * 10 + [I64, I64, I64, I32, P]
+    lib.mamba_set_scan_timing_events.restype = None
+    lib.mamba_set_scan_timing_events.argtypes = [P, P]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().mamba_status_string(int(status)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(int(status), "unknown")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MAMBA_F32
+    if t.dtype == torch.bfloat16:
+        return MAMBA_BF16
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype=None, device=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def _raise(st, where):
+    if st != 0:
+        raise MambaError(st, where)
+
+
+def conv1d_silu(x, w, bias=None, out=None):
+    """Causal depthwise conv1d + SiLU.  x [B,D,L] (f32/bf16), w [D,K] f32,
+    bias [D] f32 or None.  Returns out [B,D,L] of x's dtype."""
+    torch = _torch()
+    lib = load_library()
+    B, D, L = x.shape
+    K = w.shape[1]
+    _check(x, "x", (B, D, L), device=x.device)
+    _check(w, "w", (D, K), torch.float32, x.device)
+    _check(bias, "bias", (D,), torch.float32, x.device, optional=True)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (B, D, L), x.dtype, x.device)
+    st = lib.mamba_conv1d_silu(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), B, D, L, K,
+                               _io_dtype(x), _stream(x.device))
+    _raise(st, "mamba_conv1d_silu")
+    return out
+
+
+def selective_scan_fwd_workspace_size(B, D, L, N, dtype=None) -> int:
+    io = MAMBA_F32 if dtype is None else _io_dtype(_torch().empty(0, dtype=dtype))
+    return int(load_library().mamba_selective_scan_fwd_workspace_size(B, D, L, N, io))
+
+
+def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+                       return_last_state=False, out=None, workspace=None, h_last=None):
+    """Fused selective-scan forward.  x, dt, z [B,D,L]; Bm, Cm [B,L,N] (all of
+    one dtype, f32 or bf16); A [D,N], dt_bias [D], Dskip [D], h0 [B,D,N] f32.
+    Returns y [B,D,L] (x's dtype), and h_last [B,D,N] f32 if return_last_state."""
+    torch = _torch()
+    lib = load_library()
+    B, D, L = x.shape
+    N = A.shape[1]
+    dev, io_t = x.device, x.dtype
+    _check(x, "x", (B, D, L), io_t, dev)
+    _check(dt, "dt", (B, D, L), io_t, dev)
+    _check(z, "z", (B, D, L), io_t, dev, optional=True)
+    _check(Bm, "Bm", (B, L, N), io_t, dev)
+    _check(Cm, "Cm", (B, L, N), io_t, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (D,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
+    _check(h0, "h0", (B, D, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (B, D, L), io_t, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", (B, D, N), torch.float32, dev, optional=True)
+    io = _io_dtype(x)
+    need = int(lib.mamba_selective_scan_fwd_workspace_size(B, D, L, N, io))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mamba_selective_scan_fwd(
+        _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+        _ptr(h0), _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N, io,
+        _stream(dev))
+    _raise(st, "mamba_selective_scan_fwd")
+    if return_last_state:
+        return out, h_last
+    return out
+
+
+def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, out=None):
+    """One decode step.  h [B,D,N] f32 is updated in place; x, dt, z [B,D] and
+    Bm, Cm [B,N] share one dtype (f32/bf16).  Returns y [B,D] of that dtype."""
+    torch = _torch()
+    lib = load_library()
+    B, D, N = h.shape
+    dev, io_t = h.device, x.dtype
+    _check(h, "h", (B, D, N), torch.float32, dev)
+    _check(x, "x", (B, D), io_t, dev)
+    _check(dt, "dt", (B, D), io_t, dev)
+    _check(z, "z", (B, D), io_t, dev, optional=True)
+    _check(Bm, "Bm", (B, N), io_t, dev)
+    _check(Cm, "Cm", (B, N), io_t, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (D,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (B, D), io_t, dev)
+    st = lib.mamba_selective_state_update(
+        _ptr(h), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+        _ptr(z), _ptr(out), B, D, N, _io_dtype(x), _stream(dev))
+    _raise(st, "mamba_selective_state_update")
+    return out
+
+
+def set_scan_timing_events(start=None, stop=None):
+    """Record torch.cuda.Event pair around the main scan kernel of later calls
+    from this thread (None, None turns it off)."""
+    lib = load_library()
+    if start is None or stop is None:
+        lib.mamba_set_scan_timing_events(None, None)
+    else:
+        lib.mamba_set_scan_timing_events(ctypes.c_void_p(start.cuda_event),
+                                         ctypes.c_void_p(stop.cuda_event))

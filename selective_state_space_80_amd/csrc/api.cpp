@@ -1,0 +1,274 @@
+// Host side of the C ABI declared in include/mamba_amd.h: argument
+// validation (before any HIP call), workspace sizing, and launch.
+#include "mamba_amd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+
+namespace {
+
+using mamba::kMaxN;
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // B*D*L bound (keeps every index in int64)
+
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+bool valid_dtype(int dt) { return dt == MAMBA_F32 || dt == MAMBA_BF16; }
+size_t esize(mamba_dtype dt) { return dt == MAMBA_BF16 ? 2 : 4; }
+
+bool aligned(const void *p, size_t a) { return p == nullptr || (uintptr_t)p % a == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range rng(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b)
+{
+    if (a.lo == 0 || b.lo == 0 || a.hi == a.lo || b.hi == b.lo)
+        return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Non-negative sizes whose product stays below kMaxElems.
+bool sizes_ok(int64_t a, int64_t b, int64_t c)
+{
+    if (a < 0 || b < 0 || c < 0)
+        return false;
+    if (a == 0 || b == 0 || c == 0)
+        return true;
+    if (a > kMaxElems || b > kMaxElems || c > kMaxElems)
+        return false;
+    if (a > kMaxElems / b)
+        return false;
+    return a * b <= kMaxElems / c;
+}
+
+// The kernels are built for gfx950 only.
+mamba_status device_ok()
+{
+    static std::mutex mu;
+    static int checked[64] = {0};  // 0 unknown, 1 ok, 2 bad
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return MAMBA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 64)
+        return MAMBA_ERR_DEVICE;
+    if (checked[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return MAMBA_ERR_DEVICE;
+        checked[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    return checked[dev] == 1 ? MAMBA_OK : MAMBA_ERR_DEVICE;
+}
+
+mamba_status launched(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mamba_status_string(int status)
+{
+    switch (status) {
+    case MAMBA_OK: return "MAMBA_OK";
+    case MAMBA_ERR_NULL: return "MAMBA_ERR_NULL: a required pointer is NULL";
+    case MAMBA_ERR_SHAPE: return "MAMBA_ERR_SHAPE: negative size or problem too large";
+    case MAMBA_ERR_DTYPE: return "MAMBA_ERR_DTYPE: dtype must be MAMBA_F32 or MAMBA_BF16";
+    case MAMBA_ERR_UNSUPPORTED: return "MAMBA_ERR_UNSUPPORTED: N must be 1..16, K 1..8";
+    case MAMBA_ERR_ALIGN: return "MAMBA_ERR_ALIGN: pointer not aligned to its element size";
+    case MAMBA_ERR_ALIAS: return "MAMBA_ERR_ALIAS: an output overlaps an input";
+    case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MAMBA_ERR_LAUNCH: return "MAMBA_ERR_LAUNCH: HIP failed to launch a kernel";
+    case MAMBA_ERR_DEVICE: return "MAMBA_ERR_DEVICE: no gfx950 HIP device is current";
+    default: return "unknown mamba_status";
+    }
+}
+
+int mamba_abi_version(void) { return MAMBA_AMD_ABI_VERSION; }
+
+void mamba_set_scan_timing_events(void *start, void *stop)
+{
+    if (start && stop) {
+        g_ev_start = (hipEvent_t)start;
+        g_ev_stop = (hipEvent_t)stop;
+    } else {
+        g_ev_start = nullptr;
+        g_ev_stop = nullptr;
+    }
+}
+
+mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias, void *out,
+                               int64_t B, int64_t D, int64_t L, int64_t K, mamba_dtype dtype,
+                               void *stream)
+{
+    if (!valid_dtype(dtype))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, D, L) || K < 0)
+        return MAMBA_ERR_SHAPE;
+    if (K < 1 || K > MAMBA_MAX_CONV_TAPS)
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t n = B * D * L;
+    if (n == 0)
+        return MAMBA_OK;
+    if (!x || !w || !out)
+        return MAMBA_ERR_NULL;
+    const size_t es = esize(dtype);
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(w, 4) || !aligned(bias, 4))
+        return MAMBA_ERR_ALIGN;
+    const Range ro = rng(out, (size_t)n * es);
+    if (overlap(ro, rng(x, (size_t)n * es)) || overlap(ro, rng(w, (size_t)(D * K) * 4)) ||
+        (bias && overlap(ro, rng(bias, (size_t)D * 4))))
+        return MAMBA_ERR_ALIAS;
+    if (B * D * ((L + 7) / 8) >= (int64_t(1) << 32))
+        return MAMBA_ERR_SHAPE;
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::ConvArgs a{x, w, bias, out, B, D, L, (int)K, dtype == MAMBA_BF16};
+    return launched(mamba::launch_conv1d_silu(a, (hipStream_t)stream));
+}
+
+size_t mamba_selective_scan_fwd_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                               mamba_dtype io)
+{
+    (void)io;
+    if (!sizes_ok(B, D, L) || N < 1 || N > kMaxN)
+        return 0;
+    if (B * D * L == 0)
+        return 0;
+    return mamba::scan_ws_layout(B, D, L).total;
+}
+
+mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float *dt_bias,
+                                      const float *A, const void *Bm, const void *Cm,
+                                      const float *Dskip, const void *z, const float *h0,
+                                      void *y, float *h_last, void *workspace,
+                                      size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
+                                      int64_t N, mamba_dtype io, void *stream)
+{
+    if (!valid_dtype(io))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, D, L) || N < 0)
+        return MAMBA_ERR_SHAPE;
+    if (N < 1 || N > kMaxN)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (B * D == 0)
+        return MAMBA_OK;
+    const int64_t n = B * D * L;
+    const size_t es = esize(io);
+    if (L == 0) {
+        // nothing to scan; h_last (if asked for) is the initial state
+        if (!h_last)
+            return MAMBA_OK;
+        if (!aligned(h_last, 4) || !aligned(h0, 4))
+            return MAMBA_ERR_ALIGN;
+        if (h0 && overlap(rng(h_last, (size_t)(B * D * N) * 4), rng(h0, (size_t)(B * D * N) * 4)))
+            return MAMBA_ERR_ALIAS;
+    } else {
+        if (!x || !dt || !A || !Bm || !Cm || !y)
+            return MAMBA_ERR_NULL;
+        if (!aligned(x, es) || !aligned(dt, es) || !aligned(z, es) || !aligned(y, es) ||
+            !aligned(Bm, es) || !aligned(Cm, es) || !aligned(A, 4) || !aligned(dt_bias, 4) ||
+            !aligned(Dskip, 4) || !aligned(h0, 4) || !aligned(h_last, 4))
+            return MAMBA_ERR_ALIGN;
+        if (B * L * kMaxN >= (int64_t(1) << 31))
+            return MAMBA_ERR_SHAPE;
+        const mamba::ScanWsLayout lay = mamba::scan_ws_layout(B, D, L);
+        if (lay.n_items >= (int64_t(1) << 23))
+            return MAMBA_ERR_SHAPE;
+        if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256))
+            return MAMBA_ERR_WORKSPACE;
+        const Range ry = rng(y, (size_t)n * es);
+        const Range rh = rng(h_last, h_last ? (size_t)(B * D * N) * 4 : 0);
+        const Range rw = rng(workspace, lay.total);
+        const Range ins[] = {rng(x, (size_t)n * es),          rng(dt, (size_t)n * es),
+                             rng(z, z ? (size_t)n * es : 0),  rng(Bm, (size_t)(B * L * N) * es),
+                             rng(Cm, (size_t)(B * L * N) * es), rng(A, (size_t)(D * N) * 4),
+                             rng(dt_bias, dt_bias ? (size_t)D * 4 : 0),
+                             rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                             rng(h0, h0 ? (size_t)(B * D * N) * 4 : 0)};
+        for (const Range &r : ins)
+            if (overlap(ry, r) || overlap(rh, r) || overlap(rw, r))
+                return MAMBA_ERR_ALIAS;
+        if (overlap(ry, rh) || overlap(ry, rw) || overlap(rh, rw))
+            return MAMBA_ERR_ALIAS;
+    }
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::ScanArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.Bm = Bm;
+    a.Cm = Cm;
+    a.z = z;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.h0 = h0;
+    a.y = y;
+    a.h_last = h_last;
+    a.ws = (unsigned char *)workspace;
+    a.lay = mamba::scan_ws_layout(B, D, L);
+    a.B = B;
+    a.D = D;
+    a.L = L;
+    a.N = (int)N;
+    a.bf16 = io == MAMBA_BF16;
+    a.ev_start = g_ev_start;
+    a.ev_stop = g_ev_stop;
+    return launched(mamba::launch_selective_scan(a, (hipStream_t)stream));
+}
+
+mamba_status mamba_selective_state_update(float *h, const void *x, const void *dt,
+                                          const float *dt_bias, const float *A,
+                                          const void *Bm, const void *Cm, const float *Dskip,
+                                          const void *z, void *y, int64_t B, int64_t D,
+                                          int64_t N, mamba_dtype io, void *stream)
+{
+    if (!valid_dtype(io))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, D, 1) || N < 0)
+        return MAMBA_ERR_SHAPE;
+    if (N < 1 || N > kMaxN)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (B * D == 0)
+        return MAMBA_OK;
+    if (!h || !x || !dt || !A || !Bm || !Cm || !y)
+        return MAMBA_ERR_NULL;
+    const size_t es = esize(io);
+    if (!aligned(h, 4) || !aligned(x, es) || !aligned(dt, es) || !aligned(z, es) ||
+        !aligned(y, es) || !aligned(Bm, es) || !aligned(Cm, es) || !aligned(A, 4) ||
+        !aligned(dt_bias, 4) || !aligned(Dskip, 4))
+        return MAMBA_ERR_ALIGN;
+    const int64_t n = B * D;
+    const Range ry = rng(y, (size_t)n * es);
+    const Range rh = rng(h, (size_t)(n * N) * 4);
+    const Range ins[] = {rng(x, (size_t)n * es), rng(dt, (size_t)n * es),
+                         rng(z, z ? (size_t)n * es : 0), rng(Bm, (size_t)(B * N) * es),
+                         rng(Cm, (size_t)(B * N) * es), rng(A, (size_t)(D * N) * 4),
+                         rng(dt_bias, dt_bias ? (size_t)D * 4 : 0),
+                         rng(Dskip, Dskip ? (size_t)D * 4 : 0)};
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rh, r))
+            return MAMBA_ERR_ALIAS;
+    if (overlap(ry, rh))
+        return MAMBA_ERR_ALIAS;
+    if ((D + 255) / 256 * B >= (int64_t(1) << 31))
+        return MAMBA_ERR_SHAPE;
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::StepArgs a{h, x, dt, Bm, Cm, z, dt_bias, A, Dskip, y, B, D, (int)N, io == MAMBA_BF16};
+    return launched(mamba::launch_state_update(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

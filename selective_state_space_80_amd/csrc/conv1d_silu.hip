@@ -1,0 +1,165 @@
+// Causal depthwise conv1d + SiLU for gfx950: the front end of the Mamba block
+// ("Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式" §3.1: a causal
+// Conv1D supplies local context before the selective SSM; kernel size 4 per
+// "Mamba架构与SSM模型：高效序列建模技术解析" §3.2).
+//   out[b,d,t] = SiLU(bias_d + sum_{k<K} w[d,k] x[b,d,t-(K-1)+k]),  x[t<0] = 0
+// Streaming and HBM-bound (one read, one write per element): each thread makes
+// 8 consecutive outputs of one row from one 128-bit (bf16) or two 128-bit
+// (fp32) loads plus the previous 8 inputs as the left halo, which the
+// neighbouring thread loads too, so the halo comes from cache, not HBM.
+#include "device_common.h"
+#include "internal.h"
+
+namespace mamba {
+
+namespace {
+
+constexpr int kVT = 8;  // outputs per thread
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void *base, int64_t off, float (&v)[kVT])
+{
+    if constexpr (!BF16) {
+        const float4 *q = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
+        const float4 a = q[0], c = q[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
+        const uint32_t w4[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w4[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w4[k] & 0xffff0000u);
+        }
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void *base, int64_t off, const float (&v)[kVT])
+{
+    if constexpr (!BF16) {
+        float4 *q = reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + off);
+        q[0] = make_float4(v[0], v[1], v[2], v[3]);
+        q[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        uint32_t w4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w4[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(base) + off) =
+            make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+}
+
+// VEC: L % 8 == 0 and 16-byte aligned rows, so every thread's 8 outputs lie in
+// one row and the 8-element loads are aligned.
+template <bool BF16, bool VEC, int K>
+__global__ void __launch_bounds__(256) conv1d_silu_kernel(
+    const void *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    void *__restrict__ out, int64_t D, int64_t L, int64_t vec_per_row, int64_t n_threads)
+{
+    using E = Elem<BF16>;
+    using T = typename E::T;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_threads)
+        return;
+    const int64_t row = i / vec_per_row;  // b * D + d
+    const int64_t t0 = (i - row * vec_per_row) * kVT;
+    const int64_t d = row % D;
+    const int64_t base = row * L;
+
+    float win[2 * kVT];  // x[t0-8 .. t0+7]
+    if constexpr (VEC) {
+        float cur[kVT], prev[kVT];
+        load8<BF16>(x, base + t0, cur);
+        if (t0 > 0) {
+            load8<BF16>(x, base + t0 - kVT, prev);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kVT; ++k)
+                prev[k] = 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < kVT; ++k) {
+            win[k] = prev[k];
+            win[kVT + k] = cur[k];
+        }
+    } else {
+        const T *xr = reinterpret_cast<const T *>(x) + base;
+#pragma unroll
+        for (int k = 0; k < 2 * kVT; ++k) {
+            const int64_t t = t0 - kVT + k;
+            win[k] = (t >= 0 && t < L) ? E::load(xr + t) : 0.f;
+        }
+    }
+
+    const float bv = bias ? bias[d] : 0.f;
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        wk[k] = w[d * K + k];
+    float res[kVT];
+#pragma unroll
+    for (int j = 0; j < kVT; ++j) {
+        // tap k multiplies x[t - (K-1) + k], i.e. window index kVT + j - (K-1) + k
+        float acc = bv;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            acc = fmaf(wk[k], win[kVT + j - (K - 1) + k], acc);
+        res[j] = silu_hw(acc);
+    }
+
+    if constexpr (VEC) {
+        store8<BF16>(out, base + t0, res);
+    } else {
+        T *orow = reinterpret_cast<T *>(out) + base;
+#pragma unroll
+        for (int j = 0; j < kVT; ++j)
+            if (t0 + j < L)
+                E::store(orow + t0 + j, res[j]);
+    }
+}
+
+template <bool BF16, int K>
+hipError_t launch_typed(const ConvArgs &a, hipStream_t s)
+{
+    const int64_t vpr = (a.L + kVT - 1) / kVT;
+    const int64_t n = a.B * a.D * vpr;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    const bool vec = (a.L % kVT == 0) && (((uintptr_t)a.x | (uintptr_t)a.out) % 16 == 0);
+    if (vec)
+        hipLaunchKernelGGL((conv1d_silu_kernel<BF16, true, K>), dim3(blocks), dim3(256), 0, s,
+                           a.x, a.w, a.bias, a.out, a.D, a.L, vpr, n);
+    else
+        hipLaunchKernelGGL((conv1d_silu_kernel<BF16, false, K>), dim3(blocks), dim3(256), 0, s,
+                           a.x, a.w, a.bias, a.out, a.D, a.L, vpr, n);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_k(const ConvArgs &a, hipStream_t s)
+{
+    switch (a.K) {
+    case 1: return launch_typed<BF16, 1>(a, s);
+    case 2: return launch_typed<BF16, 2>(a, s);
+    case 3: return launch_typed<BF16, 3>(a, s);
+    case 4: return launch_typed<BF16, 4>(a, s);
+    case 5: return launch_typed<BF16, 5>(a, s);
+    case 6: return launch_typed<BF16, 6>(a, s);
+    case 7: return launch_typed<BF16, 7>(a, s);
+    case 8: return launch_typed<BF16, 8>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_silu(const ConvArgs &a, hipStream_t s)
+{
+    if (a.B * a.D * a.L == 0)
+        return hipSuccess;
+    return a.bf16 ? launch_k<true>(a, s) : launch_k<false>(a, s);
+}
+
+}  // namespace mamba

@@ -1,0 +1,57 @@
+// Device-side helpers shared by the kernels: element conversion and the
+// hardware transcendental instructions of gfx950 (v_exp_f32 = 2^x,
+// v_log_f32 = log2 x, v_rcp_f32 = 1/x).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mamba {
+
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : r;
+}
+
+// Element load / store for the two I/O types.
+template <bool BF16> struct Elem;
+template <> struct Elem<false> {
+    using T = float;
+    static __device__ __forceinline__ float load(const T *p) { return *p; }
+    static __device__ __forceinline__ void store(T *p, float v) { *p = v; }
+};
+template <> struct Elem<true> {
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const T *p) { return bf16_bits_to_f32(*p); }
+    static __device__ __forceinline__ void store(T *p, float v) {
+        *p = (uint16_t)f32_to_bf16_bits(v);
+    }
+};
+
+// z * sigmoid(z) with the hardware exp2 / rcp.
+__device__ __forceinline__ float silu_hw(float z) {
+    return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));
+}
+
+// softplus(v) in log2 units: log2(1 + 2^v2) for v2 = v * log2(e).  Above
+// 2^25 the 1 no longer changes 1 + 2^v2 in fp32, so the value is v2 itself
+// (this also keeps 2^v2 from overflowing).
+__device__ __forceinline__ float softplus_log2(float v2) {
+    float l = hw_log2(1.0f + hw_exp2(v2));
+    return v2 > 25.0f ? v2 : l;
+}
+
+}  // namespace mamba

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host API (api.cpp) and the kernel
+// translation units.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mamba {
+
+// ---- selective scan geometry -------------------------------------------------
+// One wave (64 lanes) owns 64 consecutive channels of one batch row and walks a
+// chunk of kChunkT time steps; kWavesPerSeg waves of a workgroup walk
+// consecutive chunks, so a workgroup covers a segment of kSegT steps.
+constexpr int kWave = 64;
+constexpr int kChunkT = 32;
+constexpr int kWavesPerSeg = 4;
+constexpr int kSegT = kChunkT * kWavesPerSeg;
+constexpr int kMaxN = 16;
+constexpr int kAggFields = kMaxN + 1;  // decay summary + N states
+constexpr int kInclFields = kMaxN;
+constexpr int kBCStride = 3 * kMaxN;   // prepared per-(b,t) row: B, C/(n+1), C
+
+// Byte offsets of the parts of the scan workspace for one problem shape.
+struct ScanWsLayout {
+    int64_t n_dtiles = 0;  // ceil(D / 64)
+    int64_t groups = 0;    // B * n_dtiles
+    int64_t n_seg = 0;     // ceil(L / kSegT)
+    int64_t n_items = 0;   // groups * n_seg
+    size_t off_header = 0, off_flags = 0, off_tiles = 0, off_bc = 0, off_agg = 0,
+           off_incl = 0, total = 0;
+};
+ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L);
+
+struct ScanArgs {
+    const void *x, *dt, *Bm, *Cm, *z;
+    const float *dt_bias, *A, *Dskip, *h0;
+    void *y;
+    float *h_last;
+    unsigned char *ws;
+    ScanWsLayout lay;
+    int64_t B, D, L;
+    int N;
+    bool bf16;
+    hipEvent_t ev_start, ev_stop;  // optional timing of the main kernel
+};
+hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s);
+
+struct ConvArgs {
+    const void *x;
+    const float *w, *bias;
+    void *out;
+    int64_t B, D, L;
+    int K;
+    bool bf16;
+};
+hipError_t launch_conv1d_silu(const ConvArgs &a, hipStream_t s);
+
+struct StepArgs {
+    float *h;
+    const void *x, *dt, *Bm, *Cm, *z;
+    const float *dt_bias, *A, *Dskip;
+    void *y;
+    int64_t B, D;
+    int N;
+    bool bf16;
+};
+hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
+
+}  // namespace mamba

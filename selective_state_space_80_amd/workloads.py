@@ -68,14 +68,11 @@ WORKLOADS = {
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 (ties to even); return float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32)
-    # NaN stays NaN (not produced by these generators, kept for completeness)
-    return np.where(np.isnan(a), a, out)
+    """Round float32 values to the nearest bf16 (ties to even) with torch's
+    conversion; return them as float32."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
 def _normal(rng, shape, std=1.0):

