@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+held in HBM: causal depthwise conv1d(k=4) + SiLU, then the fused selective
+scan (softplus step, ZOH, recurrence, readout, D skip, SiLU(z) gate), on the
+Mamba block at d_model=768 (B=2, D_inner=1536, L=8192, N=16, fp32 I/O).
+
+Prints ONE JSON line with the metric (scanned Gelem/s = B*L*D_inner / step
+time), the roofline of the dominant kernel (the main scan kernel, timed with
+HIP events on its own stream through the library's timing hook) and the fp64
+oracle timed on a bounded sample of the same workload on the host cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # fp32 VALU lane-ops/s without packed math
+SCAN_SRC = os.path.join(ROOT, "selective_state_space_80_amd", "csrc", "scan_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def scan_bytes(B, D, L, N, esz, gate=True, last_state=False):
+    """Algorithmic HBM bytes of one scan: x, dt (and z) read once, y written
+    once, B and C read once per (b, t), A/D/dt_bias once, h_last if returned."""
+    per_elem = (3 if gate else 2) * esz + esz
+    return (B * D * L * per_elem + 2 * B * L * N * esz + D * N * 4 + 2 * D * 4
+            + (B * D * N * 4 if last_state else 0))
+
+
+def conv_bytes(B, D, L, K, esz):
+    return 2 * B * D * L * esz + D * K * 4
+
+
+def traffic_record():
+    """HBM traffic of the main scan kernel measured by rocprofv3 counters, if
+    taken on the current kernel source (else None)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+    return rec if rec.get("scan_fwd_sha256") == sha else None
+
+
+def cpu_baseline(p, B, D, L, target_s=12.0):
+    """The fp64 oracle (conv then scan) on a bounded sample of the workload:
+    whole sequences of the first channels of batch row 0."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    # calibrate on a few channels, then size the sample for ~target_s
+    t0 = time.perf_counter()
+    ch = 8
+    xs = oracle.conv1d_silu(p["x_raw"][:1, :ch], p["conv_w"][:ch])
+    oracle.selective_scan(xs, p["dt"][:1, :ch], p["A"][:ch], p["Bm"][:1], p["Cm"][:1],
+                          p["dt_bias"][:ch], p["Dskip"][:ch], p["z"][:1, :ch], nthreads=threads)
+    per_ch = (time.perf_counter() - t0) / ch
+    ch = int(max(threads, min(D, target_s * threads / max(per_ch, 1e-9))))
+    ch = max(threads, ch // threads * threads)
+    t0 = time.perf_counter()
+    xs = oracle.conv1d_silu(p["x_raw"][:1, :ch], p["conv_w"][:ch])
+    oracle.selective_scan(xs, p["dt"][:1, :ch], p["A"][:ch], p["Bm"][:1], p["Cm"][:1],
+                          p["dt_bias"][:ch], p["Dskip"][:ch], p["z"][:1, :ch], nthreads=threads)
+    dt = time.perf_counter() - t0
+    elems = ch * L
+    return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"batch row 0, channels 0..{ch - 1} of {D}, all {L} steps "
+                      f"(conv1d+SiLU then scan, fp64, {threads} threads; {elems} elements)"}
+
+
+def run_block(args, torch, mamba, W):
+    wl = W.WORKLOADS[1]
+    B, D, L, N = wl.B, wl.D, wl.L, wl.N
+    p = W.scan_inputs(wl)
+    dev = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x_raw, cw = T(p["x_raw"]), T(p["conv_w"])
+    dt, A, Bm, Cm = T(p["dt"]), T(p["A"]), T(p["Bm"]), T(p["Cm"])
+    bias, Dk, z = T(p["dt_bias"]), T(p["Dskip"]), T(p["z"])
+    xc = torch.empty_like(x_raw)
+    y = torch.empty_like(x_raw)
+    ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        mamba.conv1d_silu(x_raw, cw, None, out=xc)
+        mamba.selective_scan_fwd(xc, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    conv_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mamba.set_scan_timing_events_raw(pairs[i][0], pairs[i][1])
+        conv_ev[i][0].record()
+        mamba.conv1d_silu(x_raw, cw, None, out=xc)
+        conv_ev[i][1].record()
+        mamba.selective_scan_fwd(xc, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mamba.set_scan_timing_events_raw(None, None)
+    scan_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    conv_ms = float(np.mean([a.elapsed_time(b) for a, b in conv_ev]))
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    ms_step = elapsed / args.steps * 1e3
+    elems = B * D * L
+    sb = scan_bytes(B, D, L, N, 4)
+    cb = conv_bytes(B, D, L, 4, 4)
+    achieved = sb / (scan_ms * 1e-3) / 1e9
+    tr = traffic_record()
+    traffic = None
+    if tr is not None:
+        traffic = round((tr["fetch_bytes"] + tr["write_bytes"]), 0)
+    out = {
+        "metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
+        "value": round(elems / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "d_model": 768, "d_inner": D, "seq_len": L,
+                   "d_state": N, "d_conv": 4, "io": "f32", "state": "f32",
+                   "step": "conv1d_silu + selective_scan_fwd"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "scan_main_kernel<fp32>",
+                     "kernel_ms": round(scan_ms, 4),
+                     "algorithmic_bytes": sb},
+        "kernels": {"scan_ms": round(scan_ms, 4),
+                    "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2),
+                    "conv_ms": round(conv_ms, 4),
+                    "conv_GBps": round(cb / (conv_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(p, B, D, L)
+    return out
+
+
+def run_scan(args, torch, mamba, W, idx):
+    wl = W.WORKLOADS[idx]
+    B, D, L, N = wl.B, wl.D, wl.L, wl.N
+    p = W.scan_inputs(wl)
+    dev = torch.device("cuda:0")
+    bf = wl.io == "bf16"
+    io_t = torch.bfloat16 if bf else torch.float32
+    T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    x, dt, z = T(p["x"], io_t), T(p["dt"], io_t), T(p["z"], io_t)
+    Bm, Cm = T(p["Bm"], io_t), T(p["Cm"], io_t)
+    A, bias, Dk = T(p["A"]), T(p["dt_bias"]), T(p["Dskip"])
+    y = torch.empty_like(x)
+    ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(args.warmup):
+        mamba.selective_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mamba.set_scan_timing_events_raw(pairs[i][0], pairs[i][1])
+        mamba.selective_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mamba.set_scan_timing_events_raw(None, None)
+    scan_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    ms_step = elapsed / args.steps * 1e3
+    elems = B * D * L
+    sb = scan_bytes(B, D, L, N, 2 if bf else 4)
+    achieved = sb / (scan_ms * 1e-3) / 1e9
+    return {"metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
+            "value": round(elems / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16-io/f32", "data": "synthetic",
+            "config": {"workload": wl.name, "batch": B, "d_inner": D, "seq_len": L,
+                       "d_state": N, "io": wl.io},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel_ms": round(scan_ms, 4)},
+            "kernels": {"scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}}
+
+
+def run_decode(args, torch, mamba, W):
+    wl = W.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    init = W.decode_initial(wl)
+    T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    h = T(init["h0"])
+    A, bias, Dk = T(init["A"]), T(init["dt_bias"]), T(init["Dskip"])
+    toks = []
+    for s in range(8):
+        st = W.decode_step_inputs(wl, s)
+        toks.append({k: T(v, torch.bfloat16) for k, v in st.items()})
+    y = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        t = toks[i % len(toks)]
+        mamba.selective_state_update(h, t["x"], t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"],
+                                     out=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = wl.B * wl.D * (2 * wl.N * 4 + 4 * 2) + wl.B * 2 * wl.N * 2 + wl.D * (wl.N + 2) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "decode state update GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16-io/f32", "data": "synthetic",
+            "config": {"workload": wl.name, "batch": wl.B, "d_inner": wl.D, "d_state": wl.N},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "note": "state (84 MB) stays resident in the 256 MB MALL between steps"}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="block",
+                    choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the hot path "
+              "shards over batch/channels with no communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import selective_state_space_80_amd as mamba
+    from selective_state_space_80_amd import workloads as W
+
+    mamba.load_library()
+    if args.workload == "block":
+        out = run_block(args, torch, mamba, W)
+    elif args.workload == "scan_bf16_l2048":
+        out = run_scan(args, torch, mamba, W, 2)
+    elif args.workload == "scan_bf16_l131072":
+        out = run_scan(args, torch, mamba, W, 3)
+    else:
+        out = run_decode(args, torch, mamba, W)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -208,12 +208,12 @@ def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None
     return out
 
 
-def set_scan_timing_events(start=None, stop=None):
-    """Record torch.cuda.Event pair around the main scan kernel of later calls
-    from this thread (None, None turns it off)."""
+def set_scan_timing_events_raw(start=None, stop=None):
+    """Have later scan calls from this thread record the raw hipEvent_t
+    handles `start` / `stop` (ctypes.c_void_p) around their main kernel, on the
+    call's stream.  None, None turns it off."""
     lib = load_library()
     if start is None or stop is None:
         lib.mamba_set_scan_timing_events(None, None)
     else:
-        lib.mamba_set_scan_timing_events(ctypes.c_void_p(start.cuda_event),
-                                         ctypes.c_void_p(stop.cuda_event))
+        lib.mamba_set_scan_timing_events(start, stop)

@@ -18,11 +18,18 @@
 //   * The end state of a chunk is an affine map h -> P h + S of its start state
 //     (the block-wise scan with a prefix state handed to later blocks,
 //     "Mamba: Linear-Time Sequence Modeling with Selective SSMs", selective scan
-//     section).  Chunk maps are combined in LDS inside the workgroup, and across
-//     workgroups by a decoupled look-back over per-segment records in the
-//     workspace (Merrill & Garland 2016: aggregate first, inclusive prefix once
-//     known).  Segment ids come from an atomic ticket, so every segment a wave
-//     waits for has already started: no deadlock whatever the dispatch order.
+//     section).  Chunk maps are combined in LDS inside the workgroup.  Across
+//     workgroups every segment publishes its map (an aggregate record) in the
+//     workspace; segments are grouped 16 to a superblock, and the last segment
+//     of a superblock also publishes the state at its end (an inclusive
+//     record).  A segment's start state is the previous superblock's inclusive
+//     state with the aggregates of the earlier segments of its own superblock
+//     folded on top, in a fixed order, by the 4 waves in parallel.  The
+//     association order therefore never depends on scheduling (results are
+//     bit-for-bit repeatable), and the only serial chain is one hop per
+//     superblock.  Segment ids come from an atomic ticket, so every segment a
+//     wave waits for has already started: no deadlock whatever the dispatch
+//     order.
 //   * Once a chunk knows its true start state h_in, each kept output gets the
 //     missing term sum_n C_tn * (prod_(s<=t) Ā_sn) * h_in,n added, then the
 //     gate, then one store.  Every input element is read once, y written once.
@@ -57,6 +64,7 @@ constexpr uint32_t kPathStructured = 0u;
 constexpr uint32_t kPathGeneral = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
 constexpr int kSpinLimit = 1 << 22;
+constexpr int64_t kSuperSeg = 16;  // segments per superblock of the carry
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -200,15 +208,30 @@ __device__ __forceinline__ void store_chunk(void *base, int64_t off, int nt, boo
     }
 }
 
+// Carry records between workgroups.  Every record word and every flag is
+// accessed with agent-scope relaxed atomics, which are coherent across the
+// XCDs' L2 caches without whole-cache write-back or invalidation.  A writer
+// waits until all of its record stores have completed (vmcnt = 0) before it
+// stores the flag; a reader loads record words only after it has seen the
+// flag, so it reads this call's values.
 __device__ __forceinline__ uint32_t load_flag(const uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ float load_rec(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_rec(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void publish_flag(uint32_t *p, uint32_t v, int lane)
 {
-    // all lanes' record stores become visible at agent scope before the flag
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0)
         __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -257,7 +280,8 @@ template <bool BF16, bool STRUCT>
 __device__ __forceinline__ void scan_segment(
     const ScanKArgs &p, const float *__restrict__ bcp, uint32_t *__restrict__ flags,
     float *__restrict__ agg, float *__restrict__ incl, WsHeader *hdr, int64_t seg, int64_t g,
-    int w, int lane, float (*s_agg)[kAggFields][kWave], float (*s_hin)[kWave])
+    int w, int lane, float (*s_agg)[kAggFields][kWave], float (*s_part)[kAggFields][kWave],
+    float (*s_hin)[kWave], int *s_ctl)
 {
     const ScanWsLayout &lay = p.lay;
     const int64_t G = lay.groups;
@@ -365,6 +389,12 @@ __device__ __forceinline__ void scan_segment(
         }
     }
 
+    // z is only needed by the final gating: start its loads now so they are in
+    // flight while the workgroup resolves its start state
+    float zr[kChunkT];
+    if (p.z && nt > 0)
+        load_chunk<BF16>(p.z, row_off, nt, vec, zr);
+
     // ---- 2. combine chunk maps inside the workgroup ------------------------
     s_agg[w][0][lane] = summ;
 #pragma unroll
@@ -372,10 +402,14 @@ __device__ __forceinline__ void scan_segment(
         s_agg[w][1 + n][lane] = hs[n];
     __syncthreads();
 
+    // ---- 3. find which earlier segments' records give this segment's start --
+    //  sI     : nearest earlier segment with an inclusive (start-resolved) record,
+    //           -1 meaning "the initial state h0"
+    //  depth  : number of segments after sI (up to seg-1) whose aggregates
+    //           must be folded on top of it
+    float F = 0.f, Sg[kMaxN];
     if (w == 0) {
-        // segment map = chunk maps of waves 0..3 composed in time order
-        float F = s_agg[0][0][lane];
-        float Sg[kMaxN];
+        F = s_agg[0][0][lane];
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             Sg[n] = s_agg[0][1 + n][lane];
@@ -389,99 +423,133 @@ __device__ __forceinline__ void scan_segment(
                 Sg[n] = fmaf(P[n], Sg[n], s_agg[k][1 + n][lane]);
             F = combine_summary<STRUCT>(F, fk);
         }
-
-        // ---- 3. start state of the segment --------------------------------
-        float hin[kMaxN];
-        if (seg == 0) {
+        // Fixed association order, independent of scheduling: a segment folds
+        // the aggregates of the earlier segments of its superblock, in order,
+        // onto the inclusive state that ends the previous superblock.
+        const int64_t sI = (seg / kSuperSeg) * kSuperSeg - 1;  // -1 = h0
+        const int64_t depth = seg - 1 - sI;
+        if (seg + 1 < lay.n_seg) {
+            // successors in this superblock fold this segment's aggregate
+            float *rec = agg + item * (kAggFields * kWave);
+            store_rec(rec + lane, F);
 #pragma unroll
             for (int n = 0; n < kMaxN; ++n)
-                hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
-        } else {
-            const uint32_t *fl_g = flags + g;  // flag of segment s at fl_g[s * G]
-            const uint32_t pred = load_flag(fl_g + (seg - 1) * G);
-            if (pred != kFlagIncl) {
-                // publish this segment's aggregate so successors need not wait
-                float *rec = agg + item * (kAggFields * kWave);
-                rec[lane] = F;
-#pragma unroll
-                for (int n = 0; n < kMaxN; ++n)
-                    rec[(1 + n) * kWave + lane] = Sg[n];
-                publish_flag(flags + item, kFlagAgg, lane);
-            }
-            // decoupled look-back: lane j watches predecessor seg-1-k0-j
-            int64_t depth = -1;  // distance (0 = seg-1) of the nearest inclusive record
-            int64_t k0 = 0;
+                store_rec(rec + (1 + n) * kWave + lane, Sg[n]);
+            publish_flag(flags + item, kFlagAgg, lane);
+        }
+        if (seg > 0) {
+            // wait until the records this segment folds are all published:
+            // lane j < depth watches segment seg-1-j (aggregate), lane `depth`
+            // watches segment sI (inclusive state; none needed when sI < 0)
+            const int64_t s = seg - 1 - lane;
+            uint32_t want = 0u;
+            if (lane < depth)
+                want = kFlagAgg;
+            else if (lane == depth && sI >= 0)
+                want = kFlagIncl;
             int spins = 0;
             for (;;) {
-                const int64_t s = seg - 1 - k0 - lane;
-                const uint32_t f = (s >= 0) ? load_flag(fl_g + s * G) : kFlagIncl;
-                const uint64_t incl_m = __ballot(f == kFlagIncl);
-                const uint64_t ready_m = __ballot(f != 0u);
-                if (incl_m) {
-                    const int js = __builtin_ctzll(incl_m);
-                    const uint64_t need = (js >= 63) ? ~0ull : ((2ull << js) - 1ull);
-                    if ((ready_m & need) == need) {
-                        depth = k0 + js;
-                        break;
-                    }
-                } else if (ready_m == ~0ull) {
-                    k0 += kWave;
-                    continue;
-                }
-                if (++spins > kSpinLimit) {
+                const uint32_t f = want ? load_flag(flags + s * G + g) : 0u;
+                if (__ballot(f < want) == 0ull)
+                    break;
+                if (++spins > kSpinLimit) {  // never expected; keeps the kernel finite
                     if (lane == 0)
                         atomicOr(&hdr->error, kErrSpinTimeout);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            if (depth < 0) {
-#pragma unroll
-                for (int n = 0; n < kMaxN; ++n)
-                    hin[n] = 0.f;
-            } else {
-                const int64_t sI = seg - 1 - depth;
-                if (sI < 0) {
-#pragma unroll
-                    for (int n = 0; n < kMaxN; ++n)
-                        hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
-                } else {
-                    const float *rec = incl + (sI * G + g) * (kInclFields * kWave);
-#pragma unroll
-                    for (int n = 0; n < kMaxN; ++n)
-                        hin[n] = rec[n * kWave + lane];
-                }
-                for (int64_t s2 = sI + 1; s2 <= seg - 1; ++s2) {
-                    const float *rec = agg + (s2 * G + g) * (kAggFields * kWave);
-                    float P[kMaxN];
-                    decay_factors<STRUCT>(rec[lane], Ar, P);
-#pragma unroll
-                    for (int n = 0; n < kMaxN; ++n)
-                        hin[n] = fmaf(P[n], hin[n], rec[(1 + n) * kWave + lane]);
-                }
-            }
         }
-        // ---- 4. publish the inclusive state of the segment -----------------
-        {
+        if (lane == 0) {
+            s_ctl[0] = sI;
+            s_ctl[1] = depth;
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. fold the predecessors' aggregates, four waves in parallel --------
+    const int64_t sI = __builtin_amdgcn_readfirstlane((int)s_ctl[0]);
+    const int64_t depth = __builtin_amdgcn_readfirstlane((int)s_ctl[1]);
+    {
+        const int64_t per = (depth + kWavesPerSeg - 1) / kWavesPerSeg;
+        const int64_t lo = min(depth, (int64_t)w * per), hi = min(depth, lo + per);
+        float pf = STRUCT ? 1.f : 0.f;  // identity map
+        float ps[kMaxN];
+#pragma unroll
+        for (int n = 0; n < kMaxN; ++n)
+            ps[n] = 0.f;
+        for (int64_t j = lo; j < hi; j += 2) {
+            // two records per round trip; records are in time order
+            const bool two = j + 1 < hi;
+            const float *r0 = agg + ((sI + 1 + j) * G + g) * (kAggFields * kWave);
+            const float *r1 = two ? r0 + G * (kAggFields * kWave) : r0;
+            float f0 = load_rec(r0 + lane), f1 = load_rec(r1 + lane);
+            float v0[kMaxN], v1[kMaxN];
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n) {
+                v0[n] = load_rec(r0 + (1 + n) * kWave + lane);
+                v1[n] = load_rec(r1 + (1 + n) * kWave + lane);
+            }
             float P[kMaxN];
-            decay_factors<STRUCT>(F, Ar, P);
-            float hout[kMaxN];
+            decay_factors<STRUCT>(f0, Ar, P);
 #pragma unroll
             for (int n = 0; n < kMaxN; ++n)
-                hout[n] = fmaf(P[n], hin[n], Sg[n]);
-            if (seg + 1 < lay.n_seg) {
-                float *rec = incl + item * (kInclFields * kWave);
+                ps[n] = fmaf(P[n], ps[n], v0[n]);
+            pf = combine_summary<STRUCT>(pf, f0);
+            if (two) {
+                decay_factors<STRUCT>(f1, Ar, P);
 #pragma unroll
                 for (int n = 0; n < kMaxN; ++n)
-                    rec[n * kWave + lane] = hout[n];
-                publish_flag(flags + item, kFlagIncl, lane);
-            } else if (p.h_last && active) {
-#pragma unroll
-                for (int n = 0; n < kMaxN; ++n)
-                    if (n < p.N)
-                        p.h_last[(b * p.D + d) * p.N + n] = hout[n];
+                    ps[n] = fmaf(P[n], ps[n], v1[n]);
+                pf = combine_summary<STRUCT>(pf, f1);
             }
+        }
+        s_part[w][0][lane] = pf;
+#pragma unroll
+        for (int n = 0; n < kMaxN; ++n)
+            s_part[w][1 + n][lane] = ps[n];
+    }
+    __syncthreads();
+
+    // ---- 5. segment start state, inclusive record, per-wave start state -----
+    if (w == 0) {
+        float hin[kMaxN];
+        if (sI < 0) {
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
+        } else {
+            const float *rec = incl + (sI * G + g) * (kInclFields * kWave);
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                hin[n] = load_rec(rec + n * kWave + lane);
+        }
+#pragma unroll
+        for (int k = 0; k < kWavesPerSeg; ++k) {
+            float P[kMaxN];
+            decay_factors<STRUCT>(s_part[k][0][lane], Ar, P);
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                hin[n] = fmaf(P[n], hin[n], s_part[k][1 + n][lane]);
+        }
+        float P[kMaxN];
+        decay_factors<STRUCT>(F, Ar, P);
+        float hout[kMaxN];
+#pragma unroll
+        for (int n = 0; n < kMaxN; ++n)
+            hout[n] = fmaf(P[n], hin[n], Sg[n]);
+        if (seg + 1 < lay.n_seg && (seg + 1) % kSuperSeg == 0) {
+            float *rec = incl + item * (kInclFields * kWave);
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                store_rec(rec + n * kWave + lane, hout[n]);
+            publish_flag(flags + item, kFlagIncl, lane);
+        }
+        if (seg + 1 == lay.n_seg && p.h_last && active) {
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                if (n < p.N)
+                    p.h_last[(b * p.D + d) * p.N + n] = hout[n];
         }
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
@@ -492,7 +560,7 @@ __device__ __forceinline__ void scan_segment(
     if (nt <= 0)
         return;
 
-    // ---- 5. this wave's start state, fix-up, gate, store -------------------
+    // ---- 6. this wave's start state, fix-up, gate, store -------------------
     float hin[kMaxN];
 #pragma unroll
     for (int n = 0; n < kMaxN; ++n)
@@ -505,10 +573,6 @@ __device__ __forceinline__ void scan_segment(
             hin[n] = fmaf(P[n], hin[n], s_agg[k][1 + n][lane]);
     }
     const bool zero_start = (seg == 0 && w == 0 && p.h0 == nullptr);
-
-    float zr[kChunkT];
-    if (p.z)
-        load_chunk<BF16>(p.z, row_off, nt, vec, zr);
 
     if constexpr (STRUCT) {
         // coefficient of the carried state in scaled units: (n+1) A_0 h_in,n
@@ -561,11 +625,13 @@ __device__ __forceinline__ void scan_segment(
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kWave *kWavesPerSeg) scan_main_kernel(
+__global__ void __launch_bounds__(kWave *kWavesPerSeg, 3) scan_main_kernel(
     ScanKArgs p, const float *__restrict__ bcp, const uint32_t *__restrict__ tiles)
 {
     __shared__ float s_agg[kWavesPerSeg][kAggFields][kWave];
+    __shared__ float s_part[kWavesPerSeg][kAggFields][kWave];
     __shared__ float s_hin[kMaxN][kWave];
+    __shared__ int s_ctl[2];
     __shared__ uint32_t s_ticket;
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(p.ws + p.lay.off_header);
@@ -584,10 +650,11 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg) scan_main_kernel(
     const int64_t dtile = g % p.lay.n_dtiles;
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
-        scan_segment<BF16, true>(p, bcp, flags, agg, incl, hdr, seg, g, w, lane, s_agg, s_hin);
+        scan_segment<BF16, true>(p, bcp, flags, agg, incl, hdr, seg, g, w, lane, s_agg, s_part,
+                                 s_hin, s_ctl);
     else
         scan_segment<BF16, false>(p, bcp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
-                                  s_hin);
+                                  s_part, s_hin, s_ctl);
 }
 
 // Writes h_last = h0 (or zeros) for an empty sequence (L == 0).
