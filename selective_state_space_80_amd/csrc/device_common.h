@@ -47,10 +47,10 @@ __device__ __forceinline__ float silu_hw(float z) {
 }
 
 // softplus(v) in log2 units: log2(1 + 2^v2) for v2 = v * log2(e).  Above
-// 2^25 the 1 no longer changes 1 + 2^v2 in fp32, so the value is v2 itself
-// (this also keeps 2^v2 from overflowing).
+// v2 = 25 the 1 no longer changes 1 + 2^v2 in fp32, so the value is v2 itself;
+// taking it directly also keeps 2^v2 from overflowing to +inf for v2 >= 128.
 __device__ __forceinline__ float softplus_log2(float v2) {
-    float l = hw_log2(1.0f + hw_exp2(v2));
+    const float l = hw_log2(1.0f + hw_exp2(v2));
     return v2 > 25.0f ? v2 : l;
 }
 

@@ -70,13 +70,15 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
 // Prep kernel: clears the ticket and the per-segment flags, converts B and C
-// to fp32 rows [B | C/(n+1) | C] (16 entries each, zero past N), and decides
+// to fp32 rows [B | C/(n+1)] of exactly 128 bytes plus a separate array of C
+// (16 entries each, zero past N; zero rows pad
+// each batch row to a whole number of segments), and decides
 // per 64-channel tile whether A has the structured form.
 template <bool BF16>
 __global__ void __launch_bounds__(256) scan_prep_kernel(
     const void *__restrict__ Bm_, const void *__restrict__ Cm_, const float *__restrict__ A,
-    unsigned char *__restrict__ ws, ScanWsLayout lay, int64_t D, int N, int64_t n_zero,
-    int64_t n_bc, int64_t classify_base)
+    unsigned char *__restrict__ ws, ScanWsLayout lay, int64_t D, int64_t L, int N,
+    int64_t n_zero, int64_t n_bc, int64_t classify_base)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
@@ -93,17 +95,19 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(
     }
     if (i < n_zero + n_bc) {
         const int64_t k = i - n_zero;
-        const int64_t row = k / kMaxN;  // b * L + t
+        const int64_t row = k / kMaxN;  // b * Lpad + t
         const int n = (int)(k % kMaxN);
+        const int64_t Lpad = lay.n_seg * kSegT;
+        const int64_t b = row / Lpad, t = row - b * Lpad;
         float bv = 0.f, cv = 0.f;
-        if (n < N) {
-            bv = E::load(reinterpret_cast<const T *>(Bm_) + row * N + n);
-            cv = E::load(reinterpret_cast<const T *>(Cm_) + row * N + n);
+        if (n < N && t < L) {
+            bv = E::load(reinterpret_cast<const T *>(Bm_) + (b * L + t) * N + n);
+            cv = E::load(reinterpret_cast<const T *>(Cm_) + (b * L + t) * N + n);
         }
         float *bc = reinterpret_cast<float *>(ws + lay.off_bc) + row * kBCStride;
         bc[n] = bv;
         bc[kMaxN + n] = cv / (float)(n + 1);
-        bc[2 * kMaxN + n] = cv;
+        reinterpret_cast<float *>(ws + lay.off_craw)[row * kMaxN + n] = cv;
         return;
     }
     const int64_t c = i - classify_base;  // classify region starts on a wave boundary
@@ -126,9 +130,12 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(
 // ---------------------------------------------------------------------------
 // Per-lane chunk I/O: 32 consecutive time steps of one row.  `vec` means the
 // chunk is full and the row is 16-byte aligned, so 128-bit loads are used.
+// Steps at or past L are filled with `pad` and never stored: padding x with 0
+// and dt with -inf makes such a step an exact identity of the recurrence
+// (step 0, decay 1, no input), so the step loops need no per-step branches.
 template <bool BF16>
 __device__ __forceinline__ void load_chunk(const void *base, int64_t off, int nt, bool vec,
-                                           float (&v)[kChunkT])
+                                           float (&v)[kChunkT], float pad = 0.f)
 {
     if constexpr (!BF16) {
         const float *p = reinterpret_cast<const float *>(base) + off;
@@ -145,7 +152,7 @@ __device__ __forceinline__ void load_chunk(const void *base, int64_t off, int nt
         } else {
 #pragma unroll
             for (int i = 0; i < kChunkT; ++i)
-                v[i] = (i < nt) ? p[i] : 0.f;
+                v[i] = (i < nt) ? p[i] : pad;
         }
     } else {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + off;
@@ -164,7 +171,7 @@ __device__ __forceinline__ void load_chunk(const void *base, int64_t off, int nt
         } else {
 #pragma unroll
             for (int i = 0; i < kChunkT; ++i)
-                v[i] = (i < nt) ? bf16_bits_to_f32(p[i]) : 0.f;
+                v[i] = (i < nt) ? bf16_bits_to_f32(p[i]) : pad;
         }
     }
 }
@@ -278,7 +285,8 @@ __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 // The whole per-workgroup body for one arithmetic path.
 template <bool BF16, bool STRUCT>
 __device__ __forceinline__ void scan_segment(
-    const ScanKArgs &p, const float *__restrict__ bcp, uint32_t *__restrict__ flags,
+    const ScanKArgs &p, const float *__restrict__ bcp, const float *__restrict__ crp,
+    uint32_t *__restrict__ flags,
     float *__restrict__ agg, float *__restrict__ incl, WsHeader *hdr, int64_t seg, int64_t g,
     int w, int lane, float (*s_agg)[kAggFields][kWave], float (*s_part)[kAggFields][kWave],
     float (*s_hin)[kWave], int *s_ctl)
@@ -292,10 +300,17 @@ __device__ __forceinline__ void scan_segment(
     const bool active = d < p.D;
     const int64_t dc = active ? d : (p.D - 1);  // inactive lanes read a valid row
     const int64_t t0 = seg * kSegT + (int64_t)w * kChunkT;
-    const int nt = (int)max((int64_t)0, min((int64_t)kChunkT, p.L - t0));
+    const int nt = __builtin_amdgcn_readfirstlane((int)max((int64_t)0, min((int64_t)kChunkT, p.L - t0)));
     const bool vec = p.vec && nt == kChunkT;
     const int64_t row_off = (b * p.D + dc) * p.L + t0;
-    const float *bcrow = bcp + (b * p.L + t0) * kBCStride;
+    // prepared B/C rows exist (as zeros) up to the padded length n_seg*kSegT
+    const float *bcrow = bcp + (b * lay.n_seg * kSegT + t0) * kBCStride;
+    const float *crow = crp + (b * lay.n_seg * kSegT + t0) * kMaxN;
+    // Bring this chunk's 32 B/C rows (one 128-byte line each) into L2 with a
+    // single vector load (lane l touches half l/32 of row l%32), issued with
+    // the x/dt loads.  The per-step scalar loads then hit L2 instead of each
+    // paying a full memory latency.
+    const float warm = bcrow[(lane & 31) * kBCStride + (lane >> 5) * kMaxN];
 
     // per-channel constants
     const float bias2 = (p.dt_bias ? p.dt_bias[dc] : 0.f) * kLog2e;
@@ -320,10 +335,8 @@ __device__ __forceinline__ void scan_segment(
     float summ;
     {
         float xr[kChunkT], dr[kChunkT];
-        if (nt > 0) {
-            load_chunk<BF16>(p.x, row_off, nt, vec, xr);
-            load_chunk<BF16>(p.dt, row_off, nt, vec, dr);
-        }
+        load_chunk<BF16>(p.x, row_off, nt, vec, xr, 0.f);
+        load_chunk<BF16>(p.dt, row_off, nt, vec, dr, -__builtin_huge_valf());
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             hs[n] = 0.f;
@@ -331,8 +344,8 @@ __device__ __forceinline__ void scan_segment(
             float E = 1.f;
 #pragma unroll
             for (int j = 0; j < kChunkT; ++j) {
-                if (j < nt) {
-                    const float *bc = bcrow + j * kBCStride;
+                if (j < nt) {  // one basic block per step
+                    const float *bc = bcrow + j * kBCStride;  // B, C/(n+1): scalar loads
                     const float l = softplus_log2(fmaf(dr[j], kLog2e, bias2));  // Δ/ln2
                     const float e1 = hw_exp2(a0 * l);                            // exp(Δ A_0)
                     const float xv = xr[j];
@@ -342,15 +355,12 @@ __device__ __forceinline__ void scan_segment(
                         if (n)
                             en *= e1;
                         const float pn = bc[n] * xv;
-                        const float s = hs[n] + pn;
-                        hs[n] = fmaf(en, s, -pn);
+                        const float sn = hs[n] + pn;
+                        hs[n] = fmaf(en, sn, -pn);
                         acc = fmaf(bc[kMaxN + n], hs[n], acc);
                     }
                     E *= e1;
                     yl[j] = fmaf(acc, inva0, Dd * xv);
-                    er[j] = E;
-                } else {
-                    yl[j] = 0.f;
                     er[j] = E;
                 }
             }
@@ -365,6 +375,7 @@ __device__ __forceinline__ void scan_segment(
             for (int j = 0; j < kChunkT; ++j) {
                 if (j < nt) {
                     const float *bc = bcrow + j * kBCStride;
+                    const float *cr = crow + j * kMaxN;
                     const float l = softplus_log2(fmaf(dr[j], kLog2e, bias2));
                     const float delta = l * kLn2;
                     const float xv = xr[j];
@@ -376,18 +387,17 @@ __device__ __forceinline__ void scan_segment(
                         const float en = (an == 0.f) ? 1.f : hw_exp2(an * l);
                         const float coef = (an == 0.f) ? delta : expm1f(an * delta) / an;
                         hs[n] = fmaf(en, hs[n], coef * (bc[n] * xv));
-                        acc = fmaf(bc[2 * kMaxN + n], hs[n], acc);
+                        acc = fmaf(cr[n], hs[n], acc);
                     }
                     yl[j] = fmaf(Dd, xv, acc);
-                    er[j] = cumL;
-                } else {
-                    yl[j] = 0.f;
                     er[j] = cumL;
                 }
             }
             summ = cumL;
         }
     }
+
+    __asm__ volatile("" ::"v"(warm));  // the warm-up load's value is not needed
 
     // z is only needed by the final gating: start its loads now so they are in
     // flight while the workgroup resolves its start state
@@ -573,6 +583,11 @@ __device__ __forceinline__ void scan_segment(
             hin[n] = fmaf(P[n], hin[n], s_agg[k][1 + n][lane]);
     }
     const bool zero_start = (seg == 0 && w == 0 && p.h0 == nullptr);
+    // The step conditions of the fix-up loops must not be shared with the scan
+    // loops (keeping 32 condition masks alive costs scalar registers): give the
+    // compiler a copy of nt it cannot prove equal.
+    int ntf = nt;
+    __asm__ volatile("" : "+s"(ntf));
 
     if constexpr (STRUCT) {
         // coefficient of the carried state in scaled units: (n+1) A_0 h_in,n
@@ -580,44 +595,46 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             hsc[n] = Ar[n] * hin[n];
+        if (!zero_start) {
 #pragma unroll
-        for (int j = 0; j < kChunkT; ++j) {
-            if (j < nt) {
-                float yv = yl[j];
-                if (!zero_start) {
-                    const float *bc = bcrow + j * kBCStride;
+            for (int j = 0; j < kChunkT; ++j) {
+                if (j < ntf) {
+                    const float *cs = bcrow + j * kBCStride + kMaxN;  // C/(n+1)
                     const float Ej = er[j];
-                    float q = 0.f;
+                    float qh = 0.f;
 #pragma unroll
                     for (int n = kMaxN - 1; n >= 0; --n)
-                        q = fmaf(q, Ej, bc[kMaxN + n] * hsc[n]);
-                    yv = fmaf(q * Ej, inva0, yv);
+                        qh = fmaf(qh, Ej, cs[n] * hsc[n]);
+                    yl[j] = fmaf(qh * Ej, inva0, yl[j]);
                 }
-                if (p.z)
-                    yv *= silu_hw(zr[j]);
-                yl[j] = yv;
             }
         }
-    } else {
+        if (p.z) {
 #pragma unroll
-        for (int j = 0; j < kChunkT; ++j) {
-            if (j < nt) {
-                float yv = yl[j];
-                if (!zero_start) {
-                    const float *bc = bcrow + j * kBCStride;
+            for (int j = 0; j < kChunkT; ++j)
+                yl[j] *= silu_hw(zr[j]);
+        }
+    } else {
+        if (!zero_start) {
+#pragma unroll
+            for (int j = 0; j < kChunkT; ++j) {
+                if (j < ntf) {
+                    const float *cr = crow + j * kMaxN;
                     const float Lj = er[j];
                     float corr = 0.f;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n) {
                         const float gdec = (Ar[n] == 0.f) ? 1.f : hw_exp2(Ar[n] * Lj);
-                        corr = fmaf(bc[2 * kMaxN + n] * gdec, hin[n], corr);
+                        corr = fmaf(cr[n] * gdec, hin[n], corr);
                     }
-                    yv += corr;
+                    yl[j] += corr;
                 }
-                if (p.z)
-                    yv *= silu_hw(zr[j]);
-                yl[j] = yv;
             }
+        }
+        if (p.z) {
+#pragma unroll
+            for (int j = 0; j < kChunkT; ++j)
+                yl[j] *= silu_hw(zr[j]);
         }
     }
     if (active)
@@ -626,7 +643,8 @@ __device__ __forceinline__ void scan_segment(
 
 template <bool BF16>
 __global__ void __launch_bounds__(kWave *kWavesPerSeg, 3) scan_main_kernel(
-    ScanKArgs p, const float *__restrict__ bcp, const uint32_t *__restrict__ tiles)
+    ScanKArgs p, const float *__restrict__ bcp, const float *__restrict__ crp,
+    const uint32_t *__restrict__ tiles)
 {
     __shared__ float s_agg[kWavesPerSeg][kAggFields][kWave];
     __shared__ float s_part[kWavesPerSeg][kAggFields][kWave];
@@ -650,10 +668,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, 3) scan_main_kernel(
     const int64_t dtile = g % p.lay.n_dtiles;
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
-        scan_segment<BF16, true>(p, bcp, flags, agg, incl, hdr, seg, g, w, lane, s_agg, s_part,
+        scan_segment<BF16, true>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg, s_part,
                                  s_hin, s_ctl);
     else
-        scan_segment<BF16, false>(p, bcp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, false>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
                                   s_part, s_hin, s_ctl);
 }
 
@@ -683,7 +701,9 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L)
     l.off_tiles = off;
     off = round_up(off + (size_t)l.n_dtiles * 4, 256);
     l.off_bc = off;
-    off = round_up(off + (size_t)B * (size_t)L * kBCStride * 4, 256);
+    off = round_up(off + (size_t)B * (size_t)(l.n_seg * kSegT) * kBCStride * 4, 256);
+    l.off_craw = off;
+    off = round_up(off + (size_t)B * (size_t)(l.n_seg * kSegT) * kMaxN * 4, 256);
     l.off_agg = off;
     off = round_up(off + (size_t)l.n_items * kAggFields * kWave * 4, 256);
     l.off_incl = off;
@@ -708,16 +728,16 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
         return hipSuccess;
     // prep
     const int64_t n_zero = lay.n_items > 0 ? lay.n_items : 1;
-    const int64_t n_bc = a.B * a.L * kMaxN;
+    const int64_t n_bc = a.B * lay.n_seg * kSegT * kMaxN;
     const int64_t classify_base = (n_zero + n_bc + kWave - 1) / kWave * kWave;
     const int64_t total = classify_base + lay.n_dtiles * kWave;
     const unsigned prep_blocks = (unsigned)((total + 255) / 256);
     if (a.bf16)
         hipLaunchKernelGGL(scan_prep_kernel<true>, dim3(prep_blocks), dim3(256), 0, s, a.Bm,
-                           a.Cm, a.A, a.ws, lay, a.D, a.N, n_zero, n_bc, classify_base);
+                           a.Cm, a.A, a.ws, lay, a.D, a.L, a.N, n_zero, n_bc, classify_base);
     else
         hipLaunchKernelGGL(scan_prep_kernel<false>, dim3(prep_blocks), dim3(256), 0, s, a.Bm,
-                           a.Cm, a.A, a.ws, lay, a.D, a.N, n_zero, n_bc, classify_base);
+                           a.Cm, a.A, a.ws, lay, a.D, a.L, a.N, n_zero, n_bc, classify_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -743,15 +763,16 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
                             (uintptr_t)(a.z ? a.z : a.x);
     k.vec = ((amask & 15u) == 0 && ((size_t)a.L * esz) % 16 == 0) ? 1 : 0;
     const float *bcp = reinterpret_cast<const float *>(a.ws + lay.off_bc);
+    const float *crp = reinterpret_cast<const float *>(a.ws + lay.off_craw);
     const uint32_t *tiles = reinterpret_cast<const uint32_t *>(a.ws + lay.off_tiles);
     if (a.ev_start)
         hipEventRecord(a.ev_start, s);
     if (a.bf16)
         hipLaunchKernelGGL(scan_main_kernel<true>, dim3((unsigned)lay.n_items),
-                           dim3(kWave * kWavesPerSeg), 0, s, k, bcp, tiles);
+                           dim3(kWave * kWavesPerSeg), 0, s, k, bcp, crp, tiles);
     else
         hipLaunchKernelGGL(scan_main_kernel<false>, dim3((unsigned)lay.n_items),
-                           dim3(kWave * kWavesPerSeg), 0, s, k, bcp, tiles);
+                           dim3(kWave * kWavesPerSeg), 0, s, k, bcp, crp, tiles);
     e = hipGetLastError();
     if (a.ev_stop)
         hipEventRecord(a.ev_stop, s);
