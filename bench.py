@@ -83,30 +83,38 @@ def traffic_record():
     return rec if rec.get("scan_fwd_sha256") == sha else None
 
 
-def cpu_baseline(p, B, D, L, target_s=12.0):
+def cpu_baseline(p, B, D, L, target_s=20.0):
     """The fp64 oracle (conv then scan) on a bounded sample of the workload:
-    whole sequences of the first channels of batch row 0."""
+    whole sequences of the first channels, batch row by batch row, sized for at
+    most ~target_s seconds (the whole workload when it fits)."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
-    # calibrate on a few channels, then size the sample for ~target_s
+
+    def run(b, ch):
+        xs = oracle.conv1d_silu(p["x_raw"][b:b + 1, :ch], p["conv_w"][:ch])
+        oracle.selective_scan(xs, p["dt"][b:b + 1, :ch], p["A"][:ch], p["Bm"][b:b + 1],
+                              p["Cm"][b:b + 1], p["dt_bias"][:ch], p["Dskip"][:ch],
+                              p["z"][b:b + 1, :ch], nthreads=threads)
+
     t0 = time.perf_counter()
-    ch = 8
-    xs = oracle.conv1d_silu(p["x_raw"][:1, :ch], p["conv_w"][:ch])
-    oracle.selective_scan(xs, p["dt"][:1, :ch], p["A"][:ch], p["Bm"][:1], p["Cm"][:1],
-                          p["dt_bias"][:ch], p["Dskip"][:ch], p["z"][:1, :ch], nthreads=threads)
-    per_ch = (time.perf_counter() - t0) / ch
-    ch = int(max(threads, min(D, target_s * threads / max(per_ch, 1e-9))))
-    ch = max(threads, ch // threads * threads)
+    run(0, threads)
+    per_ch = (time.perf_counter() - t0) / threads
+    budget = int(target_s / max(per_ch, 1e-9) * threads)
+    if budget >= B * D:
+        rows, ch = B, D
+    else:
+        rows, ch = 1, max(threads, min(D, budget) // threads * threads)
     t0 = time.perf_counter()
-    xs = oracle.conv1d_silu(p["x_raw"][:1, :ch], p["conv_w"][:ch])
-    oracle.selective_scan(xs, p["dt"][:1, :ch], p["A"][:ch], p["Bm"][:1], p["Cm"][:1],
-                          p["dt_bias"][:ch], p["Dskip"][:ch], p["z"][:1, :ch], nthreads=threads)
+    for b in range(rows):
+        run(b, ch)
     dt = time.perf_counter() - t0
-    elems = ch * L
+    elems = rows * ch * L
+    what = ("the whole workload" if rows * ch == B * D else
+            f"batch row 0, channels 0..{ch - 1} of {D}")
     return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"batch row 0, channels 0..{ch - 1} of {D}, all {L} steps "
-                      f"(conv1d+SiLU then scan, fp64, {threads} threads; {elems} elements)"}
+            "sample": f"{what}, all {L} steps: conv1d+SiLU then scan in fp64 on {threads} "
+                      f"host threads ({elems} elements)"}
 
 
 def run_block(args, torch, mamba, W):
@@ -160,7 +168,9 @@ def run_block(args, torch, mamba, W):
     tr = traffic_record()
     traffic = None
     if tr is not None:
-        traffic = round((tr["fetch_bytes"] + tr["write_bytes"]), 0)
+        # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
+        # a copy kernel of known size; null once the kernel source has changed
+        traffic = int(round(tr["fetch_bytes"] + tr["write_bytes"]))
     out = {
         "metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
         "value": round(elems / (ms_step * 1e-3) / 1e9, 3),
@@ -285,6 +295,9 @@ def main():
     ap.add_argument("--workload", default="block",
                     choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one elementwise kernel that reads and writes "
+                         "this many MiB (known traffic for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the hot path "
@@ -296,6 +309,16 @@ def main():
     from selective_state_space_80_amd import workloads as W
 
     mamba.load_library()
+    if args.copy_calibration_mib:
+        # one plain streaming kernel (torch's elementwise multiply) that reads
+        # and writes exactly this many bytes with ordinary loads and stores
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "block":
         out = run_block(args, torch, mamba, W)
     elif args.workload == "scan_bf16_l2048":

@@ -48,6 +48,10 @@
 #include "device_common.h"
 #include "internal.h"
 
+#ifndef SCAN_WAVES_PER_SIMD
+#define SCAN_WAVES_PER_SIMD 3
+#endif
+
 namespace mamba {
 
 namespace {
@@ -64,7 +68,22 @@ constexpr uint32_t kPathStructured = 0u;
 constexpr uint32_t kPathGeneral = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
 constexpr int kSpinLimit = 1 << 22;
-constexpr int64_t kSuperSeg = 16;  // segments per superblock of the carry
+#ifndef SCAN_SUPERSEG
+#define SCAN_SUPERSEG 16
+#endif
+constexpr int64_t kSuperSeg = SCAN_SUPERSEG;  // segments per superblock of the carry
+#ifdef SCAN_TRACE
+#define TRACE_POINT(k)                                                                        \
+    do {                                                                                      \
+        if (lane == 0)                                                                        \
+            reinterpret_cast<uint64_t *>(p.ws + lay.total - (size_t)lay.n_items * 256)[(item * 4 + w) * 8 + (k)] = \
+                __builtin_amdgcn_s_memrealtime();                                             \
+    } while (0)
+#else
+#define TRACE_POINT(k) \
+    do {               \
+    } while (0)
+#endif
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -128,21 +147,64 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per-lane chunk I/O: 32 consecutive time steps of one row.  `vec` means the
+// Per-lane chunk inputs: 32 consecutive time steps of one row.  `vec` means the
 // chunk is full and the row is 16-byte aligned, so 128-bit loads are used.
 // Steps at or past L are filled with `pad` and never stored: padding x with 0
 // and dt with -inf makes such a step an exact identity of the recurrence
-// (step 0, decay 1, no input), so the step loops need no per-step branches.
-template <bool BF16>
-__device__ __forceinline__ void load_chunk(const void *base, int64_t off, int nt, bool vec,
-                                           float (&v)[kChunkT], float pad = 0.f)
-{
-    if constexpr (!BF16) {
-        const float *p = reinterpret_cast<const float *>(base) + off;
+// (step 0, decay 1, no input).
+// Register budget: bf16 inputs stay packed two steps per register (16 VGPRs
+// for the chunk); fp32 inputs are held 16 steps at a time (16 VGPRs), the
+// second half loaded once the first is consumed.
+constexpr int kHalfT = kChunkT / 2;
+
+template <bool BF16> struct InChunk;
+
+template <> struct InChunk<true> {
+    uint32_t w[kChunkT / 2];  // step 2i in the low half, 2i+1 in the high half
+    __device__ __forceinline__ void load(const void *base, int64_t off, int half, int nt, bool vec,
+                                         float pad)
+    {
+        if (half != 0)
+            return;  // the whole chunk arrives with the first half
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + off;
+        if (vec) {
+            const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+            for (int i = 0; i < kChunkT / 8; ++i) {
+                const uint4 a = q[i];
+                w[4 * i + 0] = a.x;
+                w[4 * i + 1] = a.y;
+                w[4 * i + 2] = a.z;
+                w[4 * i + 3] = a.w;
+            }
+        } else {
+            const uint32_t pb = __float_as_uint(pad) >> 16;
+#pragma unroll
+            for (int i = 0; i < kChunkT / 2; ++i) {
+                const uint32_t lo = (2 * i < nt) ? (uint32_t)p[2 * i] : pb;
+                const uint32_t hi = (2 * i + 1 < nt) ? (uint32_t)p[2 * i + 1] : pb;
+                w[i] = lo | (hi << 16);
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int j) const
+    {
+        return (j & 1) ? __uint_as_float(w[j >> 1] & 0xffff0000u)
+                       : __uint_as_float(w[j >> 1] << 16);
+    }
+};
+
+template <> struct InChunk<false> {
+    float v[kHalfT];  // steps [half*16, half*16+16) of the chunk
+    __device__ __forceinline__ void load(const void *base, int64_t off, int half, int nt, bool vec,
+                                         float pad)
+    {
+        const int j0 = half * kHalfT;
+        const float *p = reinterpret_cast<const float *>(base) + off + j0;
         if (vec) {
             const float4 *q = reinterpret_cast<const float4 *>(p);
 #pragma unroll
-            for (int i = 0; i < kChunkT / 4; ++i) {
+            for (int i = 0; i < kHalfT / 4; ++i) {
                 const float4 a = q[i];
                 v[4 * i + 0] = a.x;
                 v[4 * i + 1] = a.y;
@@ -151,30 +213,12 @@ __device__ __forceinline__ void load_chunk(const void *base, int64_t off, int nt
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < kChunkT; ++i)
-                v[i] = (i < nt) ? p[i] : pad;
-        }
-    } else {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + off;
-        if (vec) {
-            const uint4 *q = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-            for (int i = 0; i < kChunkT / 8; ++i) {
-                const uint4 a = q[i];
-                const uint32_t w4[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    v[8 * i + 2 * k + 0] = __uint_as_float(w4[k] << 16);
-                    v[8 * i + 2 * k + 1] = __uint_as_float(w4[k] & 0xffff0000u);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kChunkT; ++i)
-                v[i] = (i < nt) ? bf16_bits_to_f32(p[i]) : pad;
+            for (int i = 0; i < kHalfT; ++i)
+                v[i] = (j0 + i < nt) ? p[i] : pad;
         }
     }
-}
+    __device__ __forceinline__ float get(int j) const { return v[j & (kHalfT - 1)]; }
+};
 
 template <bool BF16>
 __device__ __forceinline__ void store_chunk(void *base, int64_t off, int nt, bool vec,
@@ -243,6 +287,26 @@ __device__ __forceinline__ void publish_flag(uint32_t *p, uint32_t v, int lane)
         __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Spin (with sleeps) until the flag at `p` reaches `want` in every lane that
+// wants one (want = 0: nothing to wait for).  Bounded: a timeout is recorded
+// in the workspace header and the kernel carries on, so it always ends.
+__device__ __forceinline__ void wait_flags(const uint32_t *p, uint32_t want, WsHeader *hdr,
+                                           int lane)
+{
+    int spins = 0;
+    for (;;) {
+        const uint32_t f = want ? load_flag(p) : 0u;
+        if (__ballot(f < want) == 0ull)
+            return;
+        if (++spins > kSpinLimit) {  // never expected
+            if (lane == 0)
+                atomicOr(&hdr->error, kErrSpinTimeout);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 struct ScanKArgs {
     const void *x, *dt, *z;
     void *y;
@@ -255,24 +319,25 @@ struct ScanKArgs {
     int vec;  // rows of x, dt, z, y are 16-byte aligned for vector access
 };
 
-// Decay factor P_n of an aggregate whose summary is f:
-//   structured: f = prod e over the chunk, P_n = f^(n+1)
+// Apply the chunk map (f, S) to a state: h_n <- P_n(f) h_n + S_n, where
+//   structured: f = prod of e over the chunk, P_n = f^(n+1)
 //   general:    f = sum over the chunk of Δ/ln2, P_n = 2^(A_n f)   (A_n = 0 -> 1)
-template <bool STRUCT>
-__device__ __forceinline__ void decay_factors(float f, const float (&Ar)[kMaxN],
-                                              float (&P)[kMaxN])
+// S_n is read through `get(n)` so it can come from registers, LDS or a record.
+template <bool STRUCT, typename GetS>
+__device__ __forceinline__ void apply_map(float f, GetS get, const float (&Ar)[kMaxN],
+                                          float (&h)[kMaxN])
 {
-    if constexpr (STRUCT) {
-        float p = f;
+    float pw = f;
 #pragma unroll
-        for (int n = 0; n < kMaxN; ++n) {
-            P[n] = p;
-            p *= f;
+    for (int n = 0; n < kMaxN; ++n) {
+        float P;
+        if constexpr (STRUCT) {
+            P = pw;
+            pw *= f;
+        } else {
+            P = (Ar[n] == 0.f) ? 1.f : hw_exp2(Ar[n] * f);
         }
-    } else {
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            P[n] = (Ar[n] == 0.f) ? 1.f : hw_exp2(Ar[n] * f);
+        h[n] = fmaf(P, h[n], get(n));
     }
 }
 
@@ -286,11 +351,11 @@ __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 template <bool BF16, bool STRUCT>
 __device__ __forceinline__ void scan_segment(
     const ScanKArgs &p, const float *__restrict__ bcp, const float *__restrict__ crp,
-    uint32_t *__restrict__ flags,
-    float *__restrict__ agg, float *__restrict__ incl, WsHeader *hdr, int64_t seg, int64_t g,
-    int w, int lane, float (*s_agg)[kAggFields][kWave], float (*s_part)[kAggFields][kWave],
-    float (*s_hin)[kWave], int *s_ctl)
+    uint32_t *__restrict__ flags, float *__restrict__ agg, float *__restrict__ incl,
+    WsHeader *hdr, int64_t seg, int64_t g, int w, int lane, float (*s_agg)[kAggFields][kWave],
+    float (*s_part)[kAggFields][kWave], float (*s_bc)[kSegT][kMaxN])
 {
+    float(*s_hin)[kWave] = reinterpret_cast<float(*)[kWave]>(&s_bc[0][0][0]);
     const ScanWsLayout &lay = p.lay;
     const int64_t G = lay.groups;
     const int64_t item = seg * G + g;
@@ -300,29 +365,23 @@ __device__ __forceinline__ void scan_segment(
     const bool active = d < p.D;
     const int64_t dc = active ? d : (p.D - 1);  // inactive lanes read a valid row
     const int64_t t0 = seg * kSegT + (int64_t)w * kChunkT;
-    const int nt = __builtin_amdgcn_readfirstlane((int)max((int64_t)0, min((int64_t)kChunkT, p.L - t0)));
+    const int nt =
+        __builtin_amdgcn_readfirstlane((int)max((int64_t)0, min((int64_t)kChunkT, p.L - t0)));
     const bool vec = p.vec && nt == kChunkT;
     const int64_t row_off = (b * p.D + dc) * p.L + t0;
     // prepared B/C rows exist (as zeros) up to the padded length n_seg*kSegT
     const float *bcrow = bcp + (b * lay.n_seg * kSegT + t0) * kBCStride;
     const float *crow = crp + (b * lay.n_seg * kSegT + t0) * kMaxN;
-    // Bring this chunk's 32 B/C rows (one 128-byte line each) into L2 with a
-    // single vector load (lane l touches half l/32 of row l%32), issued with
-    // the x/dt loads.  The per-step scalar loads then hit L2 instead of each
-    // paying a full memory latency.
-    const float warm = bcrow[(lane & 31) * kBCStride + (lane >> 5) * kMaxN];
+    TRACE_POINT(0);
 
     // per-channel constants
     const float bias2 = (p.dt_bias ? p.dt_bias[dc] : 0.f) * kLog2e;
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
-    float Ar[kMaxN];
+    float Ar[kMaxN];  // general path only: the A row of this channel
     float a0 = -1.f, inva0 = -1.f;
     if constexpr (STRUCT) {
         a0 = p.A[dc * p.N];
         inva0 = 1.0f / a0;
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            Ar[n] = a0 * (float)(n + 1);
     } else {
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
@@ -334,53 +393,62 @@ __device__ __forceinline__ void scan_segment(
     float hs[kMaxN];
     float summ;
     {
-        float xr[kChunkT], dr[kChunkT];
-        load_chunk<BF16>(p.x, row_off, nt, vec, xr, 0.f);
-        load_chunk<BF16>(p.dt, row_off, nt, vec, dr, -__builtin_huge_valf());
+        InChunk<BF16> xin, din;
+        xin.load(p.x, row_off, 0, nt, vec, 0.f);
+        din.load(p.dt, row_off, 0, nt, vec, -__builtin_huge_valf());
+        if constexpr (STRUCT) {
+            // The segment's 128 prepared rows [B | C/(n+1)] (16 KB) go to LDS
+            // with one 128-bit load per thread and row quarter; every step then
+            // reads its row with broadcast LDS loads instead of waiting on a
+            // scalar load.
+            const float4 *src = reinterpret_cast<const float4 *>(
+                bcp + (b * lay.n_seg * kSegT + seg * kSegT) * kBCStride);
+            const int tid = w * kWave + lane;
+#pragma unroll
+            for (int i = 0; i < (kSegT * kBCStride / 4) / (kWave * kWavesPerSeg); ++i) {
+                const int q = tid + i * kWave * kWavesPerSeg;  // float4 index in the block
+                const int row = q >> 3, part = q & 7;          // 8 float4 per row
+                const float4 v = src[q];
+                *reinterpret_cast<float4 *>(&s_bc[part >> 2][row][(part & 3) * 4]) = v;
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             hs[n] = 0.f;
-        if constexpr (STRUCT) {
-            float E = 1.f;
+        float E = 1.f, cumL = 0.f;
 #pragma unroll
-            for (int j = 0; j < kChunkT; ++j) {
-                if (j < nt) {  // one basic block per step
-                    const float *bc = bcrow + j * kBCStride;  // B, C/(n+1): scalar loads
-                    const float l = softplus_log2(fmaf(dr[j], kLog2e, bias2));  // Δ/ln2
-                    const float e1 = hw_exp2(a0 * l);                            // exp(Δ A_0)
-                    const float xv = xr[j];
-                    float en = e1, acc = 0.f;
+        for (int j = 0; j < kChunkT; ++j) {
+            if (j == kHalfT) {
+                xin.load(p.x, row_off, 1, nt, vec, 0.f);
+                din.load(p.dt, row_off, 1, nt, vec, -__builtin_huge_valf());
+            }
+            if (j < nt) {  // one basic block per step
+                const float l = softplus_log2(fmaf(din.get(j), kLog2e, bias2));  // Δ/ln2
+                const float xv = xin.get(j);
+                float acc = 0.f;
+                if constexpr (STRUCT) {
+                    const float *Bj = s_bc[0][w * kChunkT + j];  // B (LDS broadcast)
+                    const float *Cj = s_bc[1][w * kChunkT + j];  // C/(n+1)
+                    const float e1 = hw_exp2(a0 * l);  // exp(Δ A_0)
+                    float en = e1;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n) {
                         if (n)
                             en *= e1;
-                        const float pn = bc[n] * xv;
+                        const float pn = Bj[n] * xv;
                         const float sn = hs[n] + pn;
                         hs[n] = fmaf(en, sn, -pn);
-                        acc = fmaf(bc[kMaxN + n], hs[n], acc);
+                        acc = fmaf(Cj[n], hs[n], acc);
                     }
                     E *= e1;
                     yl[j] = fmaf(acc, inva0, Dd * xv);
                     er[j] = E;
-                }
-            }
-            summ = E;
-            // back to true units: h_n = ĥ_n / A_n
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                hs[n] = hs[n] * (inva0 / (float)(n + 1));
-        } else {
-            float cumL = 0.f;
-#pragma unroll
-            for (int j = 0; j < kChunkT; ++j) {
-                if (j < nt) {
-                    const float *bc = bcrow + j * kBCStride;
+                } else {
+                    const float *bc = bcrow + j * kBCStride;  // B (scalar loads)
                     const float *cr = crow + j * kMaxN;
-                    const float l = softplus_log2(fmaf(dr[j], kLog2e, bias2));
                     const float delta = l * kLn2;
-                    const float xv = xr[j];
                     cumL += l;
-                    float acc = 0.f;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n) {
                         const float an = Ar[n];
@@ -393,17 +461,26 @@ __device__ __forceinline__ void scan_segment(
                     er[j] = cumL;
                 }
             }
+        }
+        if constexpr (STRUCT) {
+            summ = E;
+            // back to true units: h_n = ĥ_n / A_n
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                hs[n] = hs[n] * (inva0 / (float)(n + 1));
+        } else {
             summ = cumL;
         }
     }
+    TRACE_POINT(1);
 
-    __asm__ volatile("" ::"v"(warm));  // the warm-up load's value is not needed
-
-    // z is only needed by the final gating: start its loads now so they are in
-    // flight while the workgroup resolves its start state
-    float zr[kChunkT];
-    if (p.z && nt > 0)
-        load_chunk<BF16>(p.z, row_off, nt, vec, zr);
+    // z is only needed by the final gating: its first half (all of it for
+    // bf16) is requested now, so it arrives while the workgroup resolves its
+    // start state.  Wave 0 first publishes its record (that publish waits for
+    // every outstanding memory operation of the wave).
+    InChunk<BF16> zin;
+    if (p.z && w != 0)
+        zin.load(p.z, row_off, 0, nt, vec, 0.f);
 
     // ---- 2. combine chunk maps inside the workgroup ------------------------
     s_agg[w][0][lane] = summ;
@@ -412,32 +489,31 @@ __device__ __forceinline__ void scan_segment(
         s_agg[w][1 + n][lane] = hs[n];
     __syncthreads();
 
-    // ---- 3. find which earlier segments' records give this segment's start --
-    //  sI     : nearest earlier segment with an inclusive (start-resolved) record,
-    //           -1 meaning "the initial state h0"
-    //  depth  : number of segments after sI (up to seg-1) whose aggregates
-    //           must be folded on top of it
-    float F = 0.f, Sg[kMaxN];
+    TRACE_POINT(2);
+    // ---- 3. segment map and the records this segment folds ------------------
+    // Fixed association order, independent of scheduling: a segment folds the
+    // aggregates of the earlier segments of its superblock, in order, onto the
+    // inclusive state that ends the previous superblock (-1 = h0).
+    const int64_t sI = (seg / kSuperSeg) * kSuperSeg - 1;
+    const int64_t depth = seg - 1 - sI;
     if (w == 0) {
-        F = s_agg[0][0][lane];
+        float F = s_agg[0][0][lane];
+        float Sg[kMaxN];
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             Sg[n] = s_agg[0][1 + n][lane];
 #pragma unroll
         for (int k = 1; k < kWavesPerSeg; ++k) {
             const float fk = s_agg[k][0][lane];
-            float P[kMaxN];
-            decay_factors<STRUCT>(fk, Ar, P);
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                Sg[n] = fmaf(P[n], Sg[n], s_agg[k][1 + n][lane]);
+            apply_map<STRUCT>(fk, [&](int n) { return s_agg[k][1 + n][lane]; }, Ar, Sg);
             F = combine_summary<STRUCT>(F, fk);
         }
-        // Fixed association order, independent of scheduling: a segment folds
-        // the aggregates of the earlier segments of its superblock, in order,
-        // onto the inclusive state that ends the previous superblock.
-        const int64_t sI = (seg / kSuperSeg) * kSuperSeg - 1;  // -1 = h0
-        const int64_t depth = seg - 1 - sI;
+        // the segment map, for step 5 (slot 0 of s_part is free: wave 0 keeps
+        // its own step-4 partial in registers)
+        s_part[0][0][lane] = F;
+#pragma unroll
+        for (int n = 0; n < kMaxN; ++n)
+            s_part[0][1 + n][lane] = Sg[n];
         if (seg + 1 < lay.n_seg) {
             // successors in this superblock fold this segment's aggregate
             float *rec = agg + item * (kAggFields * kWave);
@@ -447,39 +523,20 @@ __device__ __forceinline__ void scan_segment(
                 store_rec(rec + (1 + n) * kWave + lane, Sg[n]);
             publish_flag(flags + item, kFlagAgg, lane);
         }
-        if (seg > 0) {
-            // wait until the records this segment folds are all published:
-            // lane j < depth watches segment seg-1-j (aggregate), lane `depth`
-            // watches segment sI (inclusive state; none needed when sI < 0)
-            const int64_t s = seg - 1 - lane;
-            uint32_t want = 0u;
-            if (lane < depth)
-                want = kFlagAgg;
-            else if (lane == depth && sI >= 0)
-                want = kFlagIncl;
-            int spins = 0;
-            for (;;) {
-                const uint32_t f = want ? load_flag(flags + s * G + g) : 0u;
-                if (__ballot(f < want) == 0ull)
-                    break;
-                if (++spins > kSpinLimit) {  // never expected; keeps the kernel finite
-                    if (lane == 0)
-                        atomicOr(&hdr->error, kErrSpinTimeout);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        if (lane == 0) {
-            s_ctl[0] = sI;
-            s_ctl[1] = depth;
+        if (p.z)
+            zin.load(p.z, row_off, 0, nt, vec, 0.f);
+        if (depth > 0) {
+            // wait for the aggregates this segment folds: lane j < depth
+            // watches segment seg-1-j (the inclusive state of sI is awaited
+            // later, after the fold, so that the superblock-to-superblock chain
+            // only carries one map application per hop)
+            wait_flags(flags + (seg - 1 - lane) * G + g, lane < depth ? kFlagAgg : 0u, hdr, lane);
         }
     }
     __syncthreads();
 
+    TRACE_POINT(3);
     // ---- 4. fold the predecessors' aggregates, four waves in parallel --------
-    const int64_t sI = __builtin_amdgcn_readfirstlane((int)s_ctl[0]);
-    const int64_t depth = __builtin_amdgcn_readfirstlane((int)s_ctl[1]);
     {
         const int64_t per = (depth + kWavesPerSeg - 1) / kWavesPerSeg;
         const int64_t lo = min(depth, (int64_t)w * per), hi = min(depth, lo + per);
@@ -488,84 +545,79 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             ps[n] = 0.f;
-        for (int64_t j = lo; j < hi; j += 2) {
-            // two records per round trip; records are in time order
+        for (int64_t j = lo; j < hi; j += 2) {  // records in time order, two per round trip
             const bool two = j + 1 < hi;
             const float *r0 = agg + ((sI + 1 + j) * G + g) * (kAggFields * kWave);
             const float *r1 = two ? r0 + G * (kAggFields * kWave) : r0;
-            float f0 = load_rec(r0 + lane), f1 = load_rec(r1 + lane);
-            float v0[kMaxN], v1[kMaxN];
+            float v0[kAggFields], v1[kAggFields];
 #pragma unroll
-            for (int n = 0; n < kMaxN; ++n) {
-                v0[n] = load_rec(r0 + (1 + n) * kWave + lane);
-                v1[n] = load_rec(r1 + (1 + n) * kWave + lane);
+            for (int k = 0; k < kAggFields; ++k) {
+                v0[k] = load_rec(r0 + k * kWave + lane);
+                v1[k] = load_rec(r1 + k * kWave + lane);
             }
-            float P[kMaxN];
-            decay_factors<STRUCT>(f0, Ar, P);
+            apply_map<STRUCT>(v0[0], [&](int n) { return v0[1 + n]; }, Ar, ps);
+            pf = combine_summary<STRUCT>(pf, v0[0]);
+            if (two) {
+                apply_map<STRUCT>(v1[0], [&](int n) { return v1[1 + n]; }, Ar, ps);
+                pf = combine_summary<STRUCT>(pf, v1[0]);
+            }
+        }
+        if (w != 0) {
+            s_part[w][0][lane] = pf;
 #pragma unroll
             for (int n = 0; n < kMaxN; ++n)
-                ps[n] = fmaf(P[n], ps[n], v0[n]);
-            pf = combine_summary<STRUCT>(pf, f0);
-            if (two) {
-                decay_factors<STRUCT>(f1, Ar, P);
+                s_part[w][1 + n][lane] = ps[n];
+        }
+        __syncthreads();
+
+        TRACE_POINT(4);
+        // ---- 5. segment start state and inclusive record ---------------------
+        if (w == 0) {
+            float hin[kMaxN];
+            if (sI >= 0)
+                wait_flags(flags + sI * G + g, lane == 0 ? kFlagIncl : 0u, hdr, lane);
+            if (sI < 0) {
 #pragma unroll
                 for (int n = 0; n < kMaxN; ++n)
-                    ps[n] = fmaf(P[n], ps[n], v1[n]);
-                pf = combine_summary<STRUCT>(pf, f1);
+                    hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
+            } else {
+                const float *rec = incl + (sI * G + g) * (kInclFields * kWave);
+#pragma unroll
+                for (int n = 0; n < kMaxN; ++n)
+                    hin[n] = load_rec(rec + n * kWave + lane);
+            }
+            // wave 0's own partial is still in registers; then waves 1..3
+            apply_map<STRUCT>(pf, [&](int n) { return ps[n]; }, Ar, hin);
+#pragma unroll
+            for (int k = 1; k < kWavesPerSeg; ++k)
+                apply_map<STRUCT>(s_part[k][0][lane],
+                                  [&](int n) { return s_part[k][1 + n][lane]; }, Ar, hin);
+#pragma unroll
+            for (int n = 0; n < kMaxN; ++n)
+                s_hin[n][lane] = hin[n];
+            const bool publish = seg + 1 < lay.n_seg && (seg + 1) % kSuperSeg == 0;
+            const bool last = seg + 1 == lay.n_seg;
+            if (publish || (last && p.h_last)) {
+                // state at the end of the segment
+                apply_map<STRUCT>(s_part[0][0][lane],
+                                  [&](int n) { return s_part[0][1 + n][lane]; }, Ar, hin);
+                if (publish) {
+                    float *rec = incl + item * (kInclFields * kWave);
+#pragma unroll
+                    for (int n = 0; n < kMaxN; ++n)
+                        store_rec(rec + n * kWave + lane, hin[n]);
+                    publish_flag(flags + item, kFlagIncl, lane);
+                } else if (active) {
+#pragma unroll
+                    for (int n = 0; n < kMaxN; ++n)
+                        if (n < p.N)
+                            p.h_last[(b * p.D + d) * p.N + n] = hin[n];
+                }
             }
         }
-        s_part[w][0][lane] = pf;
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            s_part[w][1 + n][lane] = ps[n];
     }
     __syncthreads();
-
-    // ---- 5. segment start state, inclusive record, per-wave start state -----
-    if (w == 0) {
-        float hin[kMaxN];
-        if (sI < 0) {
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
-        } else {
-            const float *rec = incl + (sI * G + g) * (kInclFields * kWave);
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                hin[n] = load_rec(rec + n * kWave + lane);
-        }
-#pragma unroll
-        for (int k = 0; k < kWavesPerSeg; ++k) {
-            float P[kMaxN];
-            decay_factors<STRUCT>(s_part[k][0][lane], Ar, P);
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                hin[n] = fmaf(P[n], hin[n], s_part[k][1 + n][lane]);
-        }
-        float P[kMaxN];
-        decay_factors<STRUCT>(F, Ar, P);
-        float hout[kMaxN];
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            hout[n] = fmaf(P[n], hin[n], Sg[n]);
-        if (seg + 1 < lay.n_seg && (seg + 1) % kSuperSeg == 0) {
-            float *rec = incl + item * (kInclFields * kWave);
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                store_rec(rec + n * kWave + lane, hout[n]);
-            publish_flag(flags + item, kFlagIncl, lane);
-        }
-        if (seg + 1 == lay.n_seg && p.h_last && active) {
-#pragma unroll
-            for (int n = 0; n < kMaxN; ++n)
-                if (n < p.N)
-                    p.h_last[(b * p.D + d) * p.N + n] = hout[n];
-        }
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            s_hin[n][lane] = hin[n];
-    }
-    __syncthreads();
+    TRACE_POINT(5);
 
     if (nt <= 0)
         return;
@@ -575,13 +627,9 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
     for (int n = 0; n < kMaxN; ++n)
         hin[n] = s_hin[n][lane];
-    for (int k = 0; k < w; ++k) {
-        float P[kMaxN];
-        decay_factors<STRUCT>(s_agg[k][0][lane], Ar, P);
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            hin[n] = fmaf(P[n], hin[n], s_agg[k][1 + n][lane]);
-    }
+    for (int k = 0; k < w; ++k)
+        apply_map<STRUCT>(s_agg[k][0][lane], [&](int n) { return s_agg[k][1 + n][lane]; }, Ar,
+                          hin);
     const bool zero_start = (seg == 0 && w == 0 && p.h0 == nullptr);
     // The step conditions of the fix-up loops must not be shared with the scan
     // loops (keeping 32 condition masks alive costs scalar registers): give the
@@ -589,17 +637,17 @@ __device__ __forceinline__ void scan_segment(
     int ntf = nt;
     __asm__ volatile("" : "+s"(ntf));
 
-    if constexpr (STRUCT) {
-        // coefficient of the carried state in scaled units: (n+1) A_0 h_in,n
-        float hsc[kMaxN];
+    if (!zero_start) {
+        if constexpr (STRUCT) {
+            // coefficient of the carried state in scaled units: (n+1) A_0 h_in,n
+            float hsc[kMaxN];
 #pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            hsc[n] = Ar[n] * hin[n];
-        if (!zero_start) {
+            for (int n = 0; n < kMaxN; ++n)
+                hsc[n] = (a0 * (float)(n + 1)) * hin[n];
 #pragma unroll
             for (int j = 0; j < kChunkT; ++j) {
                 if (j < ntf) {
-                    const float *cs = bcrow + j * kBCStride + kMaxN;  // C/(n+1)
+                    const float *cs = s_bc[1][w * kChunkT + j];  // C/(n+1)
                     const float Ej = er[j];
                     float qh = 0.f;
 #pragma unroll
@@ -608,14 +656,7 @@ __device__ __forceinline__ void scan_segment(
                     yl[j] = fmaf(qh * Ej, inva0, yl[j]);
                 }
             }
-        }
-        if (p.z) {
-#pragma unroll
-            for (int j = 0; j < kChunkT; ++j)
-                yl[j] *= silu_hw(zr[j]);
-        }
-    } else {
-        if (!zero_start) {
+        } else {
 #pragma unroll
             for (int j = 0; j < kChunkT; ++j) {
                 if (j < ntf) {
@@ -631,25 +672,30 @@ __device__ __forceinline__ void scan_segment(
                 }
             }
         }
-        if (p.z) {
+    }
+    if (p.z) {
 #pragma unroll
-            for (int j = 0; j < kChunkT; ++j)
-                yl[j] *= silu_hw(zr[j]);
+        for (int j = 0; j < kChunkT; ++j) {
+            if (j == kHalfT)
+                zin.load(p.z, row_off, 1, nt, vec, 0.f);
+            yl[j] *= silu_hw(zin.get(j));
         }
     }
     if (active)
         store_chunk<BF16>(p.y, row_off, nt, vec, yl);
+    TRACE_POINT(6);
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kWave *kWavesPerSeg, 3) scan_main_kernel(
+__global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan_main_kernel(
     ScanKArgs p, const float *__restrict__ bcp, const float *__restrict__ crp,
     const uint32_t *__restrict__ tiles)
 {
     __shared__ float s_agg[kWavesPerSeg][kAggFields][kWave];
     __shared__ float s_part[kWavesPerSeg][kAggFields][kWave];
-    __shared__ float s_hin[kMaxN][kWave];
-    __shared__ int s_ctl[2];
+    // B and C/(n+1) of the segment's steps (structured path); once every wave
+    // has finished its chunk scan the B half is reused for the start states
+    __shared__ __attribute__((aligned(16))) float s_bc[2][kSegT][kMaxN];
     __shared__ uint32_t s_ticket;
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(p.ws + p.lay.off_header);
@@ -669,10 +715,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, 3) scan_main_kernel(
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
         scan_segment<BF16, true>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg, s_part,
-                                 s_hin, s_ctl);
+                                 s_bc);
     else
         scan_segment<BF16, false>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
-                                  s_part, s_hin, s_ctl);
+                                  s_part, s_bc);
 }
 
 // Writes h_last = h0 (or zeros) for an empty sequence (L == 0).
@@ -708,6 +754,9 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L)
     off = round_up(off + (size_t)l.n_items * kAggFields * kWave * 4, 256);
     l.off_incl = off;
     off = round_up(off + (size_t)l.n_items * kInclFields * kWave * 4, 256);
+#ifdef SCAN_TRACE
+    off = round_up(off + (size_t)l.n_items * 256, 256);
+#endif
     l.total = off;
     return l;
 }

@@ -1,0 +1,128 @@
+"""Summaries of rocprofv3 result databases (SQLite, ``*_results.db``).
+
+    python -m selective_state_space_80_amd.profiling trace  RESULTS.db
+    python -m selective_state_space_80_amd.profiling counters RESULTS.db [RESULTS.db ...]
+    python -m selective_state_space_80_amd.profiling traffic --fetch F.db --write W.db \
+        --copy-bytes N --kernel scan_main_kernel --out profiles/scan_traffic.json
+
+``trace`` prints per-kernel call counts and average durations in microseconds (from
+``rocprofv3 --kernel-trace --stats``); ``counters`` prints per-kernel averages of
+every counter collected with ``--pmc`` (summed over the per-XCD/SE rows of a
+dispatch, averaged over dispatches); ``traffic`` turns FETCH_SIZE / WRITE_SIZE
+(KiB per dispatch) into bytes, scaled so that a plain streaming kernel of the
+same run (bench.py --copy-calibration-mib: torch's elementwise multiply), which
+reads and writes a known number of bytes, reads and writes exactly that.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import hashlib
+import json
+import os
+import re
+import sqlite3
+import sys
+
+COPY_KERNEL = "MulFunctor"  # torch elementwise multiply: reads N bytes, writes N bytes
+
+
+def short_name(kernel: str) -> str:
+    if COPY_KERNEL in kernel:
+        return "calibration_" + COPY_KERNEL
+    k = kernel.replace("(anonymous namespace)", "anon")
+    m = re.search(r"::(\w+)(<[^>]*>)?\(", k)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    return k.split("(")[0][:60]
+
+
+def kernel_trace(db: str):
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, total_calls, total_duration, average, percentage "
+                       "from top_kernels").fetchall()
+    return [(short_name(n), int(c), float(t), float(a), float(p)) for n, c, t, a, p in rows]
+
+
+def counters(db: str):
+    """{kernel: {counter: mean over dispatches of the per-dispatch total}}"""
+    con = sqlite3.connect(db)
+    rows = con.execute("select dispatch_id, kernel_name, counter_name, value "
+                       "from counters_collection").fetchall()
+    per_dispatch = collections.defaultdict(float)
+    names = {}
+    for did, kn, cn, v in rows:
+        per_dispatch[(did, cn)] += float(v)
+        names[did] = kn
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (did, cn), v in per_dispatch.items():
+        acc[short_name(names[did])][cn].append(v)
+    return {k: {cn: sum(v) / len(v) for cn, v in d.items()} for k, d in acc.items()}
+
+
+def _find(d, sub):
+    for k, v in d.items():
+        if sub in k:
+            return v
+    raise KeyError(sub)
+
+
+def traffic(fetch_db, write_db, copy_bytes, kernel, source=None):
+    f = counters(fetch_db)
+    w = counters(write_db)
+    copy_f = _find(f, COPY_KERNEL)["FETCH_SIZE"] * 1024.0
+    copy_w = _find(w, COPY_KERNEL)["WRITE_SIZE"] * 1024.0
+    kf = _find(f, kernel)["FETCH_SIZE"] * 1024.0
+    kw = _find(w, kernel)["WRITE_SIZE"] * 1024.0
+    out = {"kernel": kernel, "copy_bytes": copy_bytes,
+           "copy_fetch_raw_bytes": copy_f, "copy_write_raw_bytes": copy_w,
+           "fetch_scale": copy_bytes / copy_f, "write_scale": copy_bytes / copy_w,
+           "fetch_raw_bytes": kf, "write_raw_bytes": kw,
+           "fetch_bytes": kf * copy_bytes / copy_f, "write_bytes": kw * copy_bytes / copy_w}
+    if source:
+        out["scan_fwd_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    c = sub.add_parser("counters")
+    c.add_argument("db", nargs="+")
+    tr = sub.add_parser("traffic")
+    tr.add_argument("--fetch", required=True)
+    tr.add_argument("--write", required=True)
+    tr.add_argument("--copy-bytes", type=int, required=True)
+    tr.add_argument("--kernel", default="scan_main_kernel")
+    tr.add_argument("--source", default=None, help="kernel source to fingerprint")
+    tr.add_argument("--out", default=None)
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        print(f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'total_us':>11s} {'pct':>6s}")
+        for n, calls, tot, avg, pct in kernel_trace(a.db):
+            print(f"{n:44s} {calls:6d} {avg:10.2f} {tot:11.1f} {pct:6.2f}")
+    elif a.cmd == "counters":
+        merged = collections.defaultdict(dict)
+        for db in a.db:
+            for k, d in counters(db).items():
+                merged[k].update(d)
+        for k, d in merged.items():
+            print(k)
+            for cn, v in sorted(d.items()):
+                print(f"    {cn:28s} {v:18,.0f}")
+    else:
+        rec = traffic(a.fetch, a.write, a.copy_bytes, a.kernel, a.source)
+        text = json.dumps(rec, indent=1)
+        if a.out:
+            os.makedirs(os.path.dirname(a.out) or ".", exist_ok=True)
+            with open(a.out, "w") as fh:
+                fh.write(text + "\n")
+        print(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
