@@ -153,19 +153,17 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(
 // and dt with -inf makes such a step an exact identity of the recurrence
 // (step 0, decay 1, no input).
 // Register budget: bf16 inputs stay packed two steps per register (16 VGPRs
-// for the chunk); fp32 inputs are held 16 steps at a time (16 VGPRs), the
-// second half loaded once the first is consumed.
-constexpr int kHalfT = kChunkT / 2;
-
+// for the chunk); fp32 inputs take 32 VGPRs, but a step's input register dies
+// at the step that writes the step's output, so inputs and outputs share
+// registers.  Each lane's chunk is one whole 128-byte line (fp32) or half of
+// one whose other half the neighbouring wave loads at the same time (bf16):
+// every line is fetched from memory once.
 template <bool BF16> struct InChunk;
 
 template <> struct InChunk<true> {
     uint32_t w[kChunkT / 2];  // step 2i in the low half, 2i+1 in the high half
-    __device__ __forceinline__ void load(const void *base, int64_t off, int half, int nt, bool vec,
-                                         float pad)
+    __device__ __forceinline__ void load(const void *base, int64_t off, int nt, bool vec, float pad)
     {
-        if (half != 0)
-            return;  // the whole chunk arrives with the first half
         const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + off;
         if (vec) {
             const uint4 *q = reinterpret_cast<const uint4 *>(p);
@@ -195,16 +193,14 @@ template <> struct InChunk<true> {
 };
 
 template <> struct InChunk<false> {
-    float v[kHalfT];  // steps [half*16, half*16+16) of the chunk
-    __device__ __forceinline__ void load(const void *base, int64_t off, int half, int nt, bool vec,
-                                         float pad)
+    float v[kChunkT];
+    __device__ __forceinline__ void load(const void *base, int64_t off, int nt, bool vec, float pad)
     {
-        const int j0 = half * kHalfT;
-        const float *p = reinterpret_cast<const float *>(base) + off + j0;
+        const float *p = reinterpret_cast<const float *>(base) + off;
         if (vec) {
             const float4 *q = reinterpret_cast<const float4 *>(p);
 #pragma unroll
-            for (int i = 0; i < kHalfT / 4; ++i) {
+            for (int i = 0; i < kChunkT / 4; ++i) {
                 const float4 a = q[i];
                 v[4 * i + 0] = a.x;
                 v[4 * i + 1] = a.y;
@@ -213,11 +209,11 @@ template <> struct InChunk<false> {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < kHalfT; ++i)
-                v[i] = (j0 + i < nt) ? p[i] : pad;
+            for (int i = 0; i < kChunkT; ++i)
+                v[i] = (i < nt) ? p[i] : pad;
         }
     }
-    __device__ __forceinline__ float get(int j) const { return v[j & (kHalfT - 1)]; }
+    __device__ __forceinline__ float get(int j) const { return v[j]; }
 };
 
 template <bool BF16>
@@ -394,8 +390,8 @@ __device__ __forceinline__ void scan_segment(
     float summ;
     {
         InChunk<BF16> xin, din;
-        xin.load(p.x, row_off, 0, nt, vec, 0.f);
-        din.load(p.dt, row_off, 0, nt, vec, -__builtin_huge_valf());
+        xin.load(p.x, row_off, nt, vec, 0.f);
+        din.load(p.dt, row_off, nt, vec, -__builtin_huge_valf());
         if constexpr (STRUCT) {
             // The segment's 128 prepared rows [B | C/(n+1)] (16 KB) go to LDS
             // with one 128-bit load per thread and row quarter; every step then
@@ -419,10 +415,6 @@ __device__ __forceinline__ void scan_segment(
         float E = 1.f, cumL = 0.f;
 #pragma unroll
         for (int j = 0; j < kChunkT; ++j) {
-            if (j == kHalfT) {
-                xin.load(p.x, row_off, 1, nt, vec, 0.f);
-                din.load(p.dt, row_off, 1, nt, vec, -__builtin_huge_valf());
-            }
             if (j < nt) {  // one basic block per step
                 const float l = softplus_log2(fmaf(din.get(j), kLog2e, bias2));  // Δ/ln2
                 const float xv = xin.get(j);
@@ -474,13 +466,14 @@ __device__ __forceinline__ void scan_segment(
     }
     TRACE_POINT(1);
 
-    // z is only needed by the final gating: its first half (all of it for
-    // bf16) is requested now, so it arrives while the workgroup resolves its
-    // start state.  Wave 0 first publishes its record (that publish waits for
-    // every outstanding memory operation of the wave).
+    // z is only needed by the final gating.  bf16 z (16 VGPRs) is requested
+    // now, so it arrives while the workgroup resolves its start state; wave 0
+    // first publishes its record (that publish waits for every outstanding
+    // memory operation of the wave).  fp32 z (32 VGPRs) is requested once the
+    // start state is known, ahead of the fix-up.
     InChunk<BF16> zin;
-    if (p.z && w != 0)
-        zin.load(p.z, row_off, 0, nt, vec, 0.f);
+    if (BF16 && p.z && w != 0)
+        zin.load(p.z, row_off, nt, vec, 0.f);
 
     // ---- 2. combine chunk maps inside the workgroup ------------------------
     s_agg[w][0][lane] = summ;
@@ -523,8 +516,8 @@ __device__ __forceinline__ void scan_segment(
                 store_rec(rec + (1 + n) * kWave + lane, Sg[n]);
             publish_flag(flags + item, kFlagAgg, lane);
         }
-        if (p.z)
-            zin.load(p.z, row_off, 0, nt, vec, 0.f);
+        if (BF16 && p.z)
+            zin.load(p.z, row_off, nt, vec, 0.f);
         if (depth > 0) {
             // wait for the aggregates this segment folds: lane j < depth
             // watches segment seg-1-j (the inclusive state of sI is awaited
@@ -623,6 +616,8 @@ __device__ __forceinline__ void scan_segment(
         return;
 
     // ---- 6. this wave's start state, fix-up, gate, store -------------------
+    if (!BF16 && p.z)
+        zin.load(p.z, row_off, nt, vec, 0.f);
     float hin[kMaxN];
 #pragma unroll
     for (int n = 0; n < kMaxN; ++n)
@@ -676,8 +671,6 @@ __device__ __forceinline__ void scan_segment(
     if (p.z) {
 #pragma unroll
         for (int j = 0; j < kChunkT; ++j) {
-            if (j == kHalfT)
-                zin.load(p.z, row_off, 1, nt, vec, 0.f);
             yl[j] *= silu_hw(zin.get(j));
         }
     }
