@@ -83,21 +83,35 @@ def traffic_record():
     return rec if rec.get("scan_fwd_sha256") == sha else None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(p, B, D, L, target_s=20.0):
     """The fp64 oracle (conv then scan) on a bounded sample of the workload:
     whole sequences of the first channels, batch row by batch row, sized for at
-    most ~target_s seconds (the whole workload when it fits)."""
+    most ~target_s seconds (the whole workload when it fits).  Also the rate of
+    one thread on a few whole sequences."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
 
-    def run(b, ch):
+    def run(b, ch, nthreads):
         xs = oracle.conv1d_silu(p["x_raw"][b:b + 1, :ch], p["conv_w"][:ch])
         oracle.selective_scan(xs, p["dt"][b:b + 1, :ch], p["A"][:ch], p["Bm"][b:b + 1],
                               p["Cm"][b:b + 1], p["dt_bias"][:ch], p["Dskip"][:ch],
-                              p["z"][b:b + 1, :ch], nthreads=threads)
+                              p["z"][b:b + 1, :ch], nthreads=nthreads)
 
     t0 = time.perf_counter()
-    run(0, threads)
+    run(0, 4, 1)
+    single = 4 * L / (time.perf_counter() - t0) / 1e9
+    t0 = time.perf_counter()
+    run(0, threads, threads)
     per_ch = (time.perf_counter() - t0) / threads
     budget = int(target_s / max(per_ch, 1e-9) * threads)
     if budget >= B * D:
@@ -106,7 +120,7 @@ def cpu_baseline(p, B, D, L, target_s=20.0):
         rows, ch = 1, max(threads, min(D, budget) // threads * threads)
     t0 = time.perf_counter()
     for b in range(rows):
-        run(b, ch)
+        run(b, ch, threads)
     dt = time.perf_counter() - t0
     elems = rows * ch * L
     what = ("the whole workload" if rows * ch == B * D else
@@ -114,7 +128,31 @@ def cpu_baseline(p, B, D, L, target_s=20.0):
     return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{what}, all {L} steps: conv1d+SiLU then scan in fp64 on {threads} "
-                      f"host threads ({elems} elements)"}
+                      f"host threads ({elems} elements)",
+            "single_thread_value": round(single, 6),
+            "single_thread_sample": f"batch row 0, channels 0..3, all {L} steps, 1 thread",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def quantiles(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def valu_record(tr, elems, kernel_ms):
+    """VALU issue utilisation of the main scan kernel: wave-level VALU
+    instructions per launch (rocprofv3 SQ_INSTS_VALU on the same kernel source)
+    over the time of one launch, against the issue peak of one wave64 fp32
+    instruction per 4 cycles on each of 1024 SIMDs at 2.4 GHz."""
+    if tr is None or "valu_insts" not in tr:
+        return None
+    peak = 256 * 4 * 2.4e9 / 4
+    per_s = tr["valu_insts"] / (kernel_ms * 1e-3)
+    return {"wave_instr_per_launch": int(tr["valu_insts"]),
+            "wave_instr_per_elem": round(tr["valu_insts"] * 64 / elems, 1),
+            "issue_peak_per_s": peak, "frac": round(per_s / peak, 4)}
 
 
 def run_block(args, torch, mamba, W):
@@ -154,8 +192,10 @@ def run_block(args, torch, mamba, W):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     mamba.set_scan_timing_events_raw(None, None)
-    scan_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
-    conv_ms = float(np.mean([a.elapsed_time(b) for a, b in conv_ev]))
+    scan_all = [ev.elapsed_ms(a, b) for a, b in pairs]
+    scan_ms = float(np.mean(scan_all))
+    conv_all = [a.elapsed_time(b) for a, b in conv_ev]
+    conv_ms = float(np.mean(conv_all))
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
@@ -192,9 +232,10 @@ def run_block(args, torch, mamba, W):
                      "traffic": traffic, "kernel": "scan_main_kernel<fp32>",
                      "kernel_ms": round(scan_ms, 4),
                      "algorithmic_bytes": sb},
-        "kernels": {"scan_ms": round(scan_ms, 4),
+        "valu": valu_record(tr, elems, scan_ms),
+        "kernels": {"scan_ms": quantiles(scan_all),
                     "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2),
-                    "conv_ms": round(conv_ms, 4),
+                    "conv_ms": quantiles(conv_all),
                     "conv_GBps": round(cb / (conv_ms * 1e-3) / 1e9, 1)},
     }
     if not args.no_cpu:
@@ -228,7 +269,8 @@ def run_scan(args, torch, mamba, W, idx):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     mamba.set_scan_timing_events_raw(None, None)
-    scan_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+    scan_all = [ev.elapsed_ms(a, b) for a, b in pairs]
+    scan_ms = float(np.mean(scan_all))
     ms_step = elapsed / args.steps * 1e3
     elems = B * D * L
     sb = scan_bytes(B, D, L, N, 2 if bf else 4)
@@ -243,7 +285,8 @@ def run_scan(args, torch, mamba, W, idx):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": None, "kernel_ms": round(scan_ms, 4)},
-            "kernels": {"scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}}
+            "kernels": {"scan_ms": quantiles(scan_all),
+                        "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}}
 
 
 def run_decode(args, torch, mamba, W):

@@ -3,7 +3,7 @@
     python -m selective_state_space_80_amd.profiling trace  RESULTS.db
     python -m selective_state_space_80_amd.profiling counters RESULTS.db [RESULTS.db ...]
     python -m selective_state_space_80_amd.profiling traffic --fetch F.db --write W.db \
-        --copy-bytes N --kernel scan_main_kernel --out profiles/scan_traffic.json
+        --copy-bytes N --kernel scan_main_kernel [--sq SQ.db] --out profiles/scan_traffic.json
 
 ``trace`` prints per-kernel call counts and average durations in microseconds (from
 ``rocprofv3 --kernel-trace --stats``); ``counters`` prints per-kernel averages of
@@ -67,7 +67,7 @@ def _find(d, sub):
     raise KeyError(sub)
 
 
-def traffic(fetch_db, write_db, copy_bytes, kernel, source=None):
+def traffic(fetch_db, write_db, copy_bytes, kernel, source=None, sq_db=None):
     f = counters(fetch_db)
     w = counters(write_db)
     copy_f = _find(f, COPY_KERNEL)["FETCH_SIZE"] * 1024.0
@@ -79,6 +79,10 @@ def traffic(fetch_db, write_db, copy_bytes, kernel, source=None):
            "fetch_scale": copy_bytes / copy_f, "write_scale": copy_bytes / copy_w,
            "fetch_raw_bytes": kf, "write_raw_bytes": kw,
            "fetch_bytes": kf * copy_bytes / copy_f, "write_bytes": kw * copy_bytes / copy_w}
+    if sq_db:
+        sq = _find(counters(sq_db), kernel)
+        out["valu_insts"] = sq["SQ_INSTS_VALU"]
+        out["waves"] = sq["SQ_WAVES"]
     if source:
         out["scan_fwd_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
     return out
@@ -98,6 +102,7 @@ def main(argv=None):
     tr.add_argument("--copy-bytes", type=int, required=True)
     tr.add_argument("--kernel", default="scan_main_kernel")
     tr.add_argument("--source", default=None, help="kernel source to fingerprint")
+    tr.add_argument("--sq", default=None, help="run with SQ_INSTS_VALU and SQ_WAVES")
     tr.add_argument("--out", default=None)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
@@ -114,7 +119,7 @@ def main(argv=None):
             for cn, v in sorted(d.items()):
                 print(f"    {cn:28s} {v:18,.0f}")
     else:
-        rec = traffic(a.fetch, a.write, a.copy_bytes, a.kernel, a.source)
+        rec = traffic(a.fetch, a.write, a.copy_bytes, a.kernel, a.source, a.sq)
         text = json.dumps(rec, indent=1)
         if a.out:
             os.makedirs(os.path.dirname(a.out) or ".", exist_ok=True)
