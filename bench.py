@@ -4,7 +4,9 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 held in HBM: causal depthwise conv1d(k=4) + SiLU, then the fused selective
 scan (softplus step, ZOH, recurrence, readout, D skip, SiLU(z) gate), on the
-Mamba block at d_model=768 (B=2, D_inner=1536, L=8192, N=16, fp32 I/O).
+Mamba block at d_model=768 (B=2, D_inner=1536, L=8192, N=16, fp32 I/O).  By
+default the conv runs inside the scan kernel (mamba_conv1d_selective_scan_fwd);
+--unfused times the two separate calls.
 
 Prints ONE JSON line with the metric (scanned Gelem/s = B*L*D_inner / step
 time), the roofline of the dominant kernel (the main scan kernel, timed with
@@ -72,12 +74,15 @@ def conv_bytes(B, D, L, K, esz):
     return 2 * B * D * L * esz + D * K * 4
 
 
-def traffic_record():
-    """HBM traffic of the main scan kernel measured by rocprofv3 counters, if
-    taken on the current kernel source (else None)."""
+def traffic_record(variant):
+    """HBM traffic and VALU instruction count of the main scan kernel measured
+    by rocprofv3 counters on the block workload (`variant` = fused or
+    unfused), if taken on the current kernel source (else None)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        rec = json.load(open(TRAFFIC_FILE)).get(variant)
+    except (OSError, ValueError, AttributeError):
+        return None
+    if not rec:
         return None
     sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
     return rec if rec.get("scan_fwd_sha256") == sha else None
@@ -158,23 +163,32 @@ def valu_record(tr, elems, kernel_ms):
 def run_block(args, torch, mamba, W):
     wl = W.WORKLOADS[1]
     B, D, L, N = wl.B, wl.D, wl.L, wl.N
+    K = 4
     p = W.scan_inputs(wl)
     dev = torch.device("cuda:0")
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x_raw, cw = T(p["x_raw"]), T(p["conv_w"])
     dt, A, Bm, Cm = T(p["dt"]), T(p["A"]), T(p["Bm"]), T(p["Cm"])
     bias, Dk, z = T(p["dt_bias"]), T(p["Dskip"]), T(p["z"])
-    xc = torch.empty_like(x_raw)
     y = torch.empty_like(x_raw)
+    xc = torch.empty_like(x_raw) if args.unfused else None
     ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
                      device=dev)
 
-    def step():
+    def conv():
         mamba.conv1d_silu(x_raw, cw, None, out=xc)
-        mamba.selective_scan_fwd(xc, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+
+    def scan():
+        if args.unfused:
+            mamba.selective_scan_fwd(xc, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+        else:
+            mamba.conv1d_selective_scan_fwd(x_raw, cw, dt, A, Bm, Cm, dt_bias=bias, Dskip=Dk,
+                                            z=z, out=y, workspace=ws)
 
     for _ in range(args.warmup):
-        step()
+        if args.unfused:
+            conv()
+        scan()
     torch.cuda.synchronize()
 
     ev = HipEvents()
@@ -185,32 +199,40 @@ def run_block(args, torch, mamba, W):
     t0 = time.perf_counter()
     for i in range(args.steps):
         mamba.set_scan_timing_events_raw(pairs[i][0], pairs[i][1])
-        conv_ev[i][0].record()
-        mamba.conv1d_silu(x_raw, cw, None, out=xc)
-        conv_ev[i][1].record()
-        mamba.selective_scan_fwd(xc, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+        if args.unfused:
+            conv_ev[i][0].record()
+            conv()
+            conv_ev[i][1].record()
+        scan()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     mamba.set_scan_timing_events_raw(None, None)
     scan_all = [ev.elapsed_ms(a, b) for a, b in pairs]
     scan_ms = float(np.mean(scan_all))
-    conv_all = [a.elapsed_time(b) for a, b in conv_ev]
-    conv_ms = float(np.mean(conv_all))
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
 
     ms_step = elapsed / args.steps * 1e3
     elems = B * D * L
-    sb = scan_bytes(B, D, L, N, 4)
-    cb = conv_bytes(B, D, L, 4, 4)
+    # the fused kernel reads the raw input where the plain scan reads the conv
+    # output: the same bytes, plus the conv weights
+    sb = scan_bytes(B, D, L, N, 4) + (0 if args.unfused else D * K * 4)
+    cb = conv_bytes(B, D, L, K, 4)
     achieved = sb / (scan_ms * 1e-3) / 1e9
-    tr = traffic_record()
+    tr = traffic_record("unfused" if args.unfused else "fused")
     traffic = None
     if tr is not None:
         # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
         # a copy kernel of known size; null once the kernel source has changed
         traffic = int(round(tr["fetch_bytes"] + tr["write_bytes"]))
+    kname = "scan_main_kernel<fp32>" if args.unfused else "scan_main_kernel<fp32, conv>"
+    kernels = {"scan_ms": quantiles(scan_all),
+               "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}
+    if args.unfused:
+        conv_all = [a.elapsed_time(b) for a, b in conv_ev]
+        kernels["conv_ms"] = quantiles(conv_all)
+        kernels["conv_GBps"] = round(cb / (float(np.mean(conv_all)) * 1e-3) / 1e9, 1)
     out = {
         "metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
         "value": round(elems / (ms_step * 1e-3) / 1e9, 3),
@@ -225,18 +247,16 @@ def run_block(args, torch, mamba, W):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "d_model": 768, "d_inner": D, "seq_len": L,
-                   "d_state": N, "d_conv": 4, "io": "f32", "state": "f32",
-                   "step": "conv1d_silu + selective_scan_fwd"},
+                   "d_state": N, "d_conv": K, "io": "f32", "state": "f32",
+                   "step": ("conv1d_silu, then selective_scan_fwd" if args.unfused else
+                            "conv1d_selective_scan_fwd (conv1d+SiLU fused into the scan)")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "scan_main_kernel<fp32>",
+                     "traffic": traffic, "kernel": kname,
                      "kernel_ms": round(scan_ms, 4),
                      "algorithmic_bytes": sb},
         "valu": valu_record(tr, elems, scan_ms),
-        "kernels": {"scan_ms": quantiles(scan_all),
-                    "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2),
-                    "conv_ms": quantiles(conv_all),
-                    "conv_GBps": round(cb / (conv_ms * 1e-3) / 1e9, 1)},
+        "kernels": kernels,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(p, B, D, L)
@@ -338,6 +358,9 @@ def main():
     ap.add_argument("--workload", default="block",
                     choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--unfused", action="store_true",
+                    help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
+                         "instead of the fused entry point")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one elementwise kernel that reads and writes "
                          "this many MiB (known traffic for scaling rocprofv3 byte counters)")

@@ -5,6 +5,9 @@
  *   mamba_conv1d_silu            causal depthwise conv1d + SiLU front end
  *   mamba_selective_scan_fwd     fused selective-scan forward (prefill)
  *   mamba_selective_state_update single-token recurrent step (decode)
+ * and two that join the front end to the scan:
+ *   mamba_conv1d_selective_scan_fwd  conv1d + SiLU fused into the scan
+ *   mamba_conv1d_update              single-token conv step with its state
  * plus workspace sizing and status helpers.
  *
  * Conventions shared by every entry point
@@ -43,9 +46,10 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 1
+#define MAMBA_AMD_ABI_VERSION 2
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
+#define MAMBA_MAX_FUSED_CONV_TAPS 4
 
 typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_dtype;
 
@@ -134,6 +138,46 @@ mamba_status mamba_selective_state_update(float *h, const void *x, const void *d
                                           const void *Bm, const void *Cm, const float *Dskip,
                                           const void *z, void *y, int64_t B, int64_t D,
                                           int64_t N, mamba_dtype io, void *stream);
+
+/*
+ * The block's front end and the scan in one pass: the scan input is
+ * SiLU(causal depthwise conv1d of x_raw) ("Mamba状态空间模型深度解析：挑战
+ * Transformer的下一代序列建模范式", §3.1: causal Conv1D, then the selective
+ * SSM, then the SiLU gate), computed inside the scan kernel, so the conv
+ * output never goes to memory.  Same result as mamba_conv1d_silu followed by
+ * mamba_selective_scan_fwd, except that the conv output is not rounded to
+ * `io` in between.
+ *   x_raw          : [B, D, L] of `io`
+ *   conv_w         : [D, K] float, K in 1..4 (MAMBA_MAX_FUSED_CONV_TAPS)
+ *   conv_bias      : [D] float or NULL (= 0)
+ *   conv_state_in  : [B, D, K-1] of `io` or NULL (= zeros): raw inputs of the
+ *                    K-1 steps before t = 0, oldest first
+ *   conv_state_out : [B, D, K-1] of `io` or NULL (= not returned): raw inputs
+ *                    of the last K-1 steps (carried-in ones when L < K-1), for
+ *                    a later call or mamba_conv1d_update.  It may be the same
+ *                    buffer as conv_state_in; it must not overlap anything else.
+ * Every other argument is as for mamba_selective_scan_fwd (same workspace size).
+ */
+mamba_status mamba_conv1d_selective_scan_fwd(
+    const void *x_raw, const float *conv_w, const float *conv_bias, int64_t K,
+    const void *conv_state_in, void *conv_state_out, const void *dt, const float *dt_bias,
+    const float *A, const void *Bm, const void *Cm, const float *Dskip, const void *z,
+    const float *h0, void *y, float *h_last, void *workspace, size_t workspace_bytes, int64_t B,
+    int64_t D, int64_t L, int64_t N, mamba_dtype io, void *stream);
+
+/*
+ * Decode step of the front end ("Mamba架构深度剖析：如何以线性时间重塑序列建模",
+ * §3: recurrent inference with a fixed-size state; the causal conv keeps its
+ * last K-1 raw inputs as state):
+ *   out[b,d] = SiLU(bias[d] + sum_{k<K-1} w[d,k] state[b,d,k] + w[d,K-1] x[b,d])
+ *   state[b,d,:] <- (state[b,d,1:], x[b,d])
+ *   state   : [B, D, K-1] of `dtype`, read and overwritten (may be NULL when K = 1)
+ *   x, out  : [B, D] of `dtype`;  w : [D, K] float;  bias : [D] float or NULL
+ * K in 1..8.  out must not overlap state, x, w or bias.
+ */
+mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, const float *bias,
+                                 void *out, int64_t B, int64_t D, int64_t K, mamba_dtype dtype,
+                                 void *stream);
 
 /*
  * Profiling hook.  When both are non-NULL hipEvent_t handles (passed as

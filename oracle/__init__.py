@@ -67,6 +67,8 @@ class Oracle:
         lib.oracle_selective_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int]
         lib.oracle_conv1d_silu.restype = ctypes.c_int
         lib.oracle_conv1d_silu.argtypes = [P] * 4 + [I64] * 4 + [ctypes.c_int]
+        lib.oracle_conv1d_update.restype = ctypes.c_int
+        lib.oracle_conv1d_update.argtypes = [P] * 5 + [I64] * 3
         lib.oracle_state_update.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [P] * 10 + [I64] * 3
         self.lib = lib
@@ -120,6 +122,20 @@ class Oracle:
             raise ValueError("oracle_conv1d_silu rejected its arguments")
         return out
 
+    def conv1d_update(self, state, x, w, bias=None):
+        """One conv step with its state.  state [B,D,K-1] (not modified), x [B,D],
+        w [D,K].  Returns (out [B,D], state_new [B,D,K-1])."""
+        x, w, bias = _f64(x), _f64(w), _f64(bias)
+        Bsz, D = x.shape
+        K = w.shape[1]
+        state = np.array(state, dtype=np.float64, copy=True, order="C").reshape(Bsz, D, K - 1)
+        out = np.empty((Bsz, D), dtype=np.float64)
+        rc = self.lib.oracle_conv1d_update(_ptr(state) if K > 1 else None, _ptr(x), _ptr(w),
+                                           _ptr(bias), _ptr(out), Bsz, D, K)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_update rejected its arguments")
+        return out, state
+
     def state_update(self, h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None):
         """One decode step.  h [B,D,N] (not modified), x/dt/z [B,D], Bm/Cm [B,N].
         Returns (y [B,D], h_new [B,D,N])."""
@@ -172,3 +188,7 @@ def conv1d_silu(*args, **kw):
 
 def state_update(*args, **kw):
     return get().state_update(*args, **kw)
+
+
+def conv1d_update(*args, **kw):
+    return get().conv1d_update(*args, **kw)

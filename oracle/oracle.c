@@ -209,6 +209,35 @@ int oracle_conv1d_silu(const double *x, const double *w, const double *bias, dou
     return 0;
 }
 
+/* Single-token step of the causal conv with its state: the K-1 previous raw
+ * inputs of each channel, oldest first ([B, D, K-1], updated in place), stand
+ * for the part of the sequence the window still reaches ("Mamba架构深度剖析：
+ * 如何以线性时间重塑序列建模" §3, recurrent inference with a fixed-size
+ * state; the conv of "Mamba状态空间模型深度解析…" §3.1).
+ *   out[b,d] = SiLU(bias[d] + sum_{k<K-1} w[d,k] state[b,d,k] + w[d,K-1] x[b,d])
+ * then the window moves by one step: the oldest input leaves, x enters. */
+int oracle_conv1d_update(double *state, const double *x, const double *w, const double *bias,
+                         double *out, int64_t B, int64_t D, int64_t K)
+{
+    if (!x || !w || !out || B < 0 || D < 0 || K < 1 || (K > 1 && !state))
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            size_t c = (size_t)b * D + d;
+            double *st = K > 1 ? state + c * (size_t)(K - 1) : NULL;
+            double acc = bias ? bias[d] : 0.0;
+            for (int64_t k = 0; k < K - 1; ++k)
+                acc += w[d * K + k] * st[k];
+            acc += w[d * K + K - 1] * x[c];
+            out[c] = oracle_silu(acc);
+            for (int64_t k = 0; k + 1 < K - 1; ++k)
+                st[k] = st[k + 1];
+            if (K > 1)
+                st[K - 2] = x[c];
+        }
+    return 0;
+}
+
 /* Single-token decode step on a stored state h [B, D, N] (updated in place).
  * x, dt, z, y: [B, D];  Bm, Cm: [B, N]. */
 int oracle_state_update(double *h, const double *x, const double *dt, const double *dt_bias,

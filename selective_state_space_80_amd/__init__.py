@@ -12,6 +12,9 @@ Entry points (same names as the C ABI, without the ``mamba_`` prefix):
                      return_last_state=False, out=None, workspace=None)
   selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, out=None)
   selective_scan_fwd_workspace_size(B, D, L, N, dtype)
+  conv1d_selective_scan_fwd(x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None,
+                            conv_state_in=None, return_conv_state=False, ...)
+  conv1d_update(state, x, w, bias=None, out=None)
 """
 from __future__ import annotations
 
@@ -31,7 +34,8 @@ STATUS_NAMES = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MA
 # every symbol include/mamba_amd.h declares
 EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_selective_scan_fwd_workspace_size", "mamba_selective_scan_fwd",
-            "mamba_selective_state_update", "mamba_set_scan_timing_events"]
+            "mamba_selective_state_update", "mamba_conv1d_selective_scan_fwd",
+            "mamba_conv1d_update", "mamba_set_scan_timing_events"]
 
 _lib = None
 
@@ -64,6 +68,11 @@ def load_library(path: str = LIBRARY):
     lib.mamba_selective_scan_fwd.argtypes = [P] * 12 + [SZ, I64, I64, I64, I64, I32, P]
     lib.mamba_selective_state_update.restype = I32
     lib.mamba_selective_state_update.argtypes = [P] * 10 + [I64, I64, I64, I32, P]
+    lib.mamba_conv1d_selective_scan_fwd.restype = I32
+    lib.mamba_conv1d_selective_scan_fwd.argtypes = ([P, P, P, I64] + [P] * 13 +
+                                                    [SZ, I64, I64, I64, I64, I32, P])
+    lib.mamba_conv1d_update.restype = I32
+    lib.mamba_conv1d_update.argtypes = [P] * 5 + [I64, I64, I64, I32, P]
     lib.mamba_set_scan_timing_events.restype = None
     lib.mamba_set_scan_timing_events.argtypes = [P, P]
     _lib = lib
@@ -179,6 +188,83 @@ def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=No
     _raise(st, "mamba_selective_scan_fwd")
     if return_last_state:
         return out, h_last
+    return out
+
+
+def conv1d_selective_scan_fwd(x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None, conv_state_in=None,
+                              return_conv_state=False, conv_state_out=None, dt_bias=None,
+                              Dskip=None, z=None, h0=None, return_last_state=False, out=None,
+                              workspace=None, h_last=None):
+    """conv1d (K <= 4 taps) + SiLU fused into the selective scan.  x_raw [B,D,L]
+    (f32/bf16) is the raw block input; conv_w [D,K], conv_bias [D] f32;
+    conv_state_in / conv_state_out [B,D,K-1] of x_raw's dtype (the raw inputs
+    before t = 0 / of the last K-1 steps; out may be the same tensor as in).
+    Other arguments as for selective_scan_fwd.  Returns y, then h_last if
+    return_last_state, then the conv state if return_conv_state."""
+    torch = _torch()
+    lib = load_library()
+    B, D, L = x_raw.shape
+    N = A.shape[1]
+    K = conv_w.shape[1]
+    dev, io_t = x_raw.device, x_raw.dtype
+    _check(x_raw, "x_raw", (B, D, L), io_t, dev)
+    _check(conv_w, "conv_w", (D, K), torch.float32, dev)
+    _check(conv_bias, "conv_bias", (D,), torch.float32, dev, optional=True)
+    _check(conv_state_in, "conv_state_in", (B, D, K - 1), io_t, dev, optional=True)
+    _check(dt, "dt", (B, D, L), io_t, dev)
+    _check(z, "z", (B, D, L), io_t, dev, optional=True)
+    _check(Bm, "Bm", (B, L, N), io_t, dev)
+    _check(Cm, "Cm", (B, L, N), io_t, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (D,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
+    _check(h0, "h0", (B, D, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty_like(x_raw)
+    _check(out, "out", (B, D, L), io_t, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", (B, D, N), torch.float32, dev, optional=True)
+    if return_conv_state and conv_state_out is None:
+        conv_state_out = torch.empty((B, D, K - 1), dtype=io_t, device=dev)
+    _check(conv_state_out, "conv_state_out", (B, D, K - 1), io_t, dev, optional=True)
+    io = _io_dtype(x_raw)
+    need = int(lib.mamba_selective_scan_fwd_workspace_size(B, D, L, N, io))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mamba_conv1d_selective_scan_fwd(
+        _ptr(x_raw), _ptr(conv_w), _ptr(conv_bias), K, _ptr(conv_state_in), _ptr(conv_state_out),
+        _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0),
+        _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N, io,
+        _stream(dev))
+    _raise(st, "mamba_conv1d_selective_scan_fwd")
+    res = [out]
+    if return_last_state:
+        res.append(h_last)
+    if return_conv_state:
+        res.append(conv_state_out)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def conv1d_update(state, x, w, bias=None, out=None):
+    """One decode step of the conv front end.  state [B,D,K-1] (x's dtype) is
+    updated in place; x [B,D] f32/bf16; w [D,K], bias [D] f32.  Returns out
+    [B,D] = SiLU(conv) of x's dtype."""
+    torch = _torch()
+    lib = load_library()
+    B, D = x.shape
+    K = w.shape[1]
+    dev, io_t = x.device, x.dtype
+    _check(x, "x", (B, D), io_t, dev)
+    _check(w, "w", (D, K), torch.float32, dev)
+    _check(bias, "bias", (D,), torch.float32, dev, optional=True)
+    _check(state, "state", (B, D, K - 1), io_t, dev, optional=(K == 1))
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (B, D), io_t, dev)
+    st = lib.mamba_conv1d_update(_ptr(state), _ptr(x), _ptr(w), _ptr(bias), _ptr(out), B, D, K,
+                                 _io_dtype(x), _stream(dev))
+    _raise(st, "mamba_conv1d_update")
     return out
 
 

@@ -82,7 +82,8 @@ const char *mamba_status_string(int status)
     case MAMBA_ERR_NULL: return "MAMBA_ERR_NULL: a required pointer is NULL";
     case MAMBA_ERR_SHAPE: return "MAMBA_ERR_SHAPE: negative size or problem too large";
     case MAMBA_ERR_DTYPE: return "MAMBA_ERR_DTYPE: dtype must be MAMBA_F32 or MAMBA_BF16";
-    case MAMBA_ERR_UNSUPPORTED: return "MAMBA_ERR_UNSUPPORTED: N must be 1..16, K 1..8";
+    case MAMBA_ERR_UNSUPPORTED:
+        return "MAMBA_ERR_UNSUPPORTED: N must be 1..16, K 1..8 (1..4 when fused into the scan)";
     case MAMBA_ERR_ALIGN: return "MAMBA_ERR_ALIGN: pointer not aligned to its element size";
     case MAMBA_ERR_ALIAS: return "MAMBA_ERR_ALIAS: an output overlaps an input";
     case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE: workspace missing, misaligned or too small";
@@ -147,31 +148,56 @@ size_t mamba_selective_scan_fwd_workspace_size(int64_t B, int64_t D, int64_t L, 
     return mamba::scan_ws_layout(B, D, L).total;
 }
 
-mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float *dt_bias,
-                                      const float *A, const void *Bm, const void *Cm,
-                                      const float *Dskip, const void *z, const float *h0,
-                                      void *y, float *h_last, void *workspace,
-                                      size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
-                                      int64_t N, mamba_dtype io, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two scan entry points.  conv_K = 0: x is the scan input;
+// conv_K in 1..4: x is the raw input of the fused conv1d + SiLU front end.
+mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
+                        const float *conv_b, const void *conv_state_in, void *conv_state_out,
+                        const void *dt, const float *dt_bias, const float *A, const void *Bm,
+                        const void *Cm, const float *Dskip, const void *z, const float *h0,
+                        void *y, float *h_last, void *workspace, size_t workspace_bytes,
+                        int64_t B, int64_t D, int64_t L, int64_t N, mamba_dtype io,
+                        void *stream)
 {
     if (!valid_dtype(io))
         return MAMBA_ERR_DTYPE;
-    if (!sizes_ok(B, D, L) || N < 0)
+    if (!sizes_ok(B, D, L) || N < 0 || conv_K < 0)
         return MAMBA_ERR_SHAPE;
     if (N < 1 || N > kMaxN)
+        return MAMBA_ERR_UNSUPPORTED;
+    const bool conv = conv_K != 0;
+    if (conv && conv_K > mamba::kFusedConvTaps)
         return MAMBA_ERR_UNSUPPORTED;
     if (B * D == 0)
         return MAMBA_OK;
     const int64_t n = B * D * L;
     const size_t es = esize(io);
+    const size_t cs_bytes = conv ? (size_t)(B * D * (conv_K - 1)) * es : 0;
+    const Range r_csin = rng(conv_state_in, conv_state_in ? cs_bytes : 0);
+    const Range r_csout = rng(conv_state_out, conv_state_out ? cs_bytes : 0);
+    if (conv) {
+        if (!conv_w)
+            return MAMBA_ERR_NULL;
+        if (!aligned(conv_w, 4) || !aligned(conv_b, 4) || !aligned(conv_state_in, es) ||
+            !aligned(conv_state_out, es))
+            return MAMBA_ERR_ALIGN;
+    }
     if (L == 0) {
-        // nothing to scan; h_last (if asked for) is the initial state
-        if (!h_last)
-            return MAMBA_OK;
+        // nothing to scan; h_last (if asked for) is the initial state, the
+        // conv state (if asked for) the carried-in one
         if (!aligned(h_last, 4) || !aligned(h0, 4))
             return MAMBA_ERR_ALIGN;
-        if (h0 && overlap(rng(h_last, (size_t)(B * D * N) * 4), rng(h0, (size_t)(B * D * N) * 4)))
+        const Range rh = rng(h_last, h_last ? (size_t)(B * D * N) * 4 : 0);
+        if (h0 && overlap(rh, rng(h0, (size_t)(B * D * N) * 4)))
             return MAMBA_ERR_ALIAS;
+        if (overlap(r_csout, rh) || overlap(r_csout, rng(h0, h0 ? (size_t)(B * D * N) * 4 : 0)) ||
+            overlap(r_csin, rh))
+            return MAMBA_ERR_ALIAS;
+        if (!h_last && !conv_state_out)
+            return MAMBA_OK;
     } else {
         if (!x || !dt || !A || !Bm || !Cm || !y)
             return MAMBA_ERR_NULL;
@@ -194,13 +220,25 @@ mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float
                              rng(Cm, (size_t)(B * L * N) * es), rng(A, (size_t)(D * N) * 4),
                              rng(dt_bias, dt_bias ? (size_t)D * 4 : 0),
                              rng(Dskip, Dskip ? (size_t)D * 4 : 0),
-                             rng(h0, h0 ? (size_t)(B * D * N) * 4 : 0)};
+                             rng(h0, h0 ? (size_t)(B * D * N) * 4 : 0),
+                             rng(conv_w, conv ? (size_t)(D * conv_K) * 4 : 0),
+                             rng(conv_b, conv && conv_b ? (size_t)D * 4 : 0),
+                             r_csin};
         for (const Range &r : ins)
             if (overlap(ry, r) || overlap(rh, r) || overlap(rw, r))
                 return MAMBA_ERR_ALIAS;
         if (overlap(ry, rh) || overlap(ry, rw) || overlap(rh, rw))
             return MAMBA_ERR_ALIAS;
+        // the conv state out may only share memory with the conv state in
+        for (const Range &r : ins)
+            if (!(r.lo == r_csin.lo && r.hi == r_csin.hi) && overlap(r_csout, r))
+                return MAMBA_ERR_ALIAS;
+        if (overlap(r_csout, ry) || overlap(r_csout, rh) || overlap(r_csout, rw))
+            return MAMBA_ERR_ALIAS;
     }
+    // a conv state out that overlaps the one in must be the very same buffer
+    if (overlap(r_csout, r_csin) && !(r_csout.lo == r_csin.lo && r_csout.hi == r_csin.hi))
+        return MAMBA_ERR_ALIAS;
     mamba_status st = device_ok();
     if (st != MAMBA_OK)
         return st;
@@ -223,9 +261,82 @@ mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float
     a.L = L;
     a.N = (int)N;
     a.bf16 = io == MAMBA_BF16;
+    a.conv_K = (int)conv_K;
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    a.conv_state_in = conv_state_in;
+    a.conv_state_out = conv_state_out;
     a.ev_start = g_ev_start;
     a.ev_stop = g_ev_stop;
     return launched(mamba::launch_selective_scan(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float *dt_bias,
+                                      const float *A, const void *Bm, const void *Cm,
+                                      const float *Dskip, const void *z, const float *h0,
+                                      void *y, float *h_last, void *workspace,
+                                      size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
+                                      int64_t N, mamba_dtype io, void *stream)
+{
+    return scan_entry(x, 0, nullptr, nullptr, nullptr, nullptr, dt, dt_bias, A, Bm, Cm, Dskip,
+                      z, h0, y, h_last, workspace, workspace_bytes, B, D, L, N, io, stream);
+}
+
+mamba_status mamba_conv1d_selective_scan_fwd(
+    const void *x_raw, const float *conv_w, const float *conv_bias, int64_t K,
+    const void *conv_state_in, void *conv_state_out, const void *dt, const float *dt_bias,
+    const float *A, const void *Bm, const void *Cm, const float *Dskip, const void *z,
+    const float *h0, void *y, float *h_last, void *workspace, size_t workspace_bytes, int64_t B,
+    int64_t D, int64_t L, int64_t N, mamba_dtype io, void *stream)
+{
+    if (K < 0)
+        return valid_dtype(io) ? MAMBA_ERR_SHAPE : MAMBA_ERR_DTYPE;
+    if (K == 0)
+        return valid_dtype(io) ? MAMBA_ERR_UNSUPPORTED : MAMBA_ERR_DTYPE;
+    return scan_entry(x_raw, K, conv_w, conv_bias, conv_state_in, conv_state_out, dt, dt_bias, A,
+                      Bm, Cm, Dskip, z, h0, y, h_last, workspace, workspace_bytes, B, D, L, N, io,
+                      stream);
+}
+
+mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, const float *bias,
+                                 void *out, int64_t B, int64_t D, int64_t K, mamba_dtype dtype,
+                                 void *stream)
+{
+    if (!valid_dtype(dtype))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, D, 1) || K < 0)
+        return MAMBA_ERR_SHAPE;
+    if (K < 1 || K > MAMBA_MAX_CONV_TAPS)
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t n = B * D;
+    if (n == 0)
+        return MAMBA_OK;
+    if (!x || !w || !out || (K > 1 && !state))
+        return MAMBA_ERR_NULL;
+    const size_t es = esize(dtype);
+    if (!aligned(state, es) || !aligned(x, es) || !aligned(out, es) || !aligned(w, 4) ||
+        !aligned(bias, 4))
+        return MAMBA_ERR_ALIGN;
+    const Range ro = rng(out, (size_t)n * es);
+    const Range rs = rng(state, K > 1 ? (size_t)(n * (K - 1)) * es : 0);
+    const Range ins[] = {rng(x, (size_t)n * es), rng(w, (size_t)(D * K) * 4),
+                         rng(bias, bias ? (size_t)D * 4 : 0)};
+    for (const Range &r : ins)
+        if (overlap(ro, r) || overlap(rs, r))
+            return MAMBA_ERR_ALIAS;
+    if (overlap(ro, rs))
+        return MAMBA_ERR_ALIAS;
+    if ((n + 255) / 256 >= (int64_t(1) << 31))
+        return MAMBA_ERR_SHAPE;
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::ConvUpdateArgs a{state, x, w, bias, out, B, D, (int)K, dtype == MAMBA_BF16};
+    return launched(mamba::launch_conv1d_update(a, (hipStream_t)stream));
 }
 
 mamba_status mamba_selective_state_update(float *h, const void *x, const void *dt,

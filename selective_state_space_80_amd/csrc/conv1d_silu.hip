@@ -153,7 +153,56 @@ hipError_t launch_k(const ConvArgs &a, hipStream_t s)
     }
 }
 
+// Decode step of the front end: one new input per channel, the K-1 previous
+// raw inputs carried in `state` ([B, D, K-1], oldest first).
+//   out[b,d] = SiLU(bias_d + sum_{k<K-1} w[d,k] state[b,d,k] + w[d,K-1] x[b,d])
+//   state[b,d,:] <- (state[b,d,1:], x[b,d])
+// One thread per channel; the state moves by one slot in place.
+template <bool BF16>
+__global__ void __launch_bounds__(256) conv1d_update_kernel(void *__restrict__ state_,
+                                                            const void *__restrict__ x_,
+                                                            const float *__restrict__ w,
+                                                            const float *__restrict__ bias,
+                                                            void *__restrict__ out_, int64_t D,
+                                                            int64_t n, int K)
+{
+    using E = Elem<BF16>;
+    using T = typename E::T;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const int64_t d = i % D;
+    T *state = reinterpret_cast<T *>(state_) + i * (K - 1);
+    const T xraw = reinterpret_cast<const T *>(x_)[i];
+    float acc = bias ? bias[d] : 0.f;
+    for (int k = 0; k < K - 1; ++k) {
+        const T v = state[k];
+        acc = fmaf(w[d * K + k], E::load(&v), acc);
+        if (k > 0)
+            state[k - 1] = v;
+    }
+    acc = fmaf(w[d * K + K - 1], E::load(&xraw), acc);
+    if (K > 1)
+        state[K - 2] = xraw;
+    E::store(reinterpret_cast<T *>(out_) + i, silu_hw(acc));
+}
+
 }  // namespace
+
+hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s)
+{
+    const int64_t n = a.B * a.D;
+    if (n == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (a.bf16)
+        hipLaunchKernelGGL(conv1d_update_kernel<true>, grid, dim3(256), 0, s, a.state, a.x, a.w,
+                           a.bias, a.out, a.D, n, a.K);
+    else
+        hipLaunchKernelGGL(conv1d_update_kernel<false>, grid, dim3(256), 0, s, a.state, a.x, a.w,
+                           a.bias, a.out, a.D, n, a.K);
+    return hipGetLastError();
+}
 
 hipError_t launch_conv1d_silu(const ConvArgs &a, hipStream_t s)
 {

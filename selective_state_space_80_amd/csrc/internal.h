@@ -32,6 +32,9 @@ struct ScanWsLayout {
 };
 ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L);
 
+// Fused causal conv1d front end of the scan: at most this many taps.
+constexpr int kFusedConvTaps = 4;
+
 struct ScanArgs {
     const void *x, *dt, *Bm, *Cm, *z;
     const float *dt_bias, *A, *Dskip, *h0;
@@ -42,6 +45,12 @@ struct ScanArgs {
     int64_t B, D, L;
     int N;
     bool bf16;
+    // fused front end (conv_K = 0: x is the scan input itself; else x is the
+    // raw input and the scan input is SiLU(causal conv1d(x)))
+    int conv_K;
+    const float *conv_w, *conv_b;
+    const void *conv_state_in;
+    void *conv_state_out;
     hipEvent_t ev_start, ev_stop;  // optional timing of the main kernel
 };
 hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s);
@@ -55,6 +64,17 @@ struct ConvArgs {
     bool bf16;
 };
 hipError_t launch_conv1d_silu(const ConvArgs &a, hipStream_t s);
+
+struct ConvUpdateArgs {
+    void *state;  // [B, D, K-1] of the I/O type, in/out
+    const void *x;
+    const float *w, *bias;
+    void *out;
+    int64_t B, D;
+    int K;
+    bool bf16;
+};
+hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);
 
 struct StepArgs {
     float *h;

@@ -313,7 +313,58 @@ struct ScanKArgs {
     int64_t B, D, L;
     int N;
     int vec;  // rows of x, dt, z, y are 16-byte aligned for vector access
+    // fused front end (CONV instantiation only): x holds the raw input
+    const float *conv_w, *conv_b;
+    const void *conv_state_in;  // [B, D, K-1] raw inputs before t = 0, or NULL (zeros)
+    int conv_K;
 };
+
+// Fused front end: the chunk's scan inputs SiLU(bias + sum_k w_k x_(t-K+1+k))
+// from the raw inputs of the chunk (already in `xin`) and of the three steps
+// before it.  Taps are right-aligned in kFusedConvTaps slots (zero weights in
+// front for K < 4).  Computed from the last step down, so each raw value is
+// still available when the outputs that need it are formed.  Steps at or past
+// the end of the sequence get the identity input 0.
+template <bool BF16>
+__device__ __forceinline__ void conv_chunk(const ScanKArgs &p, const InChunk<BF16> &xin,
+                                           int64_t bd, int64_t dc, int64_t t0, int64_t row_off,
+                                           int nt, float (&xc)[kChunkT])
+{
+    using E = Elem<BF16>;
+    using T = typename E::T;
+    const int K = p.conv_K;
+    float wk[kFusedConvTaps];
+#pragma unroll
+    for (int s = 0; s < kFusedConvTaps; ++s) {
+        const int k = s - (kFusedConvTaps - K);
+        wk[s] = (k >= 0) ? p.conv_w[dc * K + k] : 0.f;
+    }
+    const float cb = p.conv_b ? p.conv_b[dc] : 0.f;
+    float hm[kFusedConvTaps - 1];  // raw x at t0-3, t0-2, t0-1
+#pragma unroll
+    for (int i = 0; i < kFusedConvTaps - 1; ++i) {
+        const int64_t t = t0 - (kFusedConvTaps - 1) + i;
+        if (t >= p.L) {
+            hm[i] = 0.f;  // a wave past the end of the sequence (nt = 0) reads nothing
+        } else if (t >= 0) {
+            hm[i] = E::load(reinterpret_cast<const T *>(p.x) + row_off - (kFusedConvTaps - 1) + i);
+        } else {
+            const int64_t si = (int64_t)(K - 1) + t;  // slot of the carried raw inputs
+            hm[i] = (p.conv_state_in && si >= 0)
+                        ? E::load(reinterpret_cast<const T *>(p.conv_state_in) + bd * (K - 1) + si)
+                        : 0.f;
+        }
+    }
+    auto raw = [&](int i) -> float { return i >= 0 ? xin.get(i) : hm[kFusedConvTaps - 1 + i]; };
+#pragma unroll
+    for (int j = kChunkT - 1; j >= 0; --j) {
+        float acc = cb;
+#pragma unroll
+        for (int s = 0; s < kFusedConvTaps; ++s)
+            acc = fmaf(wk[s], raw(j - (kFusedConvTaps - 1) + s), acc);
+        xc[j] = (j < nt) ? silu_hw(acc) : 0.f;
+    }
+}
 
 // Apply the chunk map (f, S) to a state: h_n <- P_n(f) h_n + S_n, where
 //   structured: f = prod of e over the chunk, P_n = f^(n+1)
@@ -344,7 +395,7 @@ __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 }
 
 // The whole per-workgroup body for one arithmetic path.
-template <bool BF16, bool STRUCT>
+template <bool BF16, bool STRUCT, bool CONV>
 __device__ __forceinline__ void scan_segment(
     const ScanKArgs &p, const float *__restrict__ bcp, const float *__restrict__ crp,
     uint32_t *__restrict__ flags, float *__restrict__ agg, float *__restrict__ incl,
@@ -392,6 +443,15 @@ __device__ __forceinline__ void scan_segment(
         InChunk<BF16> xin, din;
         xin.load(p.x, row_off, nt, vec, 0.f);
         din.load(p.dt, row_off, nt, vec, -__builtin_huge_valf());
+        float xc[kChunkT];  // scan inputs of the fused front end (CONV only)
+        if constexpr (CONV)
+            conv_chunk<BF16>(p, xin, b * p.D + dc, dc, t0, row_off, nt, xc);
+        auto xget = [&](int j) -> float {
+            if constexpr (CONV)
+                return xc[j];
+            else
+                return xin.get(j);
+        };
         if constexpr (STRUCT) {
             // The segment's 128 prepared rows [B | C/(n+1)] (16 KB) go to LDS
             // with one 128-bit load per thread and row quarter; every step then
@@ -417,7 +477,7 @@ __device__ __forceinline__ void scan_segment(
         for (int j = 0; j < kChunkT; ++j) {
             if (j < nt) {  // one basic block per step
                 const float l = softplus_log2(fmaf(din.get(j), kLog2e, bias2));  // Δ/ln2
-                const float xv = xin.get(j);
+                const float xv = xget(j);
                 float acc = 0.f;
                 if constexpr (STRUCT) {
                     const float *Bj = s_bc[0][w * kChunkT + j];  // B (LDS broadcast)
@@ -679,7 +739,7 @@ __device__ __forceinline__ void scan_segment(
     TRACE_POINT(6);
 }
 
-template <bool BF16>
+template <bool BF16, bool CONV>
 __global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan_main_kernel(
     ScanKArgs p, const float *__restrict__ bcp, const float *__restrict__ crp,
     const uint32_t *__restrict__ tiles)
@@ -707,11 +767,11 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan
     const int64_t dtile = g % p.lay.n_dtiles;
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
-        scan_segment<BF16, true>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg, s_part,
-                                 s_bc);
+        scan_segment<BF16, true, CONV>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
+                                       s_part, s_bc);
     else
-        scan_segment<BF16, false>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
-                                  s_part, s_bc);
+        scan_segment<BF16, false, CONV>(p, bcp, crp, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
+                                        s_part, s_bc);
 }
 
 // Writes h_last = h0 (or zeros) for an empty sequence (L == 0).
@@ -721,6 +781,29 @@ __global__ void copy_or_zero_kernel(const float *__restrict__ src, float *__rest
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n)
         dst[i] = src ? src[i] : 0.f;
+}
+
+// Raw inputs a later call continues from: the last K-1 steps of the sequence
+// with the carried-in ones in front, state_out[s] = x_ext[L + s] where
+// x_ext[t] = x[t] for t >= 0 and state_in[K-1+t] (or 0) for t < 0.  One
+// thread per channel, slots in increasing order, so state_out may be the same
+// buffer as state_in (slot s reads slot L+s >= s before slot s is written).
+template <typename T>
+__global__ void conv_state_kernel(const T *__restrict__ x, const T *state_in, T *state_out,
+                                  int64_t BD, int64_t L, int K)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= BD)
+        return;
+    for (int s = 0; s < K - 1; ++s) {
+        const int64_t t = L - (K - 1) + s;
+        T v = T(0);
+        if (t >= 0)
+            v = x[i * L + t];
+        else if (state_in)
+            v = state_in[i * (K - 1) + (K - 1) + t];
+        state_out[i * (K - 1) + s] = v;
+    }
 }
 
 }  // namespace
@@ -757,14 +840,31 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L)
 hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
 {
     const ScanWsLayout &lay = a.lay;
+    const int64_t BD = a.B * a.D;
+    auto conv_state = [&]() -> hipError_t {
+        if (!a.conv_K || !a.conv_state_out || a.conv_K < 2 || BD == 0)
+            return hipSuccess;
+        const dim3 grid((unsigned)((BD + 255) / 256));
+        if (a.bf16)
+            hipLaunchKernelGGL(conv_state_kernel<uint16_t>, grid, dim3(256), 0, s,
+                               (const uint16_t *)a.x, (const uint16_t *)a.conv_state_in,
+                               (uint16_t *)a.conv_state_out, BD, a.L, a.conv_K);
+        else
+            hipLaunchKernelGGL(conv_state_kernel<float>, grid, dim3(256), 0, s,
+                               (const float *)a.x, (const float *)a.conv_state_in,
+                               (float *)a.conv_state_out, BD, a.L, a.conv_K);
+        return hipGetLastError();
+    };
     if (a.L == 0) {
         if (a.h_last) {
             const int64_t n = a.B * a.D * a.N;
             hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)((n + 255) / 256)),
                                dim3(256), 0, s, a.h0, a.h_last, n);
-            return hipGetLastError();
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
         }
-        return hipSuccess;
+        return conv_state();
     }
     if (lay.n_items == 0)
         return hipSuccess;
@@ -800,6 +900,10 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     k.D = a.D;
     k.L = a.L;
     k.N = a.N;
+    k.conv_w = a.conv_w;
+    k.conv_b = a.conv_b;
+    k.conv_state_in = a.conv_state_in;
+    k.conv_K = a.conv_K;
     const size_t esz = a.bf16 ? 2 : 4;
     const uintptr_t amask = (uintptr_t)a.x | (uintptr_t)a.dt | (uintptr_t)a.y |
                             (uintptr_t)(a.z ? a.z : a.x);
@@ -808,17 +912,28 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     const float *crp = reinterpret_cast<const float *>(a.ws + lay.off_craw);
     const uint32_t *tiles = reinterpret_cast<const uint32_t *>(a.ws + lay.off_tiles);
     if (a.ev_start)
-        hipEventRecord(a.ev_start, s);
-    if (a.bf16)
-        hipLaunchKernelGGL(scan_main_kernel<true>, dim3((unsigned)lay.n_items),
-                           dim3(kWave * kWavesPerSeg), 0, s, k, bcp, crp, tiles);
-    else
-        hipLaunchKernelGGL(scan_main_kernel<false>, dim3((unsigned)lay.n_items),
-                           dim3(kWave * kWavesPerSeg), 0, s, k, bcp, crp, tiles);
+        (void)hipEventRecord(a.ev_start, s);
+    const dim3 grid((unsigned)lay.n_items), block(kWave * kWavesPerSeg);
+    if (a.bf16) {
+        if (a.conv_K)
+            hipLaunchKernelGGL((scan_main_kernel<true, true>), grid, block, 0, s, k, bcp, crp, tiles);
+        else
+            hipLaunchKernelGGL((scan_main_kernel<true, false>), grid, block, 0, s, k, bcp, crp,
+                               tiles);
+    } else {
+        if (a.conv_K)
+            hipLaunchKernelGGL((scan_main_kernel<false, true>), grid, block, 0, s, k, bcp, crp,
+                               tiles);
+        else
+            hipLaunchKernelGGL((scan_main_kernel<false, false>), grid, block, 0, s, k, bcp, crp,
+                               tiles);
+    }
     e = hipGetLastError();
     if (a.ev_stop)
-        hipEventRecord(a.ev_stop, s);
-    return e;
+        (void)hipEventRecord(a.ev_stop, s);
+    if (e != hipSuccess)
+        return e;
+    return conv_state();
 }
 
 }  // namespace mamba

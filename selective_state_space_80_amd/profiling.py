@@ -3,7 +3,8 @@
     python -m selective_state_space_80_amd.profiling trace  RESULTS.db
     python -m selective_state_space_80_amd.profiling counters RESULTS.db [RESULTS.db ...]
     python -m selective_state_space_80_amd.profiling traffic --fetch F.db --write W.db \
-        --copy-bytes N --kernel scan_main_kernel [--sq SQ.db] --out profiles/scan_traffic.json
+        --copy-bytes N --kernel scan_main_kernel [--sq SQ.db] [--variant fused|unfused] \
+        --out profiles/scan_traffic.json
 
 ``trace`` prints per-kernel call counts and average durations in microseconds (from
 ``rocprofv3 --kernel-trace --stats``); ``counters`` prints per-kernel averages of
@@ -103,6 +104,8 @@ def main(argv=None):
     tr.add_argument("--kernel", default="scan_main_kernel")
     tr.add_argument("--source", default=None, help="kernel source to fingerprint")
     tr.add_argument("--sq", default=None, help="run with SQ_INSTS_VALU and SQ_WAVES")
+    tr.add_argument("--variant", default="fused",
+                    help="key of the record in --out (fused / unfused block step)")
     tr.add_argument("--out", default=None)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
@@ -120,12 +123,18 @@ def main(argv=None):
                 print(f"    {cn:28s} {v:18,.0f}")
     else:
         rec = traffic(a.fetch, a.write, a.copy_bytes, a.kernel, a.source, a.sq)
-        text = json.dumps(rec, indent=1)
+        print(json.dumps(rec, indent=1))
         if a.out:
+            try:
+                allrec = json.load(open(a.out))
+                if "kernel" in allrec:  # a single record of an older layout
+                    allrec = {}
+            except (OSError, ValueError):
+                allrec = {}
+            allrec[a.variant] = rec
             os.makedirs(os.path.dirname(a.out) or ".", exist_ok=True)
             with open(a.out, "w") as fh:
-                fh.write(text + "\n")
-        print(text)
+                fh.write(json.dumps(allrec, indent=1) + "\n")
     return 0
 
 

@@ -329,6 +329,38 @@ def pin_conv(orc):
     _close(out[0, 0], [0.4, 0.3, -0.2, 0.1, 0, 0, 0, 0], 0, 0, what="impulse")
 
 
+def pin_conv_update(orc):
+    """Conv steps with a carried window equal numpy.convolve over the whole
+    sequence, the carried-in inputs in front (and a first window of zeros is
+    the zero padding of the causal conv)."""
+    rng = np.random.default_rng(23)
+    for K in (1, 2, 4, 6):
+        Bsz, D, T = 2, 3, 9
+        pre_in = rng.normal(size=(Bsz, D, K - 1))
+        xs = rng.normal(size=(Bsz, D, T))
+        w = rng.normal(0, 0.5, size=(D, K))
+        bias = rng.normal(size=D)
+        full = np.concatenate([pre_in, xs], axis=2)
+        want = np.stack([np.stack([np.convolve(full[b, d], w[d, ::-1])[K - 1:K - 1 + T] + bias[d]
+                                   for d in range(D)]) for b in range(Bsz)])
+        want = want * expit(want)
+        state = pre_in.copy()
+        for t in range(T):
+            out, state = orc.conv1d_update(state, xs[:, :, t], w, bias)
+            _close(out, want[:, :, t], 1e-13, 1e-15, what=f"conv update K={K} t={t}")
+        _close(state, full[:, :, T:], 0, 0, what=f"conv window K={K}")
+    # starting from a zero window reproduces the zero-padded conv
+    K, T = 4, 6
+    x = rng.normal(size=(1, 2, T))
+    w = rng.normal(size=(2, K))
+    state = np.zeros((1, 2, K - 1))
+    got = []
+    for t in range(T):
+        o, state = orc.conv1d_update(state, x[:, :, t], w)
+        got.append(o)
+    _close(np.stack(got, axis=2), orc.conv1d_silu(x, w), 1e-14, 1e-15, what="zero window")
+
+
 def pin_decode_step(orc):
     """One decode step equals the exact ZOH update and gated readout, and L
     steps equal one scan over L."""
@@ -369,6 +401,6 @@ def pin_threads(orc):
     assert np.array_equal(y1, y4) and np.array_equal(h1, h4), "thread count changed result"
 
 
-ALL_PINS = [pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
+ALL_PINS = [pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
             pin_dc_gain, pin_lti_convolution, pin_chunked_carry, pin_special_cases,
             pin_hand_expansions, pin_golden_ln2, pin_conv, pin_decode_step, pin_threads]

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 1
+    assert lib.mamba_abi_version() == 2
     for st in range(10):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -120,8 +120,58 @@ def test_state_update_rejects(lib):
     assert f(*args, 0, 64, 16, F32, None) == OK
 
 
+def fused(lib, **kw):
+    a = dict(x=P(1), w=P(13), cb=P(14), K=4, csin=P(15), csout=P(16), dt=P(2), dt_bias=P(3),
+             A=P(4), Bm=P(5), Cm=P(6), Dskip=P(7), z=P(8), h0=P(9), y=P(10), h_last=P(11),
+             ws=P(12), ws_bytes=1 << 40, B=2, D=64, L=256, N=16, io=F32)
+    a.update(kw)
+    return lib.mamba_conv1d_selective_scan_fwd(
+        a["x"], a["w"], a["cb"], a["K"], a["csin"], a["csout"], a["dt"], a["dt_bias"], a["A"],
+        a["Bm"], a["Cm"], a["Dskip"], a["z"], a["h0"], a["y"], a["h_last"], a["ws"],
+        a["ws_bytes"], a["B"], a["D"], a["L"], a["N"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(io=7), EDTYPE), (dict(K=0), EUNSUP), (dict(K=5), EUNSUP), (dict(K=-1), ESHAPE),
+    (dict(N=17), EUNSUP), (dict(w=None), ENULL), (dict(x=None), ENULL),
+    (dict(w=ctypes.c_void_p(0xD0000000002)), EALIGN),
+    (dict(io=BF16, csout=ctypes.c_void_p(0xF0000000001)), EALIGN),
+    (dict(y=P(13)), EALIAS), (dict(y=P(15)), EALIAS), (dict(h_last=P(14)), EALIAS),
+    (dict(csout=P(1)), EALIAS), (dict(csout=P(10)), EALIAS), (dict(csout=P(12)), EALIAS),
+    (dict(csout=ctypes.c_void_p(0x10000000000 + 15 * 0x100000000 + 4)), EALIAS),
+    (dict(ws=None), EWS),
+])
+def test_fused_scan_rejects(lib, kw, want):
+    assert fused(lib, **kw) == want
+
+
+def test_fused_scan_empty_is_ok(lib):
+    assert fused(lib, B=0) == OK
+    assert fused(lib, D=0, x=None, w=None) == OK
+
+
+def test_conv_update_rejects(lib):
+    f = lib.mamba_conv1d_update
+    assert f(P(1), P(2), P(3), None, P(4), 2, 8, 9, F32, None) == EUNSUP
+    assert f(P(1), P(2), P(3), None, P(4), 2, 8, 0, F32, None) == EUNSUP
+    assert f(P(1), P(2), P(3), None, P(4), 2, 8, 4, 3, None) == EDTYPE
+    assert f(None, P(2), P(3), None, P(4), 2, 8, 4, F32, None) == ENULL
+    assert f(P(1), None, P(3), None, P(4), 2, 8, 4, F32, None) == ENULL
+    assert f(P(1), P(2), P(3), None, P(1), 2, 8, 4, F32, None) == EALIAS
+    assert f(P(1), P(2), P(3), None, P(2), 2, 8, 4, F32, None) == EALIAS
+    assert f(P(2), P(2), P(3), None, P(4), 2, 8, 4, F32, None) == EALIAS
+    assert f(P(1), P(2), P(3), None, ctypes.c_void_p(0x40000000001), 2, 8, 4, BF16,
+             None) == EALIGN
+    assert f(P(1), P(2), P(3), None, P(4), -2, 8, 4, F32, None) == ESHAPE
+    assert f(P(1), P(2), P(3), None, P(4), 0, 8, 4, F32, None) == OK
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="valid fake pointers must never reach a GPU")
 def test_valid_arguments_without_gpu_report_device(lib):
+    assert fused(lib) == EDEV
+    assert fused(lib, csout=P(15)) == EDEV  # conv state updated in place
+    assert lib.mamba_conv1d_update(P(1), P(2), P(3), None, P(4), 2, 8, 4, F32, None) == EDEV
+    assert lib.mamba_conv1d_update(None, P(2), P(3), None, P(4), 2, 8, 1, F32, None) == EDEV
     assert scan(lib) == EDEV
     assert lib.mamba_conv1d_silu(P(1), P(2), None, P(3), 2, 8, 32, 4, F32, None) == EDEV
     assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),

@@ -35,6 +35,8 @@ MUTANTS = [
     ("conv_bias_dropped", "double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
     ("dskip_channel_index", "j->Dskip ? j->Dskip[d] : 0.0", "j->Dskip ? j->Dskip[0] : 0.0"),
     ("a_row_index", "j->A + d * j->N,", "j->A,"),
+    ("conv_window_not_moved", "                st[k] = st[k + 1];", "                st[k] = st[k];"),
+    ("conv_update_new_input_tap", "acc += w[d * K + K - 1] * x[c];", "acc += w[d * K] * x[c];"),
 ]
 
 
