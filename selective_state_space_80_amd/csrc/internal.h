@@ -19,7 +19,6 @@ constexpr int kSegT = kChunkT * kWavesPerSeg;
 constexpr int kMaxN = 16;
 constexpr int kAggFields = kMaxN + 1;  // decay summary + N states
 constexpr int kInclFields = kMaxN;
-constexpr int kBCStride = 2 * kMaxN;   // prepared per-(b,t) row: B, C/(n+1) (128 bytes)
 
 // Byte offsets of the parts of the scan workspace for one problem shape.
 struct ScanWsLayout {
@@ -27,8 +26,7 @@ struct ScanWsLayout {
     int64_t groups = 0;    // B * n_dtiles
     int64_t n_seg = 0;     // ceil(L / kSegT)
     int64_t n_items = 0;   // groups * n_seg
-    size_t off_header = 0, off_flags = 0, off_tiles = 0, off_bc = 0, off_craw = 0,
-           off_agg = 0, off_incl = 0, total = 0;
+    size_t off_header = 0, off_flags = 0, off_tiles = 0, off_agg = 0, off_incl = 0, total = 0;
 };
 ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L);
 
