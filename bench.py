@@ -353,8 +353,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU takes tens of milliseconds of work to reach its steady clocks:
+    # fewer warm-up steps time a partly clocked-down GPU
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="block",
                     choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")

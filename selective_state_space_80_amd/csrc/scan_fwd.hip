@@ -412,6 +412,19 @@ __device__ __forceinline__ void stage_bc(const ScanKArgs &p, float (*s_bc)[kSegT
     }
 }
 
+// One LDS row of kMaxN floats into registers (four 128-bit broadcast reads).
+__device__ __forceinline__ void lds_row(const float *row, float (&v)[kMaxN])
+{
+#pragma unroll
+    for (int q = 0; q < kMaxN / 4; ++q) {
+        const float4 t = reinterpret_cast<const float4 *>(row)[q];
+        v[4 * q + 0] = t.x;
+        v[4 * q + 1] = t.y;
+        v[4 * q + 2] = t.z;
+        v[4 * q + 3] = t.w;
+    }
+}
+
 // Input coefficient of the exact ZOH step for one state, B̄_n / B_n =
 // (exp(ΔA_n) - 1) / A_n = Δ φ1(ΔA_n) with φ1(v) = (e^v - 1)/v, given
 // en = exp(ΔA_n).  For |ΔA_n| < 1/2, φ1 by its Taylor series through v^7
@@ -537,6 +550,12 @@ __device__ __forceinline__ void scan_segment(
         for (int n = 0; n < kMaxN; ++n)
             hs[n] = 0.f;
         float E = 1.f, cumL = 0.f;
+        // structured path: the step's B row is read from LDS one step ahead,
+        // into the registers the previous row has just freed, so its latency
+        // hides behind the previous step's readout
+        float Bc[kMaxN];
+        if constexpr (STRUCT)
+            lds_row(s_bc[0][w * kChunkT], Bc);
 #pragma unroll
         for (int j = 0; j < kChunkT; ++j) {
             if (j < nt) {  // one basic block per step
@@ -547,6 +566,8 @@ __device__ __forceinline__ void scan_segment(
                 if constexpr (STRUCT) {
                     // ĥ <- ĥ + (e_n - 1)(ĥ + B_n x), with e_n - 1 = e^(n+1) - 1
                     // built as (e_n - 1) = e (e_(n-1) - 1) + (e - 1)
+                    float Cr[kMaxN];
+                    lds_row(Cj, Cr);
                     const float e1 = er[j];
                     const float em0 = e1 - 1.f;  // exact (Sterbenz)
                     float em = em0;
@@ -554,10 +575,14 @@ __device__ __forceinline__ void scan_segment(
                     for (int n = 0; n < kMaxN; ++n) {
                         if (n)
                             em = fmaf(e1, em, em0);
-                        const float sn = fmaf(Bj[n], xv, hs[n]);
+                        const float sn = fmaf(Bc[n], xv, hs[n]);
                         hs[n] = fmaf(em, sn, hs[n]);
-                        acc = fmaf(Cj[n], hs[n], acc);
                     }
+                    if (j + 1 < kChunkT)
+                        lds_row(s_bc[0][w * kChunkT + j + 1], Bc);
+#pragma unroll
+                    for (int n = 0; n < kMaxN; ++n)
+                        acc = fmaf(Cr[n], hs[n], acc);
                     E *= e1;
                     yl[j] = fmaf(acc, inva0, Dd * xv);
                     er[j] = E;
