@@ -373,7 +373,7 @@ mamba_status mamba_selective_state_update(float *h, const void *x, const void *d
             return MAMBA_ERR_ALIAS;
     if (overlap(ry, rh))
         return MAMBA_ERR_ALIAS;
-    if ((D + 255) / 256 * B >= (int64_t(1) << 31))
+    if ((n * 4 + 255) / 256 >= (int64_t(1) << 31))  // launch grid (four lanes per channel)
         return MAMBA_ERR_SHAPE;
     mamba_status st = device_ok();
     if (st != MAMBA_OK)

@@ -20,7 +20,7 @@
 //     "Mamba: Linear-Time Sequence Modeling with Selective SSMs", selective scan
 //     section).  Chunk maps are combined in LDS inside the workgroup.  Across
 //     workgroups every segment publishes its map (an aggregate record) in the
-//     workspace; segments are grouped 16 to a superblock, and the last segment
+//     workspace; segments are grouped 8 to a superblock, and the last segment
 //     of a superblock also publishes the state at its end (an inclusive
 //     record).  A segment's start state is the previous superblock's inclusive
 //     state with the aggregates of the earlier segments of its own superblock
@@ -70,7 +70,7 @@ constexpr uint32_t kPathGeneral = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
 constexpr int kSpinLimit = 1 << 22;
 #ifndef SCAN_SUPERSEG
-#define SCAN_SUPERSEG 16
+#define SCAN_SUPERSEG 8
 #endif
 constexpr int64_t kSuperSeg = SCAN_SUPERSEG;  // segments per superblock of the carry
 #ifdef SCAN_TRACE
@@ -112,10 +112,15 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(const float *__restrict_
     const int64_t d = c;
     bool ok = true;
     if (d < D) {
-        const float a0 = A[d * N];
-        ok = (a0 < -1e-30f) && (a0 > -1e30f);
-        for (int n = 1; n < N; ++n)
-            ok = ok && (A[d * N + n] == (float)(n + 1) * a0);
+        // all loads first (no short-circuit), then the comparisons
+        float a[kMaxN];
+#pragma unroll
+        for (int n = 0; n < kMaxN; ++n)
+            a[n] = (n < N) ? A[d * N + n] : 0.f;
+        ok = (a[0] < -1e-30f) && (a[0] > -1e30f);
+#pragma unroll
+        for (int n = 1; n < kMaxN; ++n)
+            ok = ok & ((n >= N) | (a[n] == (float)(n + 1) * a[0]));
     }
     const uint64_t bad = __ballot(!ok);
     if ((threadIdx.x & (kWave - 1)) == 0)
@@ -423,25 +428,6 @@ __device__ __forceinline__ void lds_row(const float *row, float (&v)[kMaxN])
         v[4 * q + 2] = t.z;
         v[4 * q + 3] = t.w;
     }
-}
-
-// Input coefficient of the exact ZOH step for one state, B̄_n / B_n =
-// (exp(ΔA_n) - 1) / A_n = Δ φ1(ΔA_n) with φ1(v) = (e^v - 1)/v, given
-// en = exp(ΔA_n).  For |ΔA_n| < 1/2, φ1 by its Taylor series through v^7
-// (truncation below 1.1e-8 relative; A_n = 0 gives exactly Δ, the limit);
-// otherwise (en - 1)/A_n, where en - 1 has no cancellation (|en - 1| > 0.39).
-__device__ __forceinline__ float zoh_input_coef(float an, float delta, float en)
-{
-    const float v = an * delta;
-    float phi = 1.f / 40320.f;  // 1/8!
-    phi = fmaf(phi, v, 1.f / 5040.f);
-    phi = fmaf(phi, v, 1.f / 720.f);
-    phi = fmaf(phi, v, 1.f / 120.f);
-    phi = fmaf(phi, v, 1.f / 24.f);
-    phi = fmaf(phi, v, 1.f / 6.f);
-    phi = fmaf(phi, v, 0.5f);
-    phi = fmaf(phi, v, 1.f);
-    return fabsf(v) < 0.5f ? delta * phi : (en - 1.f) * hw_rcp(an);
 }
 
 // Apply the chunk map (f, S) to a state: h_n <- P_n(f) h_n + S_n, where

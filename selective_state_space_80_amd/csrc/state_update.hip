@@ -2,12 +2,14 @@
 // SSM, which keeps a fixed-size state per channel and advances it one token
 // at a time ("Mamba架构深度剖析：如何以线性时间重塑序列建模" §3).  For each
 // (b, d):  Δ = softplus(dt + dt_bias),  h_n <- exp(Δ A_n) h_n + B̄_n x with the
-// zero-order-hold B̄_n = expm1(Δ A_n)/A_n B_n (Δ B_n at A_n = 0)
-// ("Mamba架构与SSM模型：高效序列建模技术解析" §2.1-2.2), then
+// zero-order-hold B̄_n = (exp(Δ A_n) - 1)/A_n B_n (Δ B_n at A_n = 0)
+// ("Mamba架构与SSM模型：高效序列建模技术解析" §2), then
 // y = (sum_n C_n h_n + D x) * SiLU(z).
-// HBM-bound: the fp32 state (N*4 bytes read and written per channel) dominates
-// the traffic, so one lane owns one channel, reads its state row with 128-bit
-// loads when N = 16, and B/C of the batch row are wave-uniform scalar loads.
+// Bound by memory: the fp32 state (N*4 bytes read and written per channel)
+// dominates the traffic.  With N = 16 and aligned rows, four lanes share a
+// channel, one 16-byte quarter of its state each, so every load and store of
+// a wave covers one contiguous 1 KB run; the readout is summed over the four
+// lanes with two cross-lane adds.  Other N: one lane per channel.
 #include "device_common.h"
 #include "internal.h"
 
@@ -18,43 +20,47 @@ namespace {
 constexpr int kThreads = 256;
 
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) state_update_kernel(
+__device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4])
+{
+    if constexpr (BF16) {
+        const uint2 w = reinterpret_cast<const uint2 *>(base)[i4];
+        v[0] = __uint_as_float(w.x << 16);
+        v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16);
+        v[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+        const float4 f = reinterpret_cast<const float4 *>(base)[i4];
+        v[0] = f.x;
+        v[1] = f.y;
+        v[2] = f.z;
+        v[3] = f.w;
+    }
+}
+
+// N = 16, state and A rows 16-byte aligned, B/C rows aligned to 4 elements:
+// thread g handles states [4q, 4q+4) of channel g/4, q = g % 4.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
     const void *__restrict__ Cm_, const float *__restrict__ Dskip, const void *__restrict__ z_,
-    void *__restrict__ y_, int64_t D, int N, int vec16, int64_t blocks_per_row)
+    void *__restrict__ y_, int64_t D, int64_t n_quads)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
-    const int64_t b = (int64_t)blockIdx.x / blocks_per_row;
-    const int64_t d = ((int64_t)blockIdx.x - b * blocks_per_row) * kThreads + threadIdx.x;
-    if (d >= D)
-        return;
-    const int64_t c = b * D + d;
-    float hs[kMaxN], Ar[kMaxN], Bv[kMaxN], Cv[kMaxN];
-    const T *Bm = reinterpret_cast<const T *>(Bm_) + b * N;
-    const T *Cm = reinterpret_cast<const T *>(Cm_) + b * N;
-    if (vec16) {
-        const float4 *hq = reinterpret_cast<const float4 *>(h + c * kMaxN);
-        const float4 *aq = reinterpret_cast<const float4 *>(A + d * kMaxN);
-#pragma unroll
-        for (int i = 0; i < kMaxN / 4; ++i) {
-            const float4 hv = hq[i], av = aq[i];
-            hs[4 * i] = hv.x; hs[4 * i + 1] = hv.y; hs[4 * i + 2] = hv.z; hs[4 * i + 3] = hv.w;
-            Ar[4 * i] = av.x; Ar[4 * i + 1] = av.y; Ar[4 * i + 2] = av.z; Ar[4 * i + 3] = av.w;
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n) {
-            hs[n] = (n < N) ? h[c * N + n] : 0.f;
-            Ar[n] = (n < N) ? A[d * N + n] : 0.f;
-        }
-    }
-#pragma unroll
-    for (int n = 0; n < kMaxN; ++n) {
-        Bv[n] = (n < N) ? E::load(Bm + n) : 0.f;
-        Cv[n] = (n < N) ? E::load(Cm + n) : 0.f;
-    }
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // whole channels per wave (64 lanes = 16 channels), so a lane past the
+    // end only ever shares its shuffles with lanes past the end too
+    const bool live = g < n_quads;
+    const int64_t gc = live ? g : n_quads - 1;
+    const int64_t c = gc >> 2;  // channel b*D + d
+    const int q = (int)(gc & 3);
+    const int64_t b = c / D, d = c - b * D;
+    float hs[4], a[4], Bv[4], Cv[4];
+    load4<false>(h, gc, hs);
+    load4<false>(A, d * 4 + q, a);
+    load4<BF16>(Bm_, b * 4 + q, Bv);
+    load4<BF16>(Cm_, b * 4 + q, Cv);
     const float xv = E::load(reinterpret_cast<const T *>(x_) + c);
     const float dtv = E::load(reinterpret_cast<const T *>(dt_) + c);
     const float bias = dt_bias ? dt_bias[d] : 0.f;
@@ -62,45 +68,93 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     const float delta = l * kLn2;
     float acc = 0.f;
 #pragma unroll
-    for (int n = 0; n < kMaxN; ++n) {
-        const float an = Ar[n];
-        const float en = (an == 0.f) ? 1.f : hw_exp2(an * l);
-        const float coef = (an == 0.f) ? delta : expm1f(an * delta) / an;
-        hs[n] = fmaf(en, hs[n], coef * (Bv[n] * xv));
-        acc = fmaf(Cv[n], hs[n], acc);
+    for (int i = 0; i < 4; ++i) {
+        const float en = hw_exp2(a[i] * l);  // exp(Δ A_n); 1 when A_n = 0
+        const float coef = zoh_input_coef(a[i], delta, en);
+        hs[i] = fmaf(en, hs[i], coef * (Bv[i] * xv));
+        acc = fmaf(Cv[i], hs[i], acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (!live)
+        return;
+    if (q == 0) {
+        float yv = acc + (Dskip ? Dskip[d] : 0.f) * xv;
+        if (z_)
+            yv *= silu_hw(E::load(reinterpret_cast<const T *>(z_) + c));
+        E::store(reinterpret_cast<T *>(y_) + c, yv);
+    }
+    reinterpret_cast<float4 *>(h)[g] = make_float4(hs[0], hs[1], hs[2], hs[3]);
+}
+
+// Any N <= 16: one lane per channel.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) state_update_kernel(
+    float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
+    const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
+    const void *__restrict__ Cm_, const float *__restrict__ Dskip, const void *__restrict__ z_,
+    void *__restrict__ y_, int64_t D, int N, int64_t n_ch)
+{
+    using E = Elem<BF16>;
+    using T = typename E::T;
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= n_ch)
+        return;
+    const int64_t b = c / D, d = c - b * D;
+    const T *Bm = reinterpret_cast<const T *>(Bm_) + b * N;
+    const T *Cm = reinterpret_cast<const T *>(Cm_) + b * N;
+    const float xv = E::load(reinterpret_cast<const T *>(x_) + c);
+    const float dtv = E::load(reinterpret_cast<const T *>(dt_) + c);
+    const float bias = dt_bias ? dt_bias[d] : 0.f;
+    const float l = softplus_log2(fmaf(dtv, kLog2e, bias * kLog2e));  // Δ / ln 2
+    const float delta = l * kLn2;
+    float acc = 0.f;
+    for (int n = 0; n < N; ++n) {
+        const float an = A[d * N + n];
+        const float en = hw_exp2(an * l);
+        const float coef = zoh_input_coef(an, delta, en);
+        const float hn = fmaf(en, h[c * N + n], coef * (E::load(Bm + n) * xv));
+        h[c * N + n] = hn;
+        acc = fmaf(E::load(Cm + n), hn, acc);
     }
     float yv = acc + (Dskip ? Dskip[d] : 0.f) * xv;
     if (z_)
         yv *= silu_hw(E::load(reinterpret_cast<const T *>(z_) + c));
     E::store(reinterpret_cast<T *>(y_) + c, yv);
-    if (vec16) {
-        float4 *hq = reinterpret_cast<float4 *>(h + c * kMaxN);
-#pragma unroll
-        for (int i = 0; i < kMaxN / 4; ++i)
-            hq[i] = make_float4(hs[4 * i], hs[4 * i + 1], hs[4 * i + 2], hs[4 * i + 3]);
-    } else {
-#pragma unroll
-        for (int n = 0; n < kMaxN; ++n)
-            if (n < N)
-                h[c * N + n] = hs[n];
-    }
 }
 
 }  // namespace
 
 hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
 {
-    if (a.B * a.D == 0)
+    const int64_t n_ch = a.B * a.D;
+    if (n_ch == 0)
         return hipSuccess;
-    const int vec16 = (a.N == kMaxN && ((uintptr_t)a.h % 16) == 0 && ((uintptr_t)a.A % 16) == 0);
-    const int64_t bpr = (a.D + kThreads - 1) / kThreads;
-    dim3 grid((unsigned)(bpr * a.B));
-    if (a.bf16)
-        hipLaunchKernelGGL(state_update_kernel<true>, grid, dim3(kThreads), 0, s, a.h, a.x, a.dt,
-                           a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N, vec16, bpr);
-    else
-        hipLaunchKernelGGL(state_update_kernel<false>, grid, dim3(kThreads), 0, s, a.h, a.x,
-                           a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N, vec16, bpr);
+    const size_t bc_align = a.bf16 ? 8 : 16;
+    const bool quad = a.N == kMaxN && ((uintptr_t)a.h % 16) == 0 && ((uintptr_t)a.A % 16) == 0 &&
+                      ((uintptr_t)a.Bm % bc_align) == 0 && ((uintptr_t)a.Cm % bc_align) == 0;
+    if (quad) {
+        const int64_t n_quads = n_ch * 4;
+        const dim3 grid((unsigned)((n_quads + kThreads - 1) / kThreads));
+        if (a.bf16)
+            hipLaunchKernelGGL(state_update_quad_kernel<true>, grid, dim3(kThreads), 0, s, a.h,
+                               a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D,
+                               n_quads);
+        else
+            hipLaunchKernelGGL(state_update_quad_kernel<false>, grid, dim3(kThreads), 0, s, a.h,
+                               a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D,
+                               n_quads);
+    } else {
+        const dim3 grid((unsigned)((n_ch + kThreads - 1) / kThreads));
+        if (a.bf16)
+            hipLaunchKernelGGL(state_update_kernel<true>, grid, dim3(kThreads), 0, s, a.h, a.x,
+                               a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
+                               n_ch);
+        else
+            hipLaunchKernelGGL(state_update_kernel<false>, grid, dim3(kThreads), 0, s, a.h, a.x,
+                               a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
+                               n_ch);
+    }
     return hipGetLastError();
 }
 
