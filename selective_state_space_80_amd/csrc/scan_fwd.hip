@@ -60,11 +60,11 @@ namespace {
 struct WsHeader {
     uint32_t ticket;
     uint32_t error;
-    uint32_t pad[62];
+    uint32_t epoch;  // call counter (never 0): tag of this call's inclusive records
+    uint32_t pad[61];
 };
 
 constexpr uint32_t kFlagAgg = 1u;
-constexpr uint32_t kFlagIncl = 2u;
 constexpr uint32_t kPathStructured = 0u;
 constexpr uint32_t kPathGeneral = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
@@ -102,6 +102,8 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(const float *__restrict_
             WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + lay.off_header);
             hdr->ticket = 0u;
             hdr->error = 0u;
+            const uint32_t e = hdr->epoch + 1u;
+            hdr->epoch = e ? e : 1u;
         }
         reinterpret_cast<uint32_t *>(ws + lay.off_flags)[i] = 0u;
         return;
@@ -239,10 +241,10 @@ __device__ __forceinline__ void store_chunk(void *base, int64_t off, int nt, boo
 
 // Carry records between workgroups.  Every record word and every flag is
 // accessed with agent-scope relaxed atomics, which are coherent across the
-// XCDs' L2 caches without whole-cache write-back or invalidation.  A writer
-// waits until all of its record stores have completed (vmcnt = 0) before it
-// stores the flag; a reader loads record words only after it has seen the
-// flag, so it reads this call's values.
+// XCDs' L2 caches without whole-cache write-back or invalidation.  A writer of
+// a segment aggregate waits until all of its record stores have completed
+// (vmcnt = 0) before it stores the flag; a reader loads record words only
+// after it has seen the flag, so it reads this call's values.
 __device__ __forceinline__ uint32_t load_flag(const uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -256,6 +258,25 @@ __device__ __forceinline__ float load_rec(const float *p)
 __device__ __forceinline__ void store_rec(float *p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Inclusive records (the superblock-to-superblock chain, on the critical path
+// of long sequences) instead carry the call's epoch in the high half of every
+// 64-bit word, beside the value: a reader accepts a word once its tag is this
+// call's, so the record needs no flag, its writer no wait for its stores, and
+// its reader one round trip.  Each 64-bit word is written and read
+// atomically.  Stale words of earlier calls carry older epochs (the epoch
+// skips 0 and would only repeat after 2^32 calls on one workspace); a fresh
+// workspace would need all 16 of a lane's words to hold this epoch by chance.
+__device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t epoch)
+{
+    const uint64_t w = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void publish_flag(uint32_t *p, uint32_t v, int lane)
@@ -467,7 +488,8 @@ __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 // The whole per-workgroup body for one arithmetic path.
 template <bool BF16, bool STRUCT, bool CONV>
 __device__ __forceinline__ void scan_segment(
-    const ScanKArgs &p, uint32_t *__restrict__ flags, float *__restrict__ agg, float *__restrict__ incl,
+    const ScanKArgs &p, uint32_t *__restrict__ flags, float *__restrict__ agg,
+    uint64_t *__restrict__ incl, uint32_t epoch,
     WsHeader *hdr, int64_t seg, int64_t g, int w, int lane, float (*s_agg)[kAggFields][kWave],
     float (*s_part)[kAggFields][kWave], float (*s_bc)[kSegT][kMaxN], float (*s_A)[kWave])
 {
@@ -709,17 +731,31 @@ __device__ __forceinline__ void scan_segment(
         // ---- 5. segment start state and inclusive record ---------------------
         if (w == 0) {
             float hin[kMaxN];
-            if (sI >= 0)
-                wait_flags(flags + sI * G + g, lane == 0 ? kFlagIncl : 0u, hdr, lane);
             if (sI < 0) {
 #pragma unroll
                 for (int n = 0; n < kMaxN; ++n)
                     hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
             } else {
-                const float *rec = incl + (sI * G + g) * (kInclFields * kWave);
+                // the previous superblock's end state: poll its tagged record
+                const uint64_t *rec =
+                    incl + ((sI / kSuperSeg) * G + g) * (kInclFields * kWave) + lane;
+                for (int spins = 0;; ++spins) {
+                    bool ok = true;
 #pragma unroll
-                for (int n = 0; n < kMaxN; ++n)
-                    hin[n] = load_rec(rec + n * kWave + lane);
+                    for (int n = 0; n < kMaxN; ++n) {
+                        const uint64_t wd = load_tagged(rec + n * kWave);
+                        hin[n] = __uint_as_float((uint32_t)wd);
+                        ok = ok & ((uint32_t)(wd >> 32) == epoch);
+                    }
+                    if (__ballot(!ok) == 0ull)
+                        break;
+                    if (spins >= kSpinLimit) {  // never expected
+                        if (lane == 0)
+                            atomicOr(&hdr->error, kErrSpinTimeout);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
             }
             // wave 0's own partial is still in registers; then waves 1..3
             apply_map<STRUCT>(pf, [&](int n) { return ps[n]; }, Ar, hin);
@@ -739,11 +775,11 @@ __device__ __forceinline__ void scan_segment(
                 apply_map<STRUCT>(s_part[0][0][lane],
                                   [&](int n) { return s_part[0][1 + n][lane]; }, Ar, hin);
                 if (publish) {
-                    float *rec = incl + item * (kInclFields * kWave);
+                    uint64_t *rec =
+                        incl + ((seg / kSuperSeg) * G + g) * (kInclFields * kWave) + lane;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n)
-                        store_rec(rec + n * kWave + lane, hin[n]);
-                    publish_flag(flags + item, kFlagIncl, lane);
+                        store_tagged(rec + n * kWave, hin[n], epoch);
                 } else if (active) {
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n)
@@ -838,7 +874,8 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan
     WsHeader *hdr = reinterpret_cast<WsHeader *>(p.ws + p.lay.off_header);
     uint32_t *flags = reinterpret_cast<uint32_t *>(p.ws + p.lay.off_flags);
     float *agg = reinterpret_cast<float *>(p.ws + p.lay.off_agg);
-    float *incl = reinterpret_cast<float *>(p.ws + p.lay.off_incl);
+    uint64_t *incl = reinterpret_cast<uint64_t *>(p.ws + p.lay.off_incl);
+    const uint32_t epoch = __builtin_amdgcn_readfirstlane(hdr->epoch);
 
     if (threadIdx.x == 0)
         s_ticket = atomicAdd(&hdr->ticket, 1u);
@@ -851,10 +888,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan
     const int64_t dtile = g % p.lay.n_dtiles;
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
-        scan_segment<BF16, true, CONV>(p, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, true, CONV>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
                                        s_part, s_bc, s_A);
     else
-        scan_segment<BF16, false, CONV>(p, flags, agg, incl, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, false, CONV>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
                                         s_part, s_bc, s_A);
 }
 
@@ -908,8 +945,10 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L)
     off = round_up(off + (size_t)l.n_dtiles * 4, 256);
     l.off_agg = off;
     off = round_up(off + (size_t)l.n_items * kAggFields * kWave * 4, 256);
-    l.off_incl = off;
-    off = round_up(off + (size_t)l.n_items * kInclFields * kWave * 4, 256);
+    l.off_incl = off;  // one tagged record per superblock and group
+    off = round_up(off + (size_t)(((l.n_seg + kSuperSeg - 1) / kSuperSeg) * l.groups) *
+                             kInclFields * kWave * 8,
+                   256);
 #ifdef SCAN_TRACE
     off = round_up(off + (size_t)l.n_items * 256, 256);
 #endif
