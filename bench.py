@@ -263,7 +263,9 @@ def run_block(args, torch, mamba, W):
     return out
 
 
-def run_scan(args, torch, mamba, W, idx):
+def run_scan(args, torch, mamba, W, idx, bidir=False):
+    """One workload's scan; bidir: the forward scan, then the reverse scan of
+    a second parameter set added into the same y (a bidirectional layer)."""
     wl = W.WORKLOADS[idx]
     B, D, L, N = wl.B, wl.D, wl.L, wl.N
     p = W.scan_inputs(wl)
@@ -277,15 +279,28 @@ def run_scan(args, torch, mamba, W, idx):
     y = torch.empty_like(x)
     ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
                      device=dev)
-    for _ in range(args.warmup):
+    if bidir:
+        q = W.make_scan_inputs(B, D, L, N, wl.io, wl.seed + 500)
+        dt2, Bm2, Cm2 = T(q["dt"], io_t), T(q["Bm"], io_t), T(q["Cm"], io_t)
+        A2, bias2, Dk2 = T(q["A"]), T(q["dt_bias"]), T(q["Dskip"])
+
+    def step(i=None, pair=None):
+        if pair is not None:
+            mamba.set_scan_timing_events_raw(pair[0], pair[1])
         mamba.selective_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+        if bidir:
+            mamba.set_scan_timing_events_raw(None, None)
+            mamba.selective_scan_fwd(x, dt2, A2, Bm2, Cm2, bias2, Dk2, z, out=y, workspace=ws,
+                                     reverse=True, accumulate=True)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        mamba.set_scan_timing_events_raw(pairs[i][0], pairs[i][1])
-        mamba.selective_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+        step(i, pairs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     mamba.set_scan_timing_events_raw(None, None)
@@ -296,12 +311,16 @@ def run_scan(args, torch, mamba, W, idx):
     sb = scan_bytes(B, D, L, N, 2 if bf else 4)
     achieved = sb / (scan_ms * 1e-3) / 1e9
     return {"metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
-            "value": round(elems / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
+            "value": round(elems * (2 if bidir else 1) / (ms_step * 1e-3) / 1e9, 3),
+            "unit": "Gelem/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16-io/f32", "data": "synthetic",
-            "config": {"workload": wl.name, "batch": B, "d_inner": D, "seq_len": L,
-                       "d_state": N, "io": wl.io},
+            "config": {"workload": wl.name + ("_bidirectional" if bidir else ""), "batch": B,
+                       "d_inner": D, "seq_len": L, "d_state": N, "io": wl.io,
+                       "step": ("forward scan, then reverse scan added into y" if bidir else
+                                "forward scan"),
+                       "elements_per_step": elems * (2 if bidir else 1)},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": None, "kernel_ms": round(scan_ms, 4)},
@@ -358,7 +377,8 @@ def main():
     # fewer warm-up steps time a partly clocked-down GPU
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="block",
-                    choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode"])
+                    choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode",
+                             "bidir_bf16_l2048"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--unfused", action="store_true",
                     help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
@@ -393,6 +413,8 @@ def main():
         out = run_scan(args, torch, mamba, W, 2)
     elif args.workload == "scan_bf16_l131072":
         out = run_scan(args, torch, mamba, W, 3)
+    elif args.workload == "bidir_bf16_l2048":
+        out = run_scan(args, torch, mamba, W, 2, bidir=True)
     else:
         out = run_decode(args, torch, mamba, W)
     print(json.dumps(out), flush=True)

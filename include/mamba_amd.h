@@ -5,6 +5,7 @@
  *   mamba_conv1d_silu            causal depthwise conv1d + SiLU front end
  *   mamba_selective_scan_fwd     fused selective-scan forward (prefill)
  *   mamba_selective_state_update single-token recurrent step (decode)
+ * the scan with direction / accumulate flags (mamba_selective_scan_fwd_ex),
  * and two that join the front end to the scan:
  *   mamba_conv1d_selective_scan_fwd  conv1d + SiLU fused into the scan
  *   mamba_conv1d_update              single-token conv step with its state
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 2
+#define MAMBA_AMD_ABI_VERSION 3
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
@@ -138,6 +139,34 @@ mamba_status mamba_selective_state_update(float *h, const void *x, const void *d
                                           const void *Bm, const void *Cm, const float *Dskip,
                                           const void *z, void *y, int64_t B, int64_t D,
                                           int64_t N, mamba_dtype io, void *stream);
+
+/* Flags of mamba_selective_scan_fwd_ex. */
+#define MAMBA_SCAN_REVERSE 1u    /* scan from step L-1 down to step 0 */
+#define MAMBA_SCAN_ACCUMULATE 2u /* add the gated output to y instead of storing it */
+
+/*
+ * mamba_selective_scan_fwd with flags, for the scan directions of a
+ * bidirectional layer ("Mamba架构与SSM模型：高效序列建模技术解析", §2: sequences
+ * modelled in both directions by alternating the scan direction; §3: the
+ * module's bidirectional option).
+ *   MAMBA_SCAN_REVERSE     the same recurrence in reversed time: the state runs
+ *                          from step L-1 down to step 0, so y_t sees steps
+ *                          t..L-1.  h0 is the state before step L-1, h_last the
+ *                          state after step 0.  Equal to the forward scan of the
+ *                          time-reversed x, dt, z, Bm, Cm, reversed back.
+ *   MAMBA_SCAN_ACCUMULATE  y[...] += out instead of y[...] = out (bf16: the sum
+ *                          is formed in fp32 from the stored value and rounded
+ *                          once), so a forward call followed by a reverse call
+ *                          with this flag leaves (y_fwd + y_rev) in y.
+ * Unknown flags return MAMBA_ERR_UNSUPPORTED.  Every other argument and rule
+ * is as for mamba_selective_scan_fwd (flags = 0 is that call).
+ */
+mamba_status mamba_selective_scan_fwd_ex(const void *x, const void *dt, const float *dt_bias,
+                                         const float *A, const void *Bm, const void *Cm,
+                                         const float *Dskip, const void *z, const float *h0,
+                                         void *y, float *h_last, void *workspace,
+                                         size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
+                                         int64_t N, mamba_dtype io, unsigned flags, void *stream);
 
 /*
  * The block's front end and the scan in one pass: the scan input is

@@ -109,6 +109,17 @@ class Oracle:
             raise ValueError("oracle_selective_scan_fwd rejected its arguments")
         return y, h_last
 
+    def selective_scan_reverse(self, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+                               nthreads: int = 1):
+        """The scan in reversed time (state from step L-1 down to step 0): by
+        definition the forward scan of the time-reversed sequences, reversed
+        back ("Mamba架构与SSM模型：高效序列建模技术解析" §2, both directions)."""
+        flip = lambda a: None if a is None else np.ascontiguousarray(np.flip(np.asarray(a), -1))
+        flip_bc = lambda a: np.ascontiguousarray(np.flip(np.asarray(a), -2))
+        y, h = self.selective_scan(flip(x), flip(dt), A, flip_bc(Bm), flip_bc(Cm), dt_bias, Dskip,
+                                   flip(z), h0, nthreads)
+        return flip(y), h
+
     def conv1d_silu(self, x, w, bias=None, apply_silu: bool = True):
         """Causal depthwise conv1d (+ SiLU).  x [B,D,L], w [D,K] -> [B,D,L]."""
         x, w, bias = _f64(x), _f64(w), _f64(bias)
@@ -184,6 +195,10 @@ def selective_scan(*args, **kw):
 
 def conv1d_silu(*args, **kw):
     return get().conv1d_silu(*args, **kw)
+
+
+def selective_scan_reverse(*args, **kw):
+    return get().selective_scan_reverse(*args, **kw)
 
 
 def state_update(*args, **kw):

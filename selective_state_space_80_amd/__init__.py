@@ -26,6 +26,8 @@ LIBRARY = os.path.join(HERE, "libmamba_amd.so")
 
 MAMBA_F32 = 0
 MAMBA_BF16 = 1
+MAMBA_SCAN_REVERSE = 1
+MAMBA_SCAN_ACCUMULATE = 2
 
 STATUS_NAMES = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ERR_DTYPE",
                 4: "MAMBA_ERR_UNSUPPORTED", 5: "MAMBA_ERR_ALIGN", 6: "MAMBA_ERR_ALIAS",
@@ -34,7 +36,8 @@ STATUS_NAMES = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MA
 # every symbol include/mamba_amd.h declares
 EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_selective_scan_fwd_workspace_size", "mamba_selective_scan_fwd",
-            "mamba_selective_state_update", "mamba_conv1d_selective_scan_fwd",
+            "mamba_selective_state_update", "mamba_selective_scan_fwd_ex",
+            "mamba_conv1d_selective_scan_fwd",
             "mamba_conv1d_update", "mamba_set_scan_timing_events"]
 
 _lib = None
@@ -68,6 +71,9 @@ def load_library(path: str = LIBRARY):
     lib.mamba_selective_scan_fwd.argtypes = [P] * 12 + [SZ, I64, I64, I64, I64, I32, P]
     lib.mamba_selective_state_update.restype = I32
     lib.mamba_selective_state_update.argtypes = [P] * 10 + [I64, I64, I64, I32, P]
+    lib.mamba_selective_scan_fwd_ex.restype = I32
+    lib.mamba_selective_scan_fwd_ex.argtypes = ([P] * 12 + [SZ, I64, I64, I64, I64, I32,
+                                                             ctypes.c_uint, P])
     lib.mamba_conv1d_selective_scan_fwd.restype = I32
     lib.mamba_conv1d_selective_scan_fwd.argtypes = ([P, P, P, I64] + [P] * 13 +
                                                     [SZ, I64, I64, I64, I64, I32, P])
@@ -153,10 +159,12 @@ def selective_scan_fwd_workspace_size(B, D, L, N, dtype=None) -> int:
 
 
 def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
-                       return_last_state=False, out=None, workspace=None, h_last=None):
+                       return_last_state=False, out=None, workspace=None, h_last=None,
+                       reverse=False, accumulate=False):
     """Fused selective-scan forward.  x, dt, z [B,D,L]; Bm, Cm [B,L,N] (all of
     one dtype, f32 or bf16); A [D,N], dt_bias [D], Dskip [D], h0 [B,D,N] f32.
-    Returns y [B,D,L] (x's dtype), and h_last [B,D,N] f32 if return_last_state."""
+    Returns y [B,D,L] (x's dtype), and h_last [B,D,N] f32 if return_last_state.
+    reverse: scan from step L-1 down to 0; accumulate: add into `out`."""
     torch = _torch()
     lib = load_library()
     B, D, L = x.shape
@@ -172,6 +180,8 @@ def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=No
     _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
     _check(h0, "h0", (B, D, N), torch.float32, dev, optional=True)
     if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs `out` (the tensor added to)")
         out = torch.empty_like(x)
     _check(out, "out", (B, D, L), io_t, dev)
     if return_last_state and h_last is None:
@@ -181,11 +191,19 @@ def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=No
     need = int(lib.mamba_selective_scan_fwd_workspace_size(B, D, L, N, io))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib.mamba_selective_scan_fwd(
-        _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
-        _ptr(h0), _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N, io,
-        _stream(dev))
-    _raise(st, "mamba_selective_scan_fwd")
+    flags = (MAMBA_SCAN_REVERSE if reverse else 0) | (MAMBA_SCAN_ACCUMULATE if accumulate else 0)
+    if flags:
+        st = lib.mamba_selective_scan_fwd_ex(
+            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+            _ptr(h0), _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N, io,
+            flags, _stream(dev))
+        _raise(st, "mamba_selective_scan_fwd_ex")
+    else:
+        st = lib.mamba_selective_scan_fwd(
+            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+            _ptr(h0), _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N,
+            io, _stream(dev))
+        _raise(st, "mamba_selective_scan_fwd")
     if return_last_state:
         return out, h_last
     return out

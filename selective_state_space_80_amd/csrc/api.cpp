@@ -160,7 +160,7 @@ mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
                         const void *Cm, const float *Dskip, const void *z, const float *h0,
                         void *y, float *h_last, void *workspace, size_t workspace_bytes,
                         int64_t B, int64_t D, int64_t L, int64_t N, mamba_dtype io,
-                        void *stream)
+                        unsigned flags, void *stream)
 {
     if (!valid_dtype(io))
         return MAMBA_ERR_DTYPE;
@@ -169,6 +169,9 @@ mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
     if (N < 1 || N > kMaxN)
         return MAMBA_ERR_UNSUPPORTED;
     const bool conv = conv_K != 0;
+    if ((flags & ~(unsigned)(MAMBA_SCAN_REVERSE | MAMBA_SCAN_ACCUMULATE)) != 0 ||
+        (conv && (flags & MAMBA_SCAN_REVERSE)))
+        return MAMBA_ERR_UNSUPPORTED;
     if (conv && conv_K > mamba::kFusedConvTaps)
         return MAMBA_ERR_UNSUPPORTED;
     if (B * D == 0)
@@ -266,6 +269,8 @@ mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
     a.conv_b = conv_b;
     a.conv_state_in = conv_state_in;
     a.conv_state_out = conv_state_out;
+    a.reverse = (flags & MAMBA_SCAN_REVERSE) != 0;
+    a.accumulate = (flags & MAMBA_SCAN_ACCUMULATE) != 0;
     a.ev_start = g_ev_start;
     a.ev_stop = g_ev_stop;
     return launched(mamba::launch_selective_scan(a, (hipStream_t)stream));
@@ -283,7 +288,19 @@ mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float
                                       int64_t N, mamba_dtype io, void *stream)
 {
     return scan_entry(x, 0, nullptr, nullptr, nullptr, nullptr, dt, dt_bias, A, Bm, Cm, Dskip,
-                      z, h0, y, h_last, workspace, workspace_bytes, B, D, L, N, io, stream);
+                      z, h0, y, h_last, workspace, workspace_bytes, B, D, L, N, io, 0u, stream);
+}
+
+mamba_status mamba_selective_scan_fwd_ex(const void *x, const void *dt, const float *dt_bias,
+                                         const float *A, const void *Bm, const void *Cm,
+                                         const float *Dskip, const void *z, const float *h0,
+                                         void *y, float *h_last, void *workspace,
+                                         size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
+                                         int64_t N, mamba_dtype io, unsigned flags, void *stream)
+{
+    return scan_entry(x, 0, nullptr, nullptr, nullptr, nullptr, dt, dt_bias, A, Bm, Cm, Dskip,
+                      z, h0, y, h_last, workspace, workspace_bytes, B, D, L, N, io, flags,
+                      stream);
 }
 
 mamba_status mamba_conv1d_selective_scan_fwd(
@@ -299,7 +316,7 @@ mamba_status mamba_conv1d_selective_scan_fwd(
         return valid_dtype(io) ? MAMBA_ERR_UNSUPPORTED : MAMBA_ERR_DTYPE;
     return scan_entry(x_raw, K, conv_w, conv_bias, conv_state_in, conv_state_out, dt, dt_bias, A,
                       Bm, Cm, Dskip, z, h0, y, h_last, workspace, workspace_bytes, B, D, L, N, io,
-                      stream);
+                      0u, stream);
 }
 
 mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, const float *bias,

@@ -49,6 +49,8 @@ struct ScanArgs {
     const float *conv_w, *conv_b;
     const void *conv_state_in;
     void *conv_state_out;
+    bool reverse;     // scan from step L-1 down to step 0 (plain scan only)
+    bool accumulate;  // y += result
     hipEvent_t ev_start, ev_stop;  // optional timing of the main kernel
 };
 hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s);

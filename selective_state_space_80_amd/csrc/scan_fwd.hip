@@ -146,7 +146,9 @@ template <bool BF16> struct InChunk;
 
 template <> struct InChunk<true> {
     uint32_t w[kChunkT / 2];  // step 2i in the low half, 2i+1 in the high half
-    __device__ __forceinline__ void load(const void *base, int64_t off, int nt, bool vec, float pad)
+    // slots [klo, khi) come from base + off + slot, the others are `pad`
+    __device__ __forceinline__ void load(const void *base, int64_t off, int klo, int khi, bool vec,
+                                         float pad)
     {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + off;
         if (vec) {
@@ -163,8 +165,9 @@ template <> struct InChunk<true> {
             const uint32_t pb = __float_as_uint(pad) >> 16;
 #pragma unroll
             for (int i = 0; i < kChunkT / 2; ++i) {
-                const uint32_t lo = (2 * i < nt) ? (uint32_t)p[2 * i] : pb;
-                const uint32_t hi = (2 * i + 1 < nt) ? (uint32_t)p[2 * i + 1] : pb;
+                const uint32_t lo = (2 * i >= klo && 2 * i < khi) ? (uint32_t)p[2 * i] : pb;
+                const uint32_t hi =
+                    (2 * i + 1 >= klo && 2 * i + 1 < khi) ? (uint32_t)p[2 * i + 1] : pb;
                 w[i] = lo | (hi << 16);
             }
         }
@@ -178,7 +181,9 @@ template <> struct InChunk<true> {
 
 template <> struct InChunk<false> {
     float v[kChunkT];
-    __device__ __forceinline__ void load(const void *base, int64_t off, int nt, bool vec, float pad)
+    // slots [klo, khi) come from base + off + slot, the others are `pad`
+    __device__ __forceinline__ void load(const void *base, int64_t off, int klo, int khi, bool vec,
+                                         float pad)
     {
         const float *p = reinterpret_cast<const float *>(base) + off;
         if (vec) {
@@ -194,28 +199,36 @@ template <> struct InChunk<false> {
         } else {
 #pragma unroll
             for (int i = 0; i < kChunkT; ++i)
-                v[i] = (i < nt) ? p[i] : pad;
+                v[i] = (i >= klo && i < khi) ? p[i] : pad;
         }
     }
     __device__ __forceinline__ float get(int j) const { return v[j]; }
 };
 
-template <bool BF16>
-__device__ __forceinline__ void store_chunk(void *base, int64_t off, int nt, bool vec,
-                                            const float (&v)[kChunkT])
+// Stores slots [klo, khi) of a chunk, slot k's value being val(k), to
+// base + off + k; with `accumulate` each value is added to what is there.
+template <bool BF16, typename Val>
+__device__ __forceinline__ void store_chunk(void *base, int64_t off, int klo, int khi, bool vec,
+                                            bool accumulate, Val val)
 {
     if constexpr (!BF16) {
         float *p = reinterpret_cast<float *>(base) + off;
         if (vec) {
             float4 *q = reinterpret_cast<float4 *>(p);
 #pragma unroll
-            for (int i = 0; i < kChunkT / 4; ++i)
-                q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+            for (int i = 0; i < kChunkT / 4; ++i) {
+                float4 o = make_float4(val(4 * i), val(4 * i + 1), val(4 * i + 2), val(4 * i + 3));
+                if (accumulate) {
+                    const float4 old = q[i];
+                    o = make_float4(o.x + old.x, o.y + old.y, o.z + old.z, o.w + old.w);
+                }
+                q[i] = o;
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < kChunkT; ++i)
-                if (i < nt)
-                    p[i] = v[i];
+                if (i >= klo && i < khi)
+                    p[i] = accumulate ? p[i] + val(i) : val(i);
         }
     } else {
         uint16_t *p = reinterpret_cast<uint16_t *>(base) + off;
@@ -223,18 +236,33 @@ __device__ __forceinline__ void store_chunk(void *base, int64_t off, int nt, boo
             uint4 *q = reinterpret_cast<uint4 *>(p);
 #pragma unroll
             for (int i = 0; i < kChunkT / 8; ++i) {
+                uint32_t old4[4] = {0u, 0u, 0u, 0u};
+                if (accumulate) {
+                    const uint4 o = q[i];
+                    old4[0] = o.x;
+                    old4[1] = o.y;
+                    old4[2] = o.z;
+                    old4[3] = o.w;
+                }
                 uint32_t w4[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    w4[k] = f32_to_bf16_bits(v[8 * i + 2 * k]) |
-                            (f32_to_bf16_bits(v[8 * i + 2 * k + 1]) << 16);
+                for (int k = 0; k < 4; ++k) {
+                    float lo = val(8 * i + 2 * k), hi = val(8 * i + 2 * k + 1);
+                    if (accumulate) {
+                        lo += __uint_as_float(old4[k] << 16);
+                        hi += __uint_as_float(old4[k] & 0xffff0000u);
+                    }
+                    w4[k] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+                }
                 q[i] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kChunkT; ++i)
-                if (i < nt)
-                    p[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+                if (i >= klo && i < khi) {
+                    const float o = accumulate ? bf16_bits_to_f32(p[i]) + val(i) : val(i);
+                    p[i] = (uint16_t)f32_to_bf16_bits(o);
+                }
         }
     }
 }
@@ -321,6 +349,7 @@ struct ScanKArgs {
     const float *conv_w, *conv_b;
     const void *conv_state_in;  // [B, D, K-1] raw inputs before t = 0, or NULL (zeros)
     int conv_K;
+    int accumulate;  // y += result instead of y = result
 };
 
 // Fused front end: the chunk's scan inputs SiLU(bias + sum_k w_k x_(t-K+1+k))
@@ -374,20 +403,25 @@ __device__ __forceinline__ void conv_chunk(const ScanKArgs &p, const InChunk<BF1
 // path) for its kSegT steps, as fp32 rows of kMaxN: zero past N and past L.
 // Whole segments with N = 16 and aligned rows take two 128-bit loads per
 // thread and matrix (fp32) or one (bf16).
-template <bool BF16, bool STRUCT>
+template <bool BF16, bool STRUCT, bool REV>
 __device__ __forceinline__ void stage_bc(const ScanKArgs &p, float (*s_bc)[kSegT][kMaxN],
                                          int64_t b, int64_t seg, int tid)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
     constexpr int kThreads = kWave * kWavesPerSeg;
-    const int64_t t0s = seg * kSegT;
-    const T *src[2] = {reinterpret_cast<const T *>(p.Bm) + (b * p.L + t0s) * p.N,
-                       reinterpret_cast<const T *>(p.Cm) + (b * p.L + t0s) * p.N};
+    const int64_t t0s = seg * kSegT;  // first step of the segment (in scan order)
+    // a whole segment is one run of kSegT rows in memory; in reverse the run
+    // ends at the segment's first step and its rows come in the opposite order
+    const int64_t run0 = REV ? p.L - t0s - kSegT : t0s;
+    auto lrow = [](int pr) { return REV ? kSegT - 1 - pr : pr; };  // run row -> LDS row
+    const T *Bb = reinterpret_cast<const T *>(p.Bm) + b * p.L * p.N;
+    const T *Cb = reinterpret_cast<const T *>(p.Cm) + b * p.L * p.N;
     auto cscale = [](float c, int n) -> float {
         return STRUCT ? c * hw_rcp((float)(n + 1)) : c;
     };
     if (p.bc_vec && t0s + kSegT <= p.L) {
+        const T *src[2] = {Bb + run0 * p.N, Cb + run0 * p.N};
         if constexpr (!BF16) {
             constexpr int kPer = kSegT * kMaxN / 4 / kThreads;  // float4 per thread and matrix
 #pragma unroll
@@ -395,7 +429,7 @@ __device__ __forceinline__ void stage_bc(const ScanKArgs &p, float (*s_bc)[kSegT
 #pragma unroll
                 for (int i = 0; i < kPer; ++i) {
                     const int q = tid + i * kThreads;
-                    const int row = q >> 2, n4 = (q & 3) * 4;
+                    const int row = lrow(q >> 2), n4 = (q & 3) * 4;
                     float4 v = reinterpret_cast<const float4 *>(src[m])[q];
                     if (m == 1)
                         v = make_float4(cscale(v.x, n4), cscale(v.y, n4 + 1),
@@ -407,7 +441,7 @@ __device__ __forceinline__ void stage_bc(const ScanKArgs &p, float (*s_bc)[kSegT
             static_assert(kSegT * kMaxN / 8 == kThreads, "one 8-value load per thread");
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int row = tid >> 1, n8 = (tid & 1) * 8;
+                const int row = lrow(tid >> 1), n8 = (tid & 1) * 8;
                 const uint4 a = reinterpret_cast<const uint4 *>(src[m])[tid];
                 const uint32_t w4[4] = {a.x, a.y, a.z, a.w};
                 float v[8];
@@ -431,8 +465,10 @@ __device__ __forceinline__ void stage_bc(const ScanKArgs &p, float (*s_bc)[kSegT
             const int m = e / (kSegT * kMaxN);
             const int r = (e / kMaxN) % kSegT, n = e % kMaxN;
             float v = 0.f;
-            if (n < p.N && t0s + r < p.L)
-                v = E::load(src[m] + (int64_t)r * p.N + n);
+            if (n < p.N && t0s + r < p.L) {
+                const int64_t t = REV ? p.L - 1 - (t0s + r) : t0s + r;
+                v = E::load((m ? Cb : Bb) + t * p.N + n);
+            }
             s_bc[m][r][n] = m ? cscale(v, n) : v;
         }
     }
@@ -486,7 +522,7 @@ __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 }
 
 // The whole per-workgroup body for one arithmetic path.
-template <bool BF16, bool STRUCT, bool CONV>
+template <bool BF16, bool STRUCT, bool CONV, bool REV>
 __device__ __forceinline__ void scan_segment(
     const ScanKArgs &p, uint32_t *__restrict__ flags, float *__restrict__ agg,
     uint64_t *__restrict__ incl, uint32_t epoch,
@@ -506,7 +542,13 @@ __device__ __forceinline__ void scan_segment(
     const int nt =
         __builtin_amdgcn_readfirstlane((int)max((int64_t)0, min((int64_t)kChunkT, p.L - t0)));
     const bool vec = p.vec && nt == kChunkT;
-    const int64_t row_off = (b * p.D + dc) * p.L + t0;
+    // The chunk's steps t0 .. t0+nt-1 (in scan order) sit in kChunkT slots of
+    // one run of memory: slot = step - t0 forward; in reverse the run ends at
+    // the chunk's first step, slot = kChunkT-1 - (step - t0).  Slots outside
+    // [klo, khi) lie past the sequence and are never read or written.
+    const int64_t row_off = (b * p.D + dc) * p.L + (REV ? p.L - t0 - kChunkT : t0);
+    const int klo = REV ? kChunkT - nt : 0, khi = REV ? kChunkT : nt;
+    auto slot = [](int j) { return REV ? kChunkT - 1 - j : j; };
     TRACE_POINT(0);
 
     // per-channel constants
@@ -533,8 +575,8 @@ __device__ __forceinline__ void scan_segment(
     float summ;
     {
         InChunk<BF16> xin, din;
-        xin.load(p.x, row_off, nt, vec, 0.f);
-        din.load(p.dt, row_off, nt, vec, -__builtin_huge_valf());
+        xin.load(p.x, row_off, klo, khi, vec, 0.f);
+        din.load(p.dt, row_off, klo, khi, vec, -__builtin_huge_valf());
         float xc[kChunkT];  // scan inputs of the fused front end (CONV only)
         if constexpr (CONV)
             conv_chunk<BF16>(p, xin, b * p.D + dc, dc, t0, row_off, nt, xc);
@@ -542,16 +584,16 @@ __device__ __forceinline__ void scan_segment(
             if constexpr (CONV)
                 return xc[j];
             else
-                return xin.get(j);
+                return xin.get(slot(j));
         };
-        stage_bc<BF16, STRUCT>(p, s_bc, b, seg, w * kWave + lane);
+        stage_bc<BF16, STRUCT, REV>(p, s_bc, b, seg, w * kWave + lane);
         __syncthreads();
         // Step decays of the whole chunk first (independent chains, out of
         // the serial loop): er[j] = exp(Δ_j A_0) (structured) or Δ_j/ln2.
         // Padded steps (dt = -inf) give Δ = 0: decay 1.
 #pragma unroll
         for (int j = 0; j < kChunkT; ++j) {
-            const float l = softplus_log2(fmaf(din.get(j), kLog2e, bias2));  // Δ/ln2
+            const float l = softplus_log2(fmaf(din.get(slot(j)), kLog2e, bias2));  // Δ/ln2
             er[j] = STRUCT ? hw_exp2(a0 * l) : l;
         }
 #pragma unroll
@@ -630,7 +672,7 @@ __device__ __forceinline__ void scan_segment(
     // start state is known, ahead of the fix-up.
     InChunk<BF16> zin;
     if (BF16 && p.z && w != 0)
-        zin.load(p.z, row_off, nt, vec, 0.f);
+        zin.load(p.z, row_off, klo, khi, vec, 0.f);
 
     // ---- 2. combine chunk maps inside the workgroup ------------------------
     s_agg[w][0][lane] = summ;
@@ -680,7 +722,7 @@ __device__ __forceinline__ void scan_segment(
             publish_flag(flags + item, kFlagAgg, lane);
         }
         if (BF16 && p.z)
-            zin.load(p.z, row_off, nt, vec, 0.f);
+            zin.load(p.z, row_off, klo, khi, vec, 0.f);
         if (depth > 0) {
             // wait for the aggregates this segment folds: lane j < depth
             // watches segment seg-1-j (the inclusive state of sI is awaited
@@ -797,7 +839,7 @@ __device__ __forceinline__ void scan_segment(
 
     // ---- 6. this wave's start state, fix-up, gate, store -------------------
     if (!BF16 && p.z)
-        zin.load(p.z, row_off, nt, vec, 0.f);
+        zin.load(p.z, row_off, klo, khi, vec, 0.f);
     float hin[kMaxN];
 #pragma unroll
     for (int n = 0; n < kMaxN; ++n)
@@ -851,15 +893,16 @@ __device__ __forceinline__ void scan_segment(
     if (p.z) {
 #pragma unroll
         for (int j = 0; j < kChunkT; ++j) {
-            yl[j] *= silu_hw(zin.get(j));
+            yl[j] *= silu_hw(zin.get(slot(j)));
         }
     }
     if (active)
-        store_chunk<BF16>(p.y, row_off, nt, vec, yl);
+        store_chunk<BF16>(p.y, row_off, klo, khi, vec, p.accumulate != 0,
+                          [&](int k) { return yl[slot(k)]; });
     TRACE_POINT(6);
 }
 
-template <bool BF16, bool CONV>
+template <bool BF16, bool CONV, bool REV>
 __global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan_main_kernel(
     ScanKArgs p, const uint32_t *__restrict__ tiles)
 {
@@ -888,10 +931,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan
     const int64_t dtile = g % p.lay.n_dtiles;
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
-        scan_segment<BF16, true, CONV>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, true, CONV, REV>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
                                        s_part, s_bc, s_A);
     else
-        scan_segment<BF16, false, CONV>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, false, CONV, REV>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
                                         s_part, s_bc, s_A);
 }
 
@@ -1019,6 +1062,7 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     k.conv_b = a.conv_b;
     k.conv_state_in = a.conv_state_in;
     k.conv_K = a.conv_K;
+    k.accumulate = a.accumulate ? 1 : 0;
     const size_t esz = a.bf16 ? 2 : 4;
     const uintptr_t amask = (uintptr_t)a.x | (uintptr_t)a.dt | (uintptr_t)a.y |
                             (uintptr_t)(a.z ? a.z : a.x);
@@ -1028,17 +1072,24 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, s);
     const dim3 grid((unsigned)lay.n_items), block(kWave * kWavesPerSeg);
+#define MAMBA_SCAN_LAUNCH(BF, CV, RV) \
+    hipLaunchKernelGGL((scan_main_kernel<BF, CV, RV>), grid, block, 0, s, k, tiles)
     if (a.bf16) {
         if (a.conv_K)
-            hipLaunchKernelGGL((scan_main_kernel<true, true>), grid, block, 0, s, k, tiles);
+            MAMBA_SCAN_LAUNCH(true, true, false);
+        else if (a.reverse)
+            MAMBA_SCAN_LAUNCH(true, false, true);
         else
-            hipLaunchKernelGGL((scan_main_kernel<true, false>), grid, block, 0, s, k, tiles);
+            MAMBA_SCAN_LAUNCH(true, false, false);
     } else {
         if (a.conv_K)
-            hipLaunchKernelGGL((scan_main_kernel<false, true>), grid, block, 0, s, k, tiles);
+            MAMBA_SCAN_LAUNCH(false, true, false);
+        else if (a.reverse)
+            MAMBA_SCAN_LAUNCH(false, false, true);
         else
-            hipLaunchKernelGGL((scan_main_kernel<false, false>), grid, block, 0, s, k, tiles);
+            MAMBA_SCAN_LAUNCH(false, false, false);
     }
+#undef MAMBA_SCAN_LAUNCH
     e = hipGetLastError();
     if (a.ev_stop)
         (void)hipEventRecord(a.ev_stop, s);

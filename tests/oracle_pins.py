@@ -361,6 +361,30 @@ def pin_conv_update(orc):
     _close(np.stack(got, axis=2), orc.conv1d_silu(x, w), 1e-14, 1e-15, what="zero window")
 
 
+def pin_reverse(orc):
+    """The reversed-time scan (state runs from step L-1 down to 0) against a
+    direct backward loop over the exact ZOH step, written here in numpy."""
+    rng = np.random.default_rng(29)
+    Bsz, D, L, N = 2, 3, 9, 4
+    x, z = rng.normal(size=(Bsz, D, L)), rng.normal(size=(Bsz, D, L))
+    dt = rng.normal(-1, 0.5, size=(Bsz, D, L))
+    A = -rng.uniform(0.2, 3, size=(D, N))
+    Bm, Cm = rng.normal(size=(Bsz, L, N)), rng.normal(size=(Bsz, L, N))
+    bias, Dv = rng.normal(size=D), rng.normal(size=D)
+    h0 = rng.normal(size=(Bsz, D, N))
+    y, hl = orc.selective_scan_reverse(x, dt, A, Bm, Cm, bias, Dv, z, h0)
+    for b in range(Bsz):
+        for d in range(D):
+            h = h0[b, d].copy()
+            for t in range(L - 1, -1, -1):
+                delta = np.log1p(np.exp(dt[b, d, t] + bias[d]))
+                a = delta * A[d]
+                h = np.exp(a) * h + np.expm1(a) / A[d] * Bm[b, t] * x[b, d, t]
+                want = (Cm[b, t] @ h + Dv[d] * x[b, d, t]) * z[b, d, t] * expit(z[b, d, t])
+                _close(y[b, d, t], want, 1e-12, 1e-14, what=f"reverse y b={b} d={d} t={t}")
+            _close(hl[b, d], h, 1e-12, 1e-14, what="reverse h_last")
+
+
 def pin_decode_step(orc):
     """One decode step equals the exact ZOH update and gated readout, and L
     steps equal one scan over L."""
@@ -401,6 +425,6 @@ def pin_threads(orc):
     assert np.array_equal(y1, y4) and np.array_equal(h1, h4), "thread count changed result"
 
 
-ALL_PINS = [pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
+ALL_PINS = [pin_reverse, pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
             pin_dc_gain, pin_lti_convolution, pin_chunked_carry, pin_special_cases,
             pin_hand_expansions, pin_golden_ln2, pin_conv, pin_decode_step, pin_threads]

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 2
+    assert lib.mamba_abi_version() == 3
     for st in range(10):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -87,6 +87,27 @@ def scan(lib, **kw):
 ])
 def test_scan_rejects(lib, kw, want):
     assert scan(lib, **kw) == want
+
+
+def scan_ex(lib, flags, **kw):
+    a = dict(x=P(1), dt=P(2), dt_bias=P(3), A=P(4), Bm=P(5), Cm=P(6), Dskip=P(7), z=P(8),
+             h0=P(9), y=P(10), h_last=P(11), ws=P(12), ws_bytes=1 << 40, B=2, D=64, L=256,
+             N=16, io=F32)
+    a.update(kw)
+    return lib.mamba_selective_scan_fwd_ex(a["x"], a["dt"], a["dt_bias"], a["A"], a["Bm"],
+                                           a["Cm"], a["Dskip"], a["z"], a["h0"], a["y"],
+                                           a["h_last"], a["ws"], a["ws_bytes"], a["B"], a["D"],
+                                           a["L"], a["N"], a["io"], flags, None)
+
+
+def test_scan_ex_flags(lib):
+    assert scan_ex(lib, 4) == EUNSUP
+    assert scan_ex(lib, 1 << 31) == EUNSUP
+    assert scan_ex(lib, 3, y=P(1)) == EALIAS
+    assert scan_ex(lib, 1, B=0) == OK
+    if not _gpu_visible():
+        for f in (0, 1, 2, 3):
+            assert scan_ex(lib, f) == EDEV
 
 
 def test_scan_empty_is_ok(lib):
