@@ -67,6 +67,8 @@ class Oracle:
         lib.oracle_selective_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int]
         lib.oracle_conv1d_silu.restype = ctypes.c_int
         lib.oracle_conv1d_silu.argtypes = [P] * 4 + [I64] * 4 + [ctypes.c_int]
+        lib.oracle_selective_scan_bwd.restype = ctypes.c_int
+        lib.oracle_selective_scan_bwd.argtypes = [P] * 20 + [I64] * 4
         lib.oracle_conv1d_update.restype = ctypes.c_int
         lib.oracle_conv1d_update.argtypes = [P] * 5 + [I64] * 3
         lib.oracle_state_update.restype = ctypes.c_int
@@ -108,6 +110,29 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_selective_scan_fwd rejected its arguments")
         return y, h_last
+
+    def selective_scan_bwd(self, x, dt, A, Bm, Cm, dout, dt_bias=None, Dskip=None, z=None,
+                           h0=None, dh_last=None):
+        """Gradients of J = sum(out * dout) (+ sum(h_last * dh_last)) of the
+        forward scan.  Returns a dict: dx, ddt, dz (or None), dA, dD, ddt_bias,
+        dB, dC, dh0 (or None)."""
+        x, dt, A, Bm, Cm, dout = map(_f64, (x, dt, A, Bm, Cm, dout))
+        dt_bias, Dskip, z, h0, dh_last = map(_f64, (dt_bias, Dskip, z, h0, dh_last))
+        Bsz, D, L = x.shape
+        N = A.shape[1]
+        g = {"dx": np.empty_like(x), "ddt": np.empty_like(x),
+             "dz": np.empty_like(x) if z is not None else None,
+             "dA": np.empty((D, N)), "dD": np.empty(D), "ddt_bias": np.empty(D),
+             "dB": np.empty((Bsz, L, N)), "dC": np.empty((Bsz, L, N)),
+             "dh0": np.empty((Bsz, D, N)) if h0 is not None else None}
+        rc = self.lib.oracle_selective_scan_bwd(
+            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+            _ptr(h0), _ptr(dout), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dz"]),
+            _ptr(g["dA"]), _ptr(g["dD"]), _ptr(g["ddt_bias"]), _ptr(g["dB"]), _ptr(g["dC"]),
+            _ptr(g["dh0"]), Bsz, D, L, N)
+        if rc != 0:
+            raise ValueError("oracle_selective_scan_bwd rejected its arguments")
+        return g
 
     def selective_scan_reverse(self, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
                                nthreads: int = 1):
@@ -203,6 +228,10 @@ def selective_scan_reverse(*args, **kw):
 
 def state_update(*args, **kw):
     return get().state_update(*args, **kw)
+
+
+def selective_scan_bwd(*args, **kw):
+    return get().selective_scan_bwd(*args, **kw)
 
 
 def conv1d_update(*args, **kw):

@@ -35,6 +35,11 @@
  *  - Decode: one step of the same recurrence on a stored state
  *      ["Mamba架构深度剖析：如何以线性时间重塑序列建模", §3: fixed-size state,
  *       step-by-step prediction at inference].
+ *  - Backward: gradients of the scan's output (and final state) with respect
+ *    to every input, by the chain rule through the steps above in reverse
+ *    order, the forward states recomputed rather than stored by the caller
+ *      ["Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式", §2.2:
+ *       intermediate states recomputed in the backward pass].
  *
  * Layouts (all row-major, fp64):
  *   x, dt, z, y : [B, D, L]      (L fastest)
@@ -235,6 +240,121 @@ int oracle_conv1d_update(double *state, const double *x, const double *w, const 
             if (K > 1)
                 st[K - 2] = x[c];
         }
+    return 0;
+}
+
+/* d/da of the ZOH input coefficient (exp(delta a) - 1)/a:
+ *   (delta a exp(delta a) - expm1(delta a)) / a^2 = delta^2 psi(delta a),
+ *   psi(u) = (u e^u - e^u + 1)/u^2 = sum_{m>=0} (m+1) u^m / (m+2)!,
+ * by its series for |u| < 1e-4 (psi(0) = 1/2) and the closed form above. */
+static double dbcoef_da(double delta, double a)
+{
+    double u = delta * a;
+    if (fabs(u) < 1e-4)
+        return delta * delta * (0.5 + u / 3.0 + u * u / 8.0 + u * u * u / 30.0);
+    return (u * exp(u) - expm1(u)) / (a * a);
+}
+
+/* Backward of oracle_selective_scan_fwd for the objective
+ *   J = sum out * dout  (+ sum h_last * dh_last when dh_last is given).
+ * Per channel the forward states are recomputed and kept, then the adjoint
+ *   lambda_t = dJ/dh_t = C_t dy_t + nu_{t+1},   nu_t = Abar_t lambda_t,
+ * nu_L = dh_last (or 0), runs backwards with dy_t = dout_t SiLU(z_t), and
+ *   dx_t    = D dy_t + sum_n lambda_tn bcoef_tn B_tn
+ *   dDelta_t = sum_n lambda_tn Abar_tn (A_n h_(t-1),n + B_tn x_t)
+ *   ddt_t   = dDelta_t sigmoid(dt_t + dt_bias)            (softplus' = sigmoid)
+ *   dz_t    = dout_t (y_t + D x_t) SiLU'(z_t)
+ *   dA_n   += lambda_tn (Delta_t Abar_tn h_(t-1),n + dbcoef/dA_n B_tn x_t)
+ *   dB_tn  += lambda_tn bcoef_tn x_t,   dC_tn += dy_t h_tn  (summed over d)
+ *   dD     += dy_t x_t,  ddt_bias += ddt_t,  dh0 = nu_0.
+ * Outputs dx, ddt, dz [B,D,L]; dA [D,N]; dD, ddt_bias [D]; dB, dC [B,L,N];
+ * dh0 [B,D,N] are overwritten (dz, dh0 only when given; dz needs z).
+ * Single-threaded: the sums over channels and batch rows are plain loops. */
+int oracle_selective_scan_bwd(const double *x, const double *dt, const double *dt_bias,
+                              const double *A, const double *Bm, const double *Cm,
+                              const double *Dskip, const double *z, const double *h0,
+                              const double *dout, const double *dh_last, double *dx,
+                              double *ddt, double *dz, double *dA, double *dD,
+                              double *ddt_bias, double *dB, double *dC, double *dh0, int64_t B,
+                              int64_t D, int64_t L, int64_t N)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !dout || !dx || !ddt || !dA || !dD || !ddt_bias ||
+        !dB || !dC || B < 0 || D < 0 || L < 0 || N < 1 || N > 64)
+        return -1;
+    double *hist = (double *)malloc(sizeof(double) * (size_t)(L + 1) * (size_t)N);
+    double *abar = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * (size_t)N);
+    double *bco = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * (size_t)N);
+    double *dlt = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double *yy = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!hist || !abar || !bco || !dlt || !yy) {
+        free(hist); free(abar); free(bco); free(dlt); free(yy);
+        return -2;
+    }
+    for (int64_t i = 0; i < D * N; ++i)
+        dA[i] = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+        dD[d] = ddt_bias[d] = 0.0;
+    for (int64_t i = 0; i < B * L * N; ++i)
+        dB[i] = dC[i] = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            const size_t c = (size_t)b * D + d;
+            const double *xr = x + c * L, *dtr = dt + c * L, *zr = z ? z + c * L : NULL;
+            const double *go = dout + c * L;
+            const double bias = dt_bias ? dt_bias[d] : 0.0, Dv = Dskip ? Dskip[d] : 0.0;
+            const double *Ad = A + d * N;
+            /* forward, keeping every state (hist row t+1 = h_t, row 0 = h0) */
+            for (int64_t n = 0; n < N; ++n)
+                hist[n] = h0 ? h0[c * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const double *Bt = Bm + ((size_t)b * L + t) * N, *Ct = Cm + ((size_t)b * L + t) * N;
+                dlt[t] = oracle_softplus(dtr[t] + bias);
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    oracle_zoh(dlt[t], Ad[n], &abar[t * N + n], &bco[t * N + n]);
+                    hist[(t + 1) * N + n] =
+                        abar[t * N + n] * hist[t * N + n] + bco[t * N + n] * Bt[n] * xr[t];
+                    y += Ct[n] * hist[(t + 1) * N + n];
+                }
+                yy[t] = y + Dv * xr[t];
+            }
+            /* backward */
+            double nu[64];
+            for (int64_t n = 0; n < N; ++n)
+                nu[n] = dh_last ? dh_last[c * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const double *Bt = Bm + ((size_t)b * L + t) * N, *Ct = Cm + ((size_t)b * L + t) * N;
+                double *dBt = dB + ((size_t)b * L + t) * N, *dCt = dC + ((size_t)b * L + t) * N;
+                double g = 1.0;
+                if (zr) {
+                    const double sg = 1.0 / (1.0 + exp(-zr[t]));
+                    g = zr[t] * sg;
+                    if (dz)
+                        dz[c * L + t] = go[t] * yy[t] * sg * (1.0 + zr[t] * (1.0 - sg));
+                }
+                const double dy = go[t] * g;
+                dD[d] += dy * xr[t];
+                double dxs = Dv * dy, dDelta = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double lam = Ct[n] * dy + nu[n];
+                    const double hp = hist[t * N + n], ab = abar[t * N + n], bc = bco[t * N + n];
+                    dCt[n] += dy * hist[(t + 1) * N + n];
+                    dBt[n] += lam * bc * xr[t];
+                    dxs += lam * bc * Bt[n];
+                    dDelta += lam * ab * (Ad[n] * hp + Bt[n] * xr[t]);
+                    dA[d * N + n] += lam * (dlt[t] * ab * hp + dbcoef_da(dlt[t], Ad[n]) * Bt[n] * xr[t]);
+                    nu[n] = ab * lam;
+                }
+                dx[c * L + t] = dxs;
+                const double v = dtr[t] + bias;
+                ddt[c * L + t] = dDelta / (1.0 + exp(-v));
+                ddt_bias[d] += ddt[c * L + t];
+            }
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n)
+                    dh0[c * N + n] = nu[n];
+        }
+    free(hist); free(abar); free(bco); free(dlt); free(yy);
     return 0;
 }
 

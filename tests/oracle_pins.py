@@ -361,6 +361,57 @@ def pin_conv_update(orc):
     _close(np.stack(got, axis=2), orc.conv1d_silu(x, w), 1e-14, 1e-15, what="zero window")
 
 
+def pin_backward_fd(orc):
+    """Every gradient of the backward against central finite differences of
+    the forward (J = sum(out * dout) + sum(h_last * dh_last)), one input at a
+    time along a random direction, with A holding zero, tiny (|Delta A| below
+    the series switch) and ordinary entries."""
+    rng = np.random.default_rng(31)
+    Bsz, D, L, N = 2, 3, 7, 4
+    base = {
+        "x": rng.normal(size=(Bsz, D, L)), "dt": rng.normal(-0.5, 0.7, size=(Bsz, D, L)),
+        "z": rng.normal(size=(Bsz, D, L)), "A": -rng.uniform(0.3, 2.5, size=(D, N)),
+        "Bm": rng.normal(size=(Bsz, L, N)), "Cm": rng.normal(size=(Bsz, L, N)),
+        "dt_bias": rng.normal(size=D), "Dskip": rng.normal(size=D),
+        "h0": rng.normal(size=(Bsz, D, N)),
+    }
+    base["A"][0, 1] = 0.0
+    base["A"][1, 2] = -3e-5
+    base["A"][2, 0] = 0.8  # a growing state is still differentiable
+    dout = rng.normal(size=(Bsz, D, L))
+    dh_last = rng.normal(size=(Bsz, D, N))
+
+    def J(p):
+        y, hl = orc.selective_scan(p["x"], p["dt"], p["A"], p["Bm"], p["Cm"], p["dt_bias"],
+                                   p["Dskip"], p["z"], p["h0"])
+        return float(np.sum(y * dout) + np.sum(hl * dh_last))
+
+    g = orc.selective_scan_bwd(base["x"], base["dt"], base["A"], base["Bm"], base["Cm"], dout,
+                               base["dt_bias"], base["Dskip"], base["z"], base["h0"], dh_last)
+    names = {"x": "dx", "dt": "ddt", "z": "dz", "A": "dA", "Bm": "dB", "Cm": "dC",
+             "dt_bias": "ddt_bias", "Dskip": "dD", "h0": "dh0"}
+    eps = 1e-6
+    for key, gname in names.items():
+        v = rng.normal(size=base[key].shape)
+        hi = dict(base, **{key: base[key] + eps * v})
+        lo = dict(base, **{key: base[key] - eps * v})
+        fd = (J(hi) - J(lo)) / (2 * eps)
+        an = float(np.sum(g[gname] * v))
+        _close(an, fd, 1e-6, 1e-8, what=f"d/d{key}")
+    # no gate, no initial state, no final-state gradient: the same with zeros
+    g0 = orc.selective_scan_bwd(base["x"], base["dt"], base["A"], base["Bm"], base["Cm"], dout,
+                                base["dt_bias"], base["Dskip"])
+    assert g0["dz"] is None and g0["dh0"] is None
+    v = rng.normal(size=base["x"].shape)
+
+    def J0(xx):
+        y, _ = orc.selective_scan(xx, base["dt"], base["A"], base["Bm"], base["Cm"],
+                                  base["dt_bias"], base["Dskip"])
+        return float(np.sum(y * dout))
+    fd = (J0(base["x"] + eps * v) - J0(base["x"] - eps * v)) / (2 * eps)
+    _close(float(np.sum(g0["dx"] * v)), fd, 1e-6, 1e-8, what="d/dx without gate")
+
+
 def pin_reverse(orc):
     """The reversed-time scan (state runs from step L-1 down to 0) against a
     direct backward loop over the exact ZOH step, written here in numpy."""
@@ -425,6 +476,6 @@ def pin_threads(orc):
     assert np.array_equal(y1, y4) and np.array_equal(h1, h4), "thread count changed result"
 
 
-ALL_PINS = [pin_reverse, pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
+ALL_PINS = [pin_backward_fd, pin_reverse, pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
             pin_dc_gain, pin_lti_convolution, pin_chunked_carry, pin_special_cases,
             pin_hand_expansions, pin_golden_ln2, pin_conv, pin_decode_step, pin_threads]

@@ -35,6 +35,15 @@ MUTANTS = [
     ("conv_bias_dropped", "double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
     ("dskip_channel_index", "j->Dskip ? j->Dskip[d] : 0.0", "j->Dskip ? j->Dskip[0] : 0.0"),
     ("a_row_index", "j->A + d * j->N,", "j->A,"),
+    ("bwd_ddelta_drops_state", "dDelta += lam * ab * (Ad[n] * hp + Bt[n] * xr[t]);",
+     "dDelta += lam * ab * (Bt[n] * xr[t]);"),
+    ("bwd_adjoint_not_decayed", "nu[n] = ab * lam;", "nu[n] = lam;"),
+    ("bwd_dbcoef_wrong_power", "return (u * exp(u) - expm1(u)) / (a * a);",
+     "return (u * exp(u) - expm1(u)) / a;"),
+    ("bwd_no_softplus_slope", "ddt[c * L + t] = dDelta / (1.0 + exp(-v));",
+     "ddt[c * L + t] = dDelta;"),
+    ("bwd_dC_uses_previous_state", "dCt[n] += dy * hist[(t + 1) * N + n];",
+     "dCt[n] += dy * hist[t * N + n];"),
     ("conv_window_not_moved", "                st[k] = st[k + 1];", "                st[k] = st[k];"),
     ("conv_update_new_input_tap", "acc += w[d * K + K - 1] * x[c];", "acc += w[d * K] * x[c];"),
 ]
