@@ -9,6 +9,7 @@
  * and two that join the front end to the scan:
  *   mamba_conv1d_selective_scan_fwd  conv1d + SiLU fused into the scan
  *   mamba_conv1d_update              single-token conv step with its state
+ * the scan's backward pass (mamba_selective_scan_bwd),
  * plus workspace sizing and status helpers.
  *
  * Conventions shared by every entry point
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 3
+#define MAMBA_AMD_ABI_VERSION 4
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
@@ -207,6 +208,43 @@ mamba_status mamba_conv1d_selective_scan_fwd(
 mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, const float *bias,
                                  void *out, int64_t B, int64_t D, int64_t K, mamba_dtype dtype,
                                  void *stream);
+
+/*
+ * Backward pass of the selective scan ("Mamba状态空间模型深度解析：挑战
+ * Transformer的下一代序列建模范式", §2.2: the hardware-aware algorithm
+ * recomputes the intermediate states in the backward pass instead of storing
+ * them).  Given the forward call's inputs and the gradient dout of its output
+ * (and optionally dh_last of its final state), returns the gradients of
+ *   J = sum(out * dout) + sum(h_last * dh_last)
+ * with respect to every input.  Nothing from the forward call is needed
+ * besides its inputs: the states are recomputed.
+ *   x, dt, z, dout : [B, D, L] of `io` (z NULL: ungated forward)
+ *   Bm, Cm         : [B, L, N] of `io`;  A : [D, N];  dt_bias, Dskip : [D] or NULL
+ *   h0, dh_last    : [B, D, N] float or NULL (= zeros)
+ *   dx, ddt        : [B, D, L] of `io`, required (ddt is the gradient of the
+ *                    raw dt, before dt_bias and softplus)
+ *   dz             : [B, D, L] of `io`; required when z is given, not written
+ *                    when z is NULL
+ *   dA             : [D, N] float, required
+ *   dB, dC         : [B, L, N] float, required (summed over channels)
+ *   dD, ddt_bias   : [D] float or NULL (= not returned)
+ *   dh0            : [B, D, N] float or NULL (= not returned)
+ *   workspace      : mamba_selective_scan_bwd_workspace_size(...) bytes,
+ *                    256-byte aligned (none needed when B*D*L = 0)
+ * Sums over time and channels are taken in a fixed order: the result does not
+ * depend on scheduling.  Outputs must not overlap inputs, the workspace or
+ * each other.  With L = 0 or B = 0 the parameter gradients are zero and dh0 =
+ * dh_last.  Computed in fp32; bf16 outputs are rounded once.
+ */
+size_t mamba_selective_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                               mamba_dtype io);
+
+mamba_status mamba_selective_scan_bwd(
+    const void *x, const void *dt, const float *dt_bias, const float *A, const void *Bm,
+    const void *Cm, const float *Dskip, const void *z, const float *h0, const void *dout,
+    const float *dh_last, void *dx, void *ddt, float *dA, float *dB, float *dC, float *dD,
+    void *dz, float *ddt_bias, float *dh0, void *workspace, size_t workspace_bytes, int64_t B,
+    int64_t D, int64_t L, int64_t N, mamba_dtype io, void *stream);
 
 /*
  * Profiling hook.  When both are non-NULL hipEvent_t handles (passed as

@@ -15,6 +15,9 @@ Entry points (same names as the C ABI, without the ``mamba_`` prefix):
   conv1d_selective_scan_fwd(x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None,
                             conv_state_in=None, return_conv_state=False, ...)
   conv1d_update(state, x, w, bias=None, out=None)
+  selective_scan_bwd(x, dt, A, Bm, Cm, dout, dt_bias=None, Dskip=None, z=None, h0=None,
+                     dh_last=None, workspace=None)
+  selective_scan_bwd_workspace_size(B, D, L, N, dtype)
 """
 from __future__ import annotations
 
@@ -38,7 +41,8 @@ EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_selective_scan_fwd_workspace_size", "mamba_selective_scan_fwd",
             "mamba_selective_state_update", "mamba_selective_scan_fwd_ex",
             "mamba_conv1d_selective_scan_fwd",
-            "mamba_conv1d_update", "mamba_set_scan_timing_events"]
+            "mamba_conv1d_update", "mamba_set_scan_timing_events",
+            "mamba_selective_scan_bwd_workspace_size", "mamba_selective_scan_bwd"]
 
 _lib = None
 
@@ -79,6 +83,10 @@ def load_library(path: str = LIBRARY):
                                                     [SZ, I64, I64, I64, I64, I32, P])
     lib.mamba_conv1d_update.restype = I32
     lib.mamba_conv1d_update.argtypes = [P] * 5 + [I64, I64, I64, I32, P]
+    lib.mamba_selective_scan_bwd_workspace_size.restype = SZ
+    lib.mamba_selective_scan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I32]
+    lib.mamba_selective_scan_bwd.restype = I32
+    lib.mamba_selective_scan_bwd.argtypes = [P] * 21 + [SZ, I64, I64, I64, I64, I32, P]
     lib.mamba_set_scan_timing_events.restype = None
     lib.mamba_set_scan_timing_events.argtypes = [P, P]
     _lib = lib
@@ -310,6 +318,53 @@ def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None
         _ptr(z), _ptr(out), B, D, N, _io_dtype(x), _stream(dev))
     _raise(st, "mamba_selective_state_update")
     return out
+
+
+def selective_scan_bwd_workspace_size(B, D, L, N, dtype=None) -> int:
+    io = MAMBA_F32 if dtype is None else _io_dtype(_torch().empty(0, dtype=dtype))
+    return int(load_library().mamba_selective_scan_bwd_workspace_size(B, D, L, N, io))
+
+
+def selective_scan_bwd(x, dt, A, Bm, Cm, dout, dt_bias=None, Dskip=None, z=None, h0=None,
+                       dh_last=None, workspace=None):
+    """Backward pass of selective_scan_fwd: gradients of sum(out * dout)
+    (+ sum(h_last * dh_last)) with the forward states recomputed.  Inputs as
+    for selective_scan_fwd; dout [B,D,L] of x's dtype; dh_last [B,D,N] f32 or
+    None.  Returns a dict: dx, ddt, dz (None without z) of x's dtype and
+    shape; dA [D,N], dB, dC [B,L,N], dD, ddt_bias [D], dh0 [B,D,N], all f32."""
+    torch = _torch()
+    lib = load_library()
+    B, D, L = x.shape
+    N = A.shape[1]
+    dev, io_t = x.device, x.dtype
+    _check(x, "x", (B, D, L), io_t, dev)
+    _check(dt, "dt", (B, D, L), io_t, dev)
+    _check(z, "z", (B, D, L), io_t, dev, optional=True)
+    _check(dout, "dout", (B, D, L), io_t, dev)
+    _check(Bm, "Bm", (B, L, N), io_t, dev)
+    _check(Cm, "Cm", (B, L, N), io_t, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (D,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
+    _check(h0, "h0", (B, D, N), torch.float32, dev, optional=True)
+    _check(dh_last, "dh_last", (B, D, N), torch.float32, dev, optional=True)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dx": torch.empty_like(x), "ddt": torch.empty_like(x),
+         "dz": torch.empty_like(x) if z is not None else None,
+         "dA": torch.empty((D, N), **f32), "dB": torch.empty((B, L, N), **f32),
+         "dC": torch.empty((B, L, N), **f32), "dD": torch.empty((D,), **f32),
+         "ddt_bias": torch.empty((D,), **f32), "dh0": torch.empty((B, D, N), **f32)}
+    io = _io_dtype(x)
+    need = int(lib.mamba_selective_scan_bwd_workspace_size(B, D, L, N, io))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mamba_selective_scan_bwd(
+        _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+        _ptr(h0), _ptr(dout), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]),
+        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
+        _ptr(g["dh0"]), _ptr(workspace), workspace.numel(), B, D, L, N, io, _stream(dev))
+    _raise(st, "mamba_selective_scan_bwd")
+    return g
 
 
 def set_scan_timing_events_raw(start=None, stop=None):

@@ -399,4 +399,122 @@ mamba_status mamba_selective_state_update(float *h, const void *x, const void *d
     return launched(mamba::launch_state_update(a, (hipStream_t)stream));
 }
 
+
+size_t mamba_selective_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
+                                               mamba_dtype io)
+{
+    (void)io;
+    if (!sizes_ok(B, D, L) || N < 1 || N > kMaxN)
+        return 0;
+    if (B * D * L == 0)
+        return 0;
+    return mamba::scan_bwd_ws_layout(B, D, L).total;
+}
+
+mamba_status mamba_selective_scan_bwd(
+    const void *x, const void *dt, const float *dt_bias, const float *A, const void *Bm,
+    const void *Cm, const float *Dskip, const void *z, const float *h0, const void *dout,
+    const float *dh_last, void *dx, void *ddt, float *dA, float *dB, float *dC, float *dD,
+    void *dz, float *ddt_bias, float *dh0, void *workspace, size_t workspace_bytes, int64_t B,
+    int64_t D, int64_t L, int64_t N, mamba_dtype io, void *stream)
+{
+    if (!valid_dtype(io))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, D, L) || N < 0)
+        return MAMBA_ERR_SHAPE;
+    if (N < 1 || N > kMaxN)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (D == 0)
+        return MAMBA_OK;
+    const bool empty = B * L == 0;
+    if (!dA)
+        return MAMBA_ERR_NULL;
+    if (!empty && (!x || !dt || !A || !Bm || !Cm || !dout || !dx || !ddt || !dB || !dC ||
+                   (z && !dz)))
+        return MAMBA_ERR_NULL;
+    if (!z)
+        dz = nullptr;  // no gate, no gate gradient
+    const size_t es = esize(io);
+    if (!aligned(x, es) || !aligned(dt, es) || !aligned(z, es) || !aligned(dout, es) ||
+        !aligned(Bm, es) || !aligned(Cm, es) || !aligned(dx, es) || !aligned(ddt, es) ||
+        !aligned(dz, es) || !aligned(A, 4) || !aligned(dt_bias, 4) || !aligned(Dskip, 4) ||
+        !aligned(h0, 4) || !aligned(dh_last, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
+        !aligned(dC, 4) || !aligned(dD, 4) || !aligned(ddt_bias, 4) || !aligned(dh0, 4))
+        return MAMBA_ERR_ALIGN;
+    size_t ws_need = 0;
+    if (!empty) {
+        if (B * L * kMaxN >= (int64_t(1) << 31))
+            return MAMBA_ERR_SHAPE;
+        const mamba::BwdWsLayout lay = mamba::scan_bwd_ws_layout(B, D, L);
+        if (lay.scan.n_items >= (int64_t(1) << 23))
+            return MAMBA_ERR_SHAPE;
+        ws_need = lay.total;
+        if (!workspace || workspace_bytes < ws_need || !aligned(workspace, 256))
+            return MAMBA_ERR_WORKSPACE;
+    }
+    const int64_t n = B * D * L;
+    const size_t nb = (size_t)n * es, bln = (size_t)(B * L * N) * 4, dn = (size_t)(D * N) * 4,
+                 bdn = (size_t)(B * D * N) * 4;
+    const Range ins[] = {rng(x, x ? nb : 0),
+                         rng(dt, dt ? nb : 0),
+                         rng(z, z ? nb : 0),
+                         rng(dout, dout ? nb : 0),
+                         rng(Bm, Bm ? (size_t)(B * L * N) * es : 0),
+                         rng(Cm, Cm ? (size_t)(B * L * N) * es : 0),
+                         rng(A, A ? dn : 0),
+                         rng(dt_bias, dt_bias ? (size_t)D * 4 : 0),
+                         rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                         rng(h0, h0 ? bdn : 0),
+                         rng(dh_last, dh_last ? bdn : 0)};
+    const Range outs[] = {rng(dx, dx ? nb : 0),
+                          rng(ddt, ddt ? nb : 0),
+                          rng(dz, dz ? nb : 0),
+                          rng(dA, dn),
+                          rng(dB, dB ? bln : 0),
+                          rng(dC, dC ? bln : 0),
+                          rng(dD, dD ? (size_t)D * 4 : 0),
+                          rng(ddt_bias, ddt_bias ? (size_t)D * 4 : 0),
+                          rng(dh0, dh0 ? bdn : 0),
+                          rng(workspace, ws_need)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r))
+                return MAMBA_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j]))
+                return MAMBA_ERR_ALIAS;
+    }
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::BwdArgsHost a;
+    a.x = x;
+    a.dt = dt;
+    a.Bm = Bm;
+    a.Cm = Cm;
+    a.z = z;
+    a.dout = dout;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.h0 = h0;
+    a.dh_last = dh_last;
+    a.dx = dx;
+    a.ddt = ddt;
+    a.dz = dz;
+    a.dA = dA;
+    a.dB = dB;
+    a.dC = dC;
+    a.dD = dD;
+    a.ddt_bias = ddt_bias;
+    a.dh0 = dh0;
+    a.ws = (unsigned char *)workspace;
+    a.B = B;
+    a.D = D;
+    a.L = L;
+    a.N = (int)N;
+    a.bf16 = io == MAMBA_BF16;
+    return launched(mamba::launch_selective_scan_bwd(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -51,9 +51,36 @@ struct ScanArgs {
     void *conv_state_out;
     bool reverse;     // scan from step L-1 down to step 0 (plain scan only)
     bool accumulate;  // y += result
+    // backward pass helpers: adjoint = the reverse scan of the adjoint state
+    // nu_t = Abar_t (nu_(t+1) + C_t dy_t) with x = dout (y unused; h0 = the
+    // final state's gradient, h_last = dh0); chunk_states = per 32-step chunk
+    // its start state in scan order, [groups][n_seg*4][16][64] floats
+    bool adjoint = false;
+    float *chunk_states = nullptr;
     hipEvent_t ev_start, ev_stop;  // optional timing of the main kernel
 };
 hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s);
+
+// Backward pass of the scan (scan_bwd.hip).  Gradients of sum(out * dout)
+// (+ sum(h_last * dh_last)); see launch_selective_scan_bwd.
+struct BwdWsLayout {
+    ScanWsLayout scan;  // the two scans' workspace (forward, then adjoint)
+    size_t off_hsave = 0, off_nusave = 0, off_dBp = 0, off_dCp = 0, off_dAp = 0, off_dDp = 0,
+           off_dbp = 0, total = 0;
+};
+BwdWsLayout scan_bwd_ws_layout(int64_t B, int64_t D, int64_t L);
+
+struct BwdArgsHost {
+    const void *x, *dt, *Bm, *Cm, *z, *dout;
+    const float *dt_bias, *A, *Dskip, *h0, *dh_last;
+    void *dx, *ddt, *dz;                          // [B, D, L] of the I/O type
+    float *dA, *dB, *dC, *dD, *ddt_bias, *dh0;    // fp32
+    unsigned char *ws;
+    int64_t B, D, L;
+    int N;
+    bool bf16;
+};
+hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s);
 
 struct ConvArgs {
     const void *x;

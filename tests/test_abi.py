@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 3
+    assert lib.mamba_abi_version() == 4
     for st in range(10):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -187,6 +187,60 @@ def test_conv_update_rejects(lib):
     assert f(P(1), P(2), P(3), None, P(4), 0, 8, 4, F32, None) == OK
 
 
+def bwd(lib, **kw):
+    a = dict(x=P(1), dt=P(2), dt_bias=P(3), A=P(4), Bm=P(5), Cm=P(6), Dskip=P(7), z=P(8),
+             h0=P(9), dout=P(10), dh_last=P(11), dx=P(12), ddt=P(13), dA=P(14), dB=P(15),
+             dC=P(16), dD=P(17), dz=P(18), ddt_bias=P(19), dh0=P(20), ws=P(21),
+             ws_bytes=1 << 40, B=2, D=64, L=256, N=16, io=F32)
+    a.update(kw)
+    return lib.mamba_selective_scan_bwd(
+        a["x"], a["dt"], a["dt_bias"], a["A"], a["Bm"], a["Cm"], a["Dskip"], a["z"], a["h0"],
+        a["dout"], a["dh_last"], a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+        a["ddt_bias"], a["dh0"], a["ws"], a["ws_bytes"], a["B"], a["D"], a["L"], a["N"],
+        a["io"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(io=5), EDTYPE), (dict(N=0), EUNSUP), (dict(N=17), EUNSUP),
+    (dict(L=-1), ESHAPE), (dict(D=1 << 30, L=1 << 30), ESHAPE),
+    (dict(B=1 << 20, L=1 << 12), ESHAPE),        # B*L*16 too large for the B/C grid
+    (dict(x=None), ENULL), (dict(dout=None), ENULL), (dict(dA=None), ENULL),
+    (dict(dB=None), ENULL), (dict(dz=None), ENULL),  # z given, dz missing
+    (dict(ws=None), EWS), (dict(ws_bytes=1000), EWS),
+    (dict(ws=ctypes.c_void_p(0x10000000000 + 21 * 0x100000000 + 64)), EWS),
+    (dict(dx=ctypes.c_void_p(0x10000000000 + 12 * 0x100000000 + 2)), EALIGN),
+    (dict(io=BF16, dout=ctypes.c_void_p(0x10000000000 + 10 * 0x100000000 + 1)), EALIGN),
+    (dict(dh0=ctypes.c_void_p(0x10000000000 + 20 * 0x100000000 + 2)), EALIGN),
+    (dict(dx=P(1)), EALIAS), (dict(dB=P(5)), EALIAS), (dict(dh0=P(11)), EALIAS),
+    (dict(dC=P(15)), EALIAS), (dict(dA=P(21)), EALIAS),
+    (dict(ddt=ctypes.c_void_p(0x10000000000 + 12 * 0x100000000 + 4096)), EALIAS),
+])
+def test_bwd_rejects(lib, kw, want):
+    assert bwd(lib, **kw) == want
+
+
+def test_bwd_optional_and_empty(lib):
+    # D = 0: nothing at all to do
+    assert bwd(lib, D=0, x=None, dA=None, ws=None) == OK
+    # no gate: dz is not required (and never written)
+    if not _gpu_visible():
+        assert bwd(lib, z=None, dz=None) == EDEV
+        assert bwd(lib, z=None, dz=P(18), dt_bias=None, Dskip=None, h0=None, dh_last=None,
+                   dD=None, ddt_bias=None, dh0=None) == EDEV
+        # L = 0: only dA (and the optional outputs) are written, no workspace
+        assert bwd(lib, L=0, x=None, dt=None, Bm=None, Cm=None, dout=None, dx=None, ddt=None,
+                   dB=None, dC=None, ws=None, ws_bytes=0) == EDEV
+    assert bwd(lib, L=0, dA=None) == ENULL
+
+
+def test_bwd_workspace_size(lib):
+    f = lib.mamba_selective_scan_bwd_workspace_size
+    assert f(0, 64, 256, 16, F32) == 0 and f(1, 64, 256, 0, F32) == 0
+    small, big = f(1, 64, 256, 16, F32), f(2, 1536, 2048, 16, BF16)
+    assert 0 < small < big and big % 256 == 0
+    assert small > lib.mamba_selective_scan_fwd_workspace_size(1, 64, 256, 16, F32)
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="valid fake pointers must never reach a GPU")
 def test_valid_arguments_without_gpu_report_device(lib):
     assert fused(lib) == EDEV
@@ -197,6 +251,7 @@ def test_valid_arguments_without_gpu_report_device(lib):
     assert lib.mamba_conv1d_silu(P(1), P(2), None, P(3), 2, 8, 32, 4, F32, None) == EDEV
     assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
                                             P(9), P(10), 4, 64, 16, F32, None) == EDEV
+    assert bwd(lib) == EDEV
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
