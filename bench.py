@@ -328,6 +328,53 @@ def run_scan(args, torch, mamba, W, idx, bidir=False):
                         "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}}
 
 
+def run_bwd(args, torch, mamba, W):
+    """The scan's backward pass (gradients of every input, states recomputed)
+    at the block's scan shape: B=2, D_inner=1536, L=8192, N=16, fp32 I/O."""
+    wl = W.WORKLOADS[1]
+    B, D, L, N = wl.B, wl.D, wl.L, wl.N
+    p = W.make_scan_inputs(B, D, L, N, "f32", wl.seed)
+    rng = np.random.default_rng(wl.seed + 7)
+    dout_np = rng.standard_normal((B, D, L)).astype(np.float32)
+    dev = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, dt, z, dout = T(p["x"]), T(p["dt"]), T(p["z"]), T(dout_np)
+    Bm, Cm, A, bias, Dk = T(p["Bm"]), T(p["Cm"]), T(p["A"]), T(p["dt_bias"]), T(p["Dskip"])
+    ws = torch.empty(mamba.selective_scan_bwd_workspace_size(B, D, L, N), dtype=torch.uint8,
+                     device=dev)
+
+    def step(pair=None):
+        if pair is not None:
+            mamba.set_scan_timing_events_raw(pair[0], pair[1])
+        mamba.selective_scan_bwd(x, dt, A, Bm, Cm, dout, bias, Dk, z, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mamba.set_scan_timing_events_raw(None, None)
+    k_all = [ev.elapsed_ms(a, b) for a, b in pairs]
+    k_ms = float(np.mean(k_all))
+    ms_step = elapsed / args.steps * 1e3
+    elems = B * D * L
+    return {"metric": "selective-scan backward Gelem/s (B*L*D_inner)",
+            "value": round(elems / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": f"scan_bwd_b{B}_d{D}_l{L}_n{N}_f32", "batch": B,
+                       "d_inner": D, "seq_len": L, "d_state": N, "io": "f32",
+                       "step": "forward recompute, adjoint scan, chunk gradients, reductions"},
+            "kernels": {"chunk_grad_ms": quantiles(k_all),
+                        "chunk_grad_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
+
+
 def run_decode(args, torch, mamba, W):
     wl = W.WORKLOADS[4]
     dev = torch.device("cuda:0")
@@ -378,7 +425,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="block",
                     choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode",
-                             "bidir_bf16_l2048"])
+                             "bidir_bf16_l2048", "bwd"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--unfused", action="store_true",
                     help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
@@ -415,6 +462,8 @@ def main():
         out = run_scan(args, torch, mamba, W, 3)
     elif args.workload == "bidir_bf16_l2048":
         out = run_scan(args, torch, mamba, W, 2, bidir=True)
+    elif args.workload == "bwd":
+        out = run_bwd(args, torch, mamba, W)
     else:
         out = run_decode(args, torch, mamba, W)
     print(json.dumps(out), flush=True)

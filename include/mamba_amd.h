@@ -249,7 +249,8 @@ mamba_status mamba_selective_scan_bwd(
 /*
  * Profiling hook.  When both are non-NULL hipEvent_t handles (passed as
  * void*), later calls made from this host thread record `start` right before
- * and `stop` right after the main scan kernel of mamba_selective_scan_fwd, on
+ * and `stop` right after the main scan kernel of mamba_selective_scan_fwd (and
+ * its variants), or the chunk-gradient kernel of mamba_selective_scan_bwd, on
  * the call's stream.  Pass NULL, NULL to turn it off.
  */
 void mamba_set_scan_timing_events(void *start, void *stop);

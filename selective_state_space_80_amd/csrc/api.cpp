@@ -514,6 +514,8 @@ mamba_status mamba_selective_scan_bwd(
     a.L = L;
     a.N = (int)N;
     a.bf16 = io == MAMBA_BF16;
+    a.ev_start = g_ev_start;
+    a.ev_stop = g_ev_stop;
     return launched(mamba::launch_selective_scan_bwd(a, (hipStream_t)stream));
 }
 

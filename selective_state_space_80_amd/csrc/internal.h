@@ -79,6 +79,7 @@ struct BwdArgsHost {
     int64_t B, D, L;
     int N;
     bool bf16;
+    hipEvent_t ev_start, ev_stop;  // optional timing of the chunk-gradient kernel
 };
 hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s);
 

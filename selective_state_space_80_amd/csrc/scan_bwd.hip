@@ -33,12 +33,13 @@ constexpr int kHalf = kBT / 2;       // states kept for half a chunk at a time
 constexpr int kBThreads = 256;       // 64 channels x 4 quarters
 constexpr int kCh = kBThreads / 4;   // channels per workgroup (one tile)
 constexpr int kPad = kBT + 1;        // LDS row stride of the per-channel arrays
+constexpr int kTStride = 2 * kMaxN + 4;  // row of dB then dC values, 16-byte aligned
 
-// dβ/dA for β(A) = (e^(ΔA) - 1)/A:  Δ² ψ(u), u = ΔA,
+// dβ/dA for β(A) = (e^(ΔA) - 1)/A, u = ΔA, e = e^u:  Δ² ψ(u) with
 // ψ(u) = (u e^u - e^u + 1)/u² = Σ_m (m+1) u^m / (m+2)!, by its series for
-// |u| < 1/4 (through u^6: truncation below 3e-9 relative) and the closed form
-// (u e^u - em)/u² with em = e^u - 1 otherwise.
-__device__ __forceinline__ float dbeta_dA(float delta, float u, float e)
+// |u| < 1/4 (through u^6: truncation below 3e-9 relative); otherwise the same
+// quantity as (Δ e - β)/A (β = (e - 1)/A), whose cancellation is mild there.
+__device__ __forceinline__ float dbeta_dA(float delta, float u, float e, float beta, float rcpa)
 {
     float s = 7.f / 40320.f;  // (m+1)/(m+2)! for m = 6 .. 0
     s = fmaf(s, u, 6.f / 5040.f);
@@ -47,8 +48,16 @@ __device__ __forceinline__ float dbeta_dA(float delta, float u, float e)
     s = fmaf(s, u, 3.f / 24.f);
     s = fmaf(s, u, 2.f / 6.f);
     s = fmaf(s, u, 0.5f);
-    const float closed = (u * e - (e - 1.f)) / (u * u);
-    return delta * delta * (fabsf(u) < 0.25f ? s : closed);
+    const float closed = fmaf(delta, e, -beta) * rcpa;
+    return fabsf(u) < 0.25f ? delta * delta * s : closed;
+}
+
+// Sum over the four lanes of a quad (one channel): two DPP quad permutes.
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // lane ^ 1
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // lane ^ 2
+    return v;
 }
 
 struct BwdArgs {
@@ -70,11 +79,13 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
     using T = typename E::T;
     __shared__ __align__(16) float sB[kBT][kMaxN];
     __shared__ __align__(16) float sC[kBT][kMaxN];
-    // per channel and step: Δ, x, dy, dout SiLU'(z), σ(dt + bias); after a
-    // step is done its slots hold dx (sX), ddt (sSG), dz (sGZ)
-    __shared__ float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad], sGZ[kCh][kPad],
-        sSG[kCh][kPad];
-    __shared__ float sRed[2][kBThreads / 64][kBT][kMaxN];  // per-wave dB, dC sums
+    // per channel and step: Δ, x, dy, σ(dt + bias); once a step is done its
+    // slots hold dx (sX), y + D x (sDY) and ddt (sSG)
+    __shared__ float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad], sSG[kCh][kPad];
+    // dB, dC of two steps per wave, channel-major, summed over the wave's 16
+    // channels by reading them back transposed; the wave sums go to sRed
+    __shared__ __align__(16) float sT[kBThreads / 64][2][16][kTStride];
+    __shared__ float sRed[kBThreads / 64][kBT][2 * kMaxN];
 
     const int64_t wg = blockIdx.x;
     const int64_t c = wg % p.n_chunks;         // chunk
@@ -101,44 +112,39 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         const int cc = e / kBT, r = e % kBT;
         const int64_t dd = min(tile * kCh + cc, p.D - 1);
         const int64_t i = (b * p.D + dd) * p.L + t0 + r;
-        float del = 0.f, xv = 0.f, dy = 0.f, gz = 0.f, sg = 0.f;
+        float del = 0.f, xv = 0.f, dy = 0.f, sg = 0.f;
         if (r < nt) {
             const float bias = p.dt_bias ? p.dt_bias[dd] : 0.f;
             const float v = E::load(reinterpret_cast<const T *>(p.dt) + i) + bias;
             del = softplus_log2(v * kLog2e) * kLn2;
             sg = hw_rcp(1.f + hw_exp2(-v * kLog2e));
             xv = E::load(reinterpret_cast<const T *>(p.x) + i);
-            const float go = E::load(reinterpret_cast<const T *>(p.dout) + i);
-            if (p.z) {
-                const float zv = E::load(reinterpret_cast<const T *>(p.z) + i);
-                const float sz = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
-                dy = go * zv * sz;
-                gz = go * sz * fmaf(zv, 1.f - sz, 1.f);
-            } else {
-                dy = go;
-            }
+            dy = E::load(reinterpret_cast<const T *>(p.dout) + i);
+            if (p.z)
+                dy *= silu_hw(E::load(reinterpret_cast<const T *>(p.z) + i));
         }
         sDel[cc][r] = del;
         sX[cc][r] = xv;
         sDY[cc][r] = dy;
-        sGZ[cc][r] = gz;
         sSG[cc][r] = sg;
     }
     __syncthreads();
 
     // ---- per-lane constants: states n = 4q + i of channel dc --------------
-    float a[4], hin[4], nu[4], dAacc[4];
+    float a[4], rcpa[4], hin[4], nu[4], dAacc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = 4 * q + i;
         const bool live = active && n < p.N;  // other states stay exactly zero
         a[i] = live ? p.A[dc * p.N + n] : 0.f;
+        rcpa[i] = a[i] != 0.f ? hw_rcp(a[i]) : 0.f;
         const int64_t cs = ((g * p.n_cslots + c) * kMaxN + n) * 64 + ch;
         hin[i] = live ? p.hsave[cs] : 0.f;
         nu[i] = live ? p.nusave[cs] : 0.f;
         dAacc[i] = 0.f;
     }
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
+    const float live_ch = active ? 1.f : 0.f;  // channels past D (copies) add nothing
     float dDacc = 0.f, dbacc = 0.f;
 
     // one forward step of the lane's four states
@@ -186,52 +192,53 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
                 const float e = hw_exp2(u * kLog2e);
                 const float beta = zoh_input_coef(a[i], del, e);
                 const float lam = fmaf(Cv[i], dy, nu[i]);
+                const float bx = Bv[i] * xv;
+                const float lb = lam * beta;
+                const float le = lam * e;
                 dCv[i] = dy * ht;
-                dBv[i] = lam * beta * xv;
-                dxp = fmaf(lam * beta, Bv[i], dxp);
-                ddel = fmaf(lam * e, fmaf(a[i], hp, Bv[i] * xv), ddel);
-                dAacc[i] = fmaf(lam, fmaf(del * e, hp, dbeta_dA(del, u, e) * Bv[i] * xv),
-                                dAacc[i]);
+                dBv[i] = lb * xv;
+                dxp = fmaf(lb, Bv[i], dxp);
+                ddel = fmaf(le, fmaf(a[i], hp, bx), ddel);
+                dAacc[i] = fmaf(del * le, hp, fmaf(lam * bx, dbeta_dA(del, u, e, beta, rcpa[i]),
+                                                   dAacc[i]));
                 yp = fmaf(Cv[i], ht, yp);
-                nu[i] = e * lam;
+                nu[i] = le;
             }
-            // sums over the channel's four lanes
-            dxp += __shfl_xor(dxp, 1);
-            dxp += __shfl_xor(dxp, 2);
-            ddel += __shfl_xor(ddel, 1);
-            ddel += __shfl_xor(ddel, 2);
-            yp += __shfl_xor(yp, 1);
-            yp += __shfl_xor(yp, 2);
-            // dB, dC: sums over the wave's 16 channels (lanes of equal q);
-            // channels past D (copies of the last one) add nothing
+            dxp = quad_sum(dxp);
+            ddel = quad_sum(ddel);
+            yp = quad_sum(yp);
+            // every lane of the quad holds the sums: all four store the same
+            // values, no branch
+            const float ddt = ddel * sSG[ch][r];
+            dDacc = fmaf(dy, xv, dDacc);  // padded steps have dy = x = 0
+            dbacc += ddt;                 // and σ = 0
+            sX[ch][r] = fmaf(Dd, dy, dxp);   // dx
+            sDY[ch][r] = fmaf(Dd, xv, yp);   // y + D x, for dz
+            sSG[ch][r] = ddt;                // ddt
+            // dB, dC: sums over the wave's 16 channels.  Two steps at a time: the
+            // lanes store their values channel-major, then lane l adds up the
+            // 16 channels of entry l (step j + l/32, value l%32) in order.
+            const int s2 = j & 1;
+            float4 *row = reinterpret_cast<float4 *>(&sT[wave][s2][(tid & 63) >> 2][0]);
+            row[q] = make_float4(dBv[0] * live_ch, dBv[1] * live_ch, dBv[2] * live_ch,
+                                 dBv[3] * live_ch);
+            row[4 + q] = make_float4(dCv[0] * live_ch, dCv[1] * live_ch, dCv[2] * live_ch,
+                                     dCv[3] * live_ch);
+            if (s2 == 0) {
+                __builtin_amdgcn_wave_barrier();
+                const int l = tid & 63, so = l >> 5, kn = l & 31;
+                float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dBv[i] = active ? dBv[i] : 0.f;
-                dCv[i] = active ? dCv[i] : 0.f;
+                for (int cw = 0; cw < 16; ++cw)
+                    acc += sT[wave][so][cw][kn];
+                sRed[wave][r + so][kn] = acc;
+                __builtin_amdgcn_wave_barrier();
+            }
+            // keep the accumulators' chains in their steps (otherwise the
+            // compiler sinks them to the end and every operand stays live)
 #pragma unroll
-                for (int m = 4; m < 64; m <<= 1) {
-                    dBv[i] += __shfl_xor(dBv[i], m);
-                    dCv[i] += __shfl_xor(dCv[i], m);
-                }
-            }
-            if ((tid & 63) < 4) {  // channel 0 of the wave holds the sums
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sRed[0][wave][r][4 * q + i] = dBv[i];
-                    sRed[1][wave][r][4 * q + i] = dCv[i];
-                }
-            }
-            if (q == 0) {
-                const float ddt = ddel * sSG[ch][r];
-                if (r < nt) {
-                    dDacc = fmaf(dy, xv, dDacc);
-                    dbacc += ddt;
-                }
-                const float gz = sGZ[ch][r];
-                sX[ch][r] = fmaf(Dd, dy, dxp);     // dx
-                sSG[ch][r] = ddt;                  // ddt
-                sGZ[ch][r] = gz * fmaf(Dd, xv, yp);  // dz
-            }
+            for (int i = 0; i < 4; ++i)
+                __asm__ volatile("" : "+v"(dAacc[i]), "+v"(nu[i]));
         }
     };
 
@@ -258,8 +265,14 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
             const int64_t i = (b * p.D + dd) * p.L + t0 + r;
             E::store(reinterpret_cast<T *>(p.dx) + i, sX[cc][r]);
             E::store(reinterpret_cast<T *>(p.ddt) + i, sSG[cc][r]);
-            if (p.dz)
-                E::store(reinterpret_cast<T *>(p.dz) + i, sGZ[cc][r]);
+            if (p.dz) {
+                // dz = dout (y + D x) SiLU'(z), SiLU'(z) = σ(z)(1 + z(1 - σ(z)))
+                const float zv = E::load(reinterpret_cast<const T *>(p.z) + i);
+                const float go = E::load(reinterpret_cast<const T *>(p.dout) + i);
+                const float sz = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
+                E::store(reinterpret_cast<T *>(p.dz) + i,
+                         go * sDY[cc][r] * sz * fmaf(zv, 1.f - sz, 1.f));
+            }
         }
     }
     for (int e = tid; e < kBT * kMaxN; e += kBThreads) {
@@ -268,8 +281,8 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
             float sb = 0.f, sc = 0.f;
 #pragma unroll
             for (int wv = 0; wv < kBThreads / 64; ++wv) {
-                sb += sRed[0][wv][r][n];
-                sc += sRed[1][wv][r][n];
+                sb += sRed[wv][r][n];
+                sc += sRed[wv][r][kMaxN + n];
             }
             const int64_t o = ((tile * p.B + b) * p.L + t0 + r) * kMaxN + n;
             p.dBp[o] = sb;
@@ -288,45 +301,59 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
     }
 }
 
-// Fixed-order sums of the partials: dB, dC over tiles; dA, dD, ddt_bias over
-// batch rows and chunks.
-__global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs p, float *dB, float *dC,
-                                                              float *dA, float *dD,
-                                                              float *ddt_bias, int64_t n_bc,
-                                                              int64_t n_a)
+// Fixed-order column sums of a [rows][cols] partial array:
+//   out[o * n_out + n] = Σ_r in[r][o * inner + n]   for n < n_out.
+// A workgroup takes 256/RG columns; RG row groups per column each add every
+// RG-th row with four interleaved accumulators, then one thread per column
+// adds the groups in order.  The result depends on the shape only.
+template <int RG>
+__global__ void __launch_bounds__(256) colsum_kernel(const float *__restrict__ in,
+                                                     float *__restrict__ out, int64_t rows,
+                                                     int64_t cols, int inner, int n_out)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n_bc) {  // (b, t, n) with n < N
-        const int64_t n = i % p.N, bt = i / p.N;
-        float sb = 0.f, sc = 0.f;
-        for (int64_t tl = 0; tl < p.n_dtiles; ++tl) {
-            const int64_t o = (tl * p.B * p.L + bt) * kMaxN + n;
-            sb += p.dBp[o];
-            sc += p.dCp[o];
+    constexpr int kCols = 256 / RG;
+    __shared__ float part[RG][kCols];
+    const int cg = threadIdx.x % kCols, rg = threadIdx.x / kCols;
+    const int64_t col = (int64_t)blockIdx.x * kCols + cg;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if (col < cols) {
+        int64_t r = rg;
+        for (; r + 3 * RG < rows; r += 4 * RG) {
+            s0 += in[r * cols + col];
+            s1 += in[(r + RG) * cols + col];
+            s2 += in[(r + 2 * RG) * cols + col];
+            s3 += in[(r + 3 * RG) * cols + col];
         }
-        dB[i] = sb;
-        dC[i] = sc;
-        return;
+        for (; r < rows; r += RG)
+            s0 += in[r * cols + col];
     }
-    const int64_t k = i - n_bc;
-    if (k < n_a) {  // (d, n) with n < N
-        const int64_t n = k % p.N, d = k / p.N;
-        float s = 0.f;
-        for (int64_t bc = 0; bc < p.B * p.n_chunks; ++bc)
-            s += p.dAp[(bc * p.D + d) * kMaxN + n];
-        dA[k] = s;
-        if (n == 0) {
-            float sd = 0.f, sb = 0.f;
-            for (int64_t bc = 0; bc < p.B * p.n_chunks; ++bc) {
-                sd += p.dDp[bc * p.D + d];
-                sb += p.dbp[bc * p.D + d];
-            }
-            if (dD)
-                dD[d] = sd;
-            if (ddt_bias)
-                ddt_bias[d] = sb;
-        }
+    part[rg][cg] = (s0 + s1) + (s2 + s3);
+    __syncthreads();
+    if (rg == 0 && col < cols) {
+        float t = part[0][cg];
+#pragma unroll
+        for (int k = 1; k < RG; ++k)
+            t += part[k][cg];
+        const int64_t o = col / inner;
+        const int n = (int)(col - o * inner);
+        if (n < n_out)
+            out[o * n_out + n] = t;
     }
+}
+
+hipError_t colsum(const float *in, float *out, int64_t rows, int64_t cols, int inner, int n_out,
+                  hipStream_t s)
+{
+    if (!out || cols == 0)
+        return hipSuccess;
+    if (rows >= 64) {  // long sums: 16 row groups of 16 columns
+        hipLaunchKernelGGL(colsum_kernel<16>, dim3((unsigned)((cols + 15) / 16)), dim3(256), 0,
+                           s, in, out, rows, cols, inner, n_out);
+    } else {
+        hipLaunchKernelGGL(colsum_kernel<4>, dim3((unsigned)((cols + 63) / 64)), dim3(256), 0,
+                           s, in, out, rows, cols, inner, n_out);
+    }
+    return hipGetLastError();
 }
 
 // Nothing to scan (L = 0 or B = 0): the parameter gradients are empty sums
@@ -467,17 +494,26 @@ hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s)
     k.n_cslots = w.scan.n_seg * kWavesPerSeg;
     k.N = a.N;
     const dim3 grid((unsigned)(w.scan.groups * k.n_chunks));
+    if (a.ev_start)
+        (void)hipEventRecord(a.ev_start, s);
     if (a.bf16)
         hipLaunchKernelGGL(scan_bwd_chunk_kernel<true>, grid, dim3(kBThreads), 0, s, k);
     else
         hipLaunchKernelGGL(scan_bwd_chunk_kernel<false>, grid, dim3(kBThreads), 0, s, k);
     e = hipGetLastError();
+    if (a.ev_stop)
+        (void)hipEventRecord(a.ev_stop, s);
     if (e != hipSuccess)
         return e;
-    // 4. reductions
-    const int64_t n_bc = a.B * a.L * a.N, n_a = a.D * a.N;
-    hipLaunchKernelGGL(scan_bwd_reduce_kernel, dim3((unsigned)((n_bc + n_a + 255) / 256)),
-                       dim3(256), 0, s, k, a.dB, a.dC, a.dA, a.dD, a.ddt_bias, n_bc, n_a);
+    // 4. reductions: dB, dC over tiles; dA, dD, ddt_bias over (b, chunk)
+    const int64_t rows_t = w.scan.n_dtiles, rows_c = a.B * k.n_chunks;
+    const int64_t cols_bc = a.B * a.L * kMaxN;
+    if ((e = colsum(k.dBp, a.dB, rows_t, cols_bc, kMaxN, a.N, s)) != hipSuccess ||
+        (e = colsum(k.dCp, a.dC, rows_t, cols_bc, kMaxN, a.N, s)) != hipSuccess ||
+        (e = colsum(k.dAp, a.dA, rows_c, a.D * kMaxN, kMaxN, a.N, s)) != hipSuccess ||
+        (e = colsum(k.dDp, a.dD, rows_c, a.D, 1, 1, s)) != hipSuccess ||
+        (e = colsum(k.dbp, a.ddt_bias, rows_c, a.D, 1, 1, s)) != hipSuccess)
+        return e;
     return hipGetLastError();
 }
 
