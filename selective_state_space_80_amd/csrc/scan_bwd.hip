@@ -18,7 +18,8 @@
 //      saving every chunk's incoming ν (from the future) and writing dh0;
 //   3. this file's chunk kernel: per 64-channel tile and chunk, four lanes per
 //      channel (one quarter of the 16 states each) recompute the chunk's
-//      states half a chunk at a time, walk them backwards, and write dx, ddt,
+//      states a quarter chunk at a time from checkpoints, keeping each step's
+//      decay and input coefficient, walk them backwards, and write dx, ddt,
 //      dz and per-tile / per-chunk partial sums of dB, dC, dA, dD, ddt_bias;
 //   4. a reduction of those partial sums in a fixed order (deterministic).
 #include "device_common.h"
@@ -29,27 +30,48 @@ namespace mamba {
 namespace {
 
 constexpr int kBT = 32;              // steps per chunk (the forward chunk grid)
-constexpr int kHalf = kBT / 2;       // states kept for half a chunk at a time
+constexpr int kQuarter = kBT / 4;    // steps whose states stay in registers at a time
 constexpr int kBThreads = 256;       // 64 channels x 4 quarters
 constexpr int kCh = kBThreads / 4;   // channels per workgroup (one tile)
 constexpr int kPad = kBT + 1;        // LDS row stride of the per-channel arrays
 constexpr int kTStride = 2 * kMaxN + 4;  // row of dB then dC values, 16-byte aligned
 
 // dβ/dA for β(A) = (e^(ΔA) - 1)/A, u = ΔA, e = e^u:  Δ² ψ(u) with
-// ψ(u) = (u e^u - e^u + 1)/u² = Σ_m (m+1) u^m / (m+2)!, by its series for
-// |u| < 1/4 (through u^6: truncation below 3e-9 relative); otherwise the same
-// quantity as (Δ e - β)/A (β = (e - 1)/A), whose cancellation is mild there.
-__device__ __forceinline__ float dbeta_dA(float delta, float u, float e, float beta, float rcpa)
+// ψ(u) = (u e^u - e^u + 1)/u² = Σ_m (m+1) u^m / (m+2)!, by its series through
+// u^4 for |u| < 1/8 (truncation below 1e-7 relative); otherwise the same
+// quantity as (Δ e - β)/A (β = (e - 1)/A), whose cancellation there costs at
+// most a factor 2/|u| <= 16 in relative rounding error.
+__device__ __forceinline__ float dbeta_dA(float delta, float del2, float u, float e, float beta,
+                                          float rcpa)
 {
-    float s = 7.f / 40320.f;  // (m+1)/(m+2)! for m = 6 .. 0
-    s = fmaf(s, u, 6.f / 5040.f);
-    s = fmaf(s, u, 5.f / 720.f);
+    float s = 5.f / 720.f;  // (m+1)/(m+2)! for m = 4 .. 0
     s = fmaf(s, u, 4.f / 120.f);
     s = fmaf(s, u, 3.f / 24.f);
     s = fmaf(s, u, 2.f / 6.f);
     s = fmaf(s, u, 0.5f);
     const float closed = fmaf(delta, e, -beta) * rcpa;
-    return fabsf(u) < 0.25f ? delta * delta * s : closed;
+    return fabsf(u) < 0.125f ? del2 * s : closed;
+}
+
+// Input coefficient of the exact ZOH step, β = (e^u - 1)/A = Δ φ1(u) with
+// φ1(u) = (e^u - 1)/u, u = ΔA, taken from w = u log2(e) (the exponent already
+// formed for e = 2^w):  for |u| < 1/2 the series of φ1 through u^7 written in
+// w (coefficients ln2^k/(k+1)!; truncation below 1.1e-8 relative), otherwise
+// (e - 1)/A.
+__device__ __forceinline__ float zoh_coef_w(float w, float delta, float e, float rcpa)
+{
+    constexpr float c1 = 0.693147180559945309f;  // ln 2
+    constexpr float c2 = c1 * c1, c3 = c2 * c1, c4 = c3 * c1, c5 = c4 * c1, c6 = c5 * c1,
+                    c7 = c6 * c1;
+    float phi = c7 / 40320.f;
+    phi = fmaf(phi, w, c6 / 5040.f);
+    phi = fmaf(phi, w, c5 / 720.f);
+    phi = fmaf(phi, w, c4 / 120.f);
+    phi = fmaf(phi, w, c3 / 24.f);
+    phi = fmaf(phi, w, c2 / 6.f);
+    phi = fmaf(phi, w, c1 / 2.f);
+    phi = fmaf(phi, w, 1.f);
+    return fabsf(w) < 0.5f * 1.44269504088896341f ? delta * phi : (e - 1.f) * rcpa;
 }
 
 // Sum over the four lanes of a quad (one channel): two DPP quad permutes.
@@ -110,10 +132,12 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
     }
     for (int e = tid; e < kCh * kBT; e += kBThreads) {
         const int cc = e / kBT, r = e % kBT;
-        const int64_t dd = min(tile * kCh + cc, p.D - 1);
+        const int64_t dd = tile * kCh + cc;
         const int64_t i = (b * p.D + dd) * p.L + t0 + r;
+        // steps past L and channels past D are identity steps with zero
+        // input and zero output gradient: they add nothing to dB, dC
         float del = 0.f, xv = 0.f, dy = 0.f, sg = 0.f;
-        if (r < nt) {
+        if (r < nt && dd < p.D) {
             const float bias = p.dt_bias ? p.dt_bias[dd] : 0.f;
             const float v = E::load(reinterpret_cast<const T *>(p.dt) + i) + bias;
             del = softplus_log2(v * kLog2e) * kLn2;
@@ -144,53 +168,55 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         dAacc[i] = 0.f;
     }
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
-    const float live_ch = active ? 1.f : 0.f;  // channels past D (copies) add nothing
     float dDacc = 0.f, dbacc = 0.f;
 
-    // one forward step of the lane's four states
-    auto fwd = [&](int r, float (&h)[4]) {
+    // one forward step of the lane's four states; e_n = exp(Δ A_n) and the
+    // input coefficient β_n = (e_n - 1)/A_n are returned for the caller
+    auto fwd = [&](int r, float (&h)[4], float (&ev)[4], float (&bv)[4]) {
         const float del = sDel[ch][r], xv = sX[ch][r];
+        const float l = del * kLog2e;
         const float4 B4 = *reinterpret_cast<const float4 *>(&sB[r][4 * q]);
         const float Bv[4] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = hw_exp2(a[i] * del * kLog2e);
-            h[i] = fmaf(e, h[i], zoh_input_coef(a[i], del, e) * Bv[i] * xv);
+            const float w = a[i] * l;
+            ev[i] = hw_exp2(w);
+            bv[i] = zoh_coef_w(w, del, ev[i], rcpa[i]);
+            h[i] = fmaf(ev[i], h[i], bv[i] * (Bv[i] * xv));
         }
     };
 
-    // one half chunk [r0, r0 + kHalf): states from hstart, then backwards
-    auto half = [&](int r0, const float (&hstart)[4]) {
-        float H[kHalf][4];
+    // one quarter chunk [r0, r0 + kQuarter): states, decays and input
+    // coefficients from hstart kept in registers, then walked backwards
+    auto quarter = [&](int r0, const float (&hstart)[4]) {
+        float H[kQuarter][4], Ev[kQuarter][4], Bt[kQuarter][4];
         {
             float h[4] = {hstart[0], hstart[1], hstart[2], hstart[3]};
 #pragma unroll
-            for (int j = 0; j < kHalf; ++j) {
-                fwd(r0 + j, h);
+            for (int j = 0; j < kQuarter; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                fwd(r0 + j, h, Ev[j], Bt[j]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     H[j][i] = h[i];
             }
         }
-        // Reload every step value below instead of keeping the forward pass's
-        // ones alive across the loop (registers hold the states only).
-        __asm__ volatile("" ::: "memory");
 #pragma unroll
-        for (int j = kHalf - 1; j >= 0; --j) {
+        for (int j = kQuarter - 1; j >= 0; --j) {
             __builtin_amdgcn_sched_barrier(0);
             const int r = r0 + j;
             const float del = sDel[ch][r], xv = sX[ch][r], dy = sDY[ch][r];
             const float4 B4 = *reinterpret_cast<const float4 *>(&sB[r][4 * q]);
             const float4 C4 = *reinterpret_cast<const float4 *>(&sC[r][4 * q]);
             const float Bv[4] = {B4.x, B4.y, B4.z, B4.w}, Cv[4] = {C4.x, C4.y, C4.z, C4.w};
+            const float del2 = del * del;
             float dxp = 0.f, ddel = 0.f, yp = 0.f, dBv[4], dCv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float hp = j ? H[j - 1][i] : hstart[i];
                 const float ht = H[j][i];
+                const float e = Ev[j][i], beta = Bt[j][i];
                 const float u = a[i] * del;
-                const float e = hw_exp2(u * kLog2e);
-                const float beta = zoh_input_coef(a[i], del, e);
                 const float lam = fmaf(Cv[i], dy, nu[i]);
                 const float bx = Bv[i] * xv;
                 const float lb = lam * beta;
@@ -199,7 +225,7 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
                 dBv[i] = lb * xv;
                 dxp = fmaf(lb, Bv[i], dxp);
                 ddel = fmaf(le, fmaf(a[i], hp, bx), ddel);
-                dAacc[i] = fmaf(del * le, hp, fmaf(lam * bx, dbeta_dA(del, u, e, beta, rcpa[i]),
+                dAacc[i] = fmaf(del * le, hp, fmaf(lam * bx, dbeta_dA(del, del2, u, e, beta, rcpa[i]),
                                                    dAacc[i]));
                 yp = fmaf(Cv[i], ht, yp);
                 nu[i] = le;
@@ -220,10 +246,8 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
             // 16 channels of entry l (step j + l/32, value l%32) in order.
             const int s2 = j & 1;
             float4 *row = reinterpret_cast<float4 *>(&sT[wave][s2][(tid & 63) >> 2][0]);
-            row[q] = make_float4(dBv[0] * live_ch, dBv[1] * live_ch, dBv[2] * live_ch,
-                                 dBv[3] * live_ch);
-            row[4 + q] = make_float4(dCv[0] * live_ch, dCv[1] * live_ch, dCv[2] * live_ch,
-                                     dCv[3] * live_ch);
+            row[q] = make_float4(dBv[0], dBv[1], dBv[2], dBv[3]);
+            row[4 + q] = make_float4(dCv[0], dCv[1], dCv[2], dCv[3]);
             if (s2 == 0) {
                 __builtin_amdgcn_wave_barrier();
                 const int l = tid & 63, so = l >> 5, kn = l & 31;
@@ -242,18 +266,38 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         }
     };
 
-    // second half first (its start state comes from a first-half pass), then
-    // the first half; the adjoint carries on from one to the other.  A loop,
-    // not two copies, so that nothing of one half stays live into the other.
-#pragma unroll 1
-    for (int hh = 1; hh >= 0; --hh) {
-        float hst[4] = {hin[0], hin[1], hin[2], hin[3]};
-        if (hh == 1) {
+    // Checkpoints: the states at the starts of the chunk's quarters, from one
+    // forward pass over its first three quarters.  Then the quarters from the
+    // last to the first, each recomputed from its checkpoint; the adjoint
+    // carries on from one to the next.  A loop, not four copies, so that
+    // nothing of one quarter stays live into the next.
+    float ck1[4], ck2[4], ck3[4];
+    {
+        float h[4] = {hin[0], hin[1], hin[2], hin[3]}, ev[4], bv[4];
 #pragma unroll
-            for (int j = 0; j < kHalf; ++j)
-                fwd(j, hst);
+        for (int j = 0; j < 3 * kQuarter; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            fwd(j, h, ev, bv);
+            if (j == kQuarter - 1 || j == 2 * kQuarter - 1 || j == 3 * kQuarter - 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (j == kQuarter - 1)
+                        ck1[i] = h[i];
+                    else if (j == 2 * kQuarter - 1)
+                        ck2[i] = h[i];
+                    else
+                        ck3[i] = h[i];
+                }
+            }
         }
-        half(hh * kHalf, hst);
+    }
+#pragma unroll 1
+    for (int qq = 3; qq >= 0; --qq) {
+        float hst[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            hst[i] = qq == 3 ? ck3[i] : qq == 2 ? ck2[i] : qq == 1 ? ck1[i] : hin[i];
+        quarter(qq * kQuarter, hst);
     }
     __syncthreads();
 
