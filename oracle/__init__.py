@@ -8,7 +8,9 @@ this module only builds it with gcc and marshals numpy arrays through ctypes.
 Every function here takes and returns float64 numpy arrays in the layouts
 documented in ``oracle.c``:
   x, dt, z, y [B, D, L];  Bm, Cm [B, L, N];  A [D, N];  dt_bias, Dskip [D];
-  h0, h_last [B, D, N];  conv w [D, K].
+  h0, h_last [B, D, N];  conv w [D, K];
+  Mamba-2 form: x, z, y [B, L, H, P]; dt [B, L, H]; Bm, Cm [B, L, G, N];
+  A, dt_bias, Dskip [H]; h0, h_last [B, H, P, N].
 Parity status: every function is pinned by tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -35,7 +37,11 @@ def compile_oracle(src: str = SOURCE, out: str = LIBRARY) -> str:
 
 
 def build(force: bool = True) -> str:
-    if force or not os.path.exists(LIBRARY):
+    """Compile oracle.c (always with force; else only when the library is
+    missing or older than the source)."""
+    stale = (not os.path.exists(LIBRARY)
+             or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE))
+    if force or stale:
         compile_oracle()
     return LIBRARY
 
@@ -71,6 +77,8 @@ class Oracle:
         lib.oracle_selective_scan_bwd.argtypes = [P] * 20 + [I64] * 4
         lib.oracle_conv1d_update.restype = ctypes.c_int
         lib.oracle_conv1d_update.argtypes = [P] * 5 + [I64] * 3
+        lib.oracle_ssd_scan_fwd.restype = ctypes.c_int
+        lib.oracle_ssd_scan_fwd.argtypes = [P] * 11 + [I64] * 6
         lib.oracle_state_update.restype = ctypes.c_int
         lib.oracle_state_update.argtypes = [P] * 10 + [I64] * 3
         self.lib = lib
@@ -133,6 +141,27 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_selective_scan_bwd rejected its arguments")
         return g
+
+    def ssd_scan(self, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None):
+        """Mamba-2 form (one decay per head, B/C per group of heads).
+        x, z [B,L,H,P]; dt [B,L,H]; Bm, Cm [B,L,G,N]; A, dt_bias, Dskip [H];
+        h0 [B,H,P,N].  Returns (y [B,L,H,P], h_last [B,H,P,N])."""
+        x, dt, A, Bm, Cm = map(_f64, (x, dt, A, Bm, Cm))
+        dt_bias, Dskip, z, h0 = map(_f64, (dt_bias, Dskip, z, h0))
+        Bsz, L, H, P = x.shape
+        G, N = Bm.shape[2], Bm.shape[3]
+        assert dt.shape == (Bsz, L, H) and A.shape == (H,)
+        assert Bm.shape == (Bsz, L, G, N) and Cm.shape == Bm.shape
+        assert z is None or z.shape == x.shape
+        assert h0 is None or h0.shape == (Bsz, H, P, N)
+        y = np.empty(x.shape, dtype=np.float64)
+        h_last = np.empty((Bsz, H, P, N), dtype=np.float64)
+        rc = self.lib.oracle_ssd_scan_fwd(
+            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+            _ptr(h0), _ptr(y), _ptr(h_last), Bsz, L, H, P, G, N)
+        if rc != 0:
+            raise ValueError("oracle_ssd_scan_fwd rejected its arguments")
+        return y, h_last
 
     def selective_scan_reverse(self, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
                                nthreads: int = 1):
@@ -236,3 +265,7 @@ def selective_scan_bwd(*args, **kw):
 
 def conv1d_update(*args, **kw):
     return get().conv1d_update(*args, **kw)
+
+
+def ssd_scan(*args, **kw):
+    return get().ssd_scan(*args, **kw)

@@ -40,6 +40,15 @@
  *    order, the forward states recomputed rather than stored by the caller
  *      ["Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式", §2.2:
  *       intermediate states recomputed in the backward pass].
+ *  - Mamba-2 form ("SSD"): the same selective recurrence with one decay
+ *    value per head (A = a_h times the identity, shared by the head's P
+ *    channels and all N states) and B, C shared by a group of heads, which
+ *    makes the sequence map a structured (semiseparable) matrix that can be
+ *    applied with matrix multiplications
+ *      ["Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式", §4.2:
+ *       Mamba-2 restates the SSM as structured matrix multiplication].
+ *    Written here as the plain recurrence; Δ, ZOH, readout, skip and gate as
+ *    above.
  *
  * Layouts (all row-major, fp64):
  *   x, dt, z, y : [B, D, L]      (L fastest)
@@ -47,6 +56,8 @@
  *   A           : [D, N];  dt_bias, Dskip : [D];  h0, h_last : [B, D, N]
  *   conv w      : [D, K];  conv bias : [D]
  *   decode      : h [B, D, N] in/out, x/dt/z/y [B, D], Bm/Cm [B, N]
+ *   Mamba-2     : x, z, y [B, L, H, P];  dt [B, L, H];  Bm, Cm [B, L, G, N];
+ *                 A, dt_bias, Dskip [H];  h0, h_last [B, H, P, N]
  * NULL for dt_bias / Dskip / z / h0 / h_last / conv bias means "absent"
  * (zero bias, no skip, no gate, zero initial state, state not returned).
  */
@@ -374,5 +385,61 @@ int oracle_state_update(double *h, const double *x, const double *dt, const doub
                         Bm + (size_t)b * N, Cm + (size_t)b * N, Dskip ? Dskip[d] : 0.0,
                         z ? z + c : NULL);
         }
+    return 0;
+}
+
+/* Mamba-2 form: per head h (group g = h / (H/G)), state S[p][n] over the head's
+ * P channels and N states, all decaying with the head's scalar a = A[h]:
+ *   Δ = softplus(dt[b,t,h] + dt_bias[h]),  Abar = exp(Δ a),  bcoef = expm1(Δ a)/a
+ *   S[p][n] <- Abar S[p][n] + bcoef Bm[b,t,g,n] x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] S[p][n] + Dskip[h] x[b,t,h,p]) * SiLU(z[b,t,h,p])
+ * Returns 0, or -1 on bad arguments. */
+int oracle_ssd_scan_fwd(const double *x, const double *dt, const double *dt_bias,
+                        const double *A, const double *Bm, const double *Cm,
+                        const double *Dskip, const double *z, const double *h0, double *y,
+                        double *h_last, int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                        int64_t N)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !y || B < 0 || L < 0 || H < 1 || P < 1 || G < 1 ||
+        N < 1 || H % G != 0)
+        return -1;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(P * N));
+    if (!S)
+        return -1;
+    const int64_t heads_per_group = H / G;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h / heads_per_group;
+            const double a = A[h];
+            const double bias = dt_bias ? dt_bias[h] : 0.0;
+            const double Dv = Dskip ? Dskip[h] : 0.0;
+            for (int64_t i = 0; i < P * N; ++i)
+                S[i] = h0 ? h0[(b * H + h) * P * N + i] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const double delta = oracle_softplus(dt[(b * L + t) * H + h] + bias);
+                double abar, bcoef;
+                oracle_zoh(delta, a, &abar, &bcoef);
+                const double *Bt = Bm + ((b * L + t) * G + g) * N;
+                const double *Ct = Cm + ((b * L + t) * G + g) * N;
+                const int64_t row = ((b * L + t) * H + h) * P;
+                for (int64_t p = 0; p < P; ++p) {
+                    const double xv = x[row + p];
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        S[p * N + n] = abar * S[p * N + n] + bcoef * Bt[n] * xv;
+                        acc += Ct[n] * S[p * N + n];
+                    }
+                    acc += Dv * xv;
+                    if (z)
+                        acc *= oracle_silu(z[row + p]);
+                    y[row + p] = acc;
+                }
+            }
+            if (h_last)
+                for (int64_t i = 0; i < P * N; ++i)
+                    h_last[(b * H + h) * P * N + i] = S[i];
+        }
+    }
+    free(S);
     return 0;
 }

@@ -15,7 +15,11 @@ mismatch.  They check the oracle against things other than itself:
   * special cases (B = 0, C = 0, step -> infinity, A = 0, saturated gate),
     hand expansions for L <= 3, and a hand-derived rational worked example
     (tests/golden/zoh_ln2_worked_example.txt),
-  * numpy.convolve for the causal depthwise conv1d, scipy.special.expit for SiLU.
+  * numpy.convolve for the causal depthwise conv1d, scipy.special.expit for SiLU,
+  * the Mamba-2 form against its structured-matrix (quadratic) form built in
+    numpy, and against the selective scan it reduces to when every state of a
+    channel shares its head's decay ("Mamba状态空间模型深度解析：挑战Transformer的
+    下一代序列建模范式", §4.2).
 ``tests/test_oracle_mutants.py`` plants mistakes in copies of oracle.c and
 checks that at least one pin fails for each of them.
 """
@@ -476,6 +480,73 @@ def pin_threads(orc):
     assert np.array_equal(y1, y4) and np.array_equal(h1, h4), "thread count changed result"
 
 
-ALL_PINS = [pin_backward_fd, pin_reverse, pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
+def _ssd_problem(rng, Bsz, L, H, P, G, N, zero_head=True):
+    x = rng.normal(size=(Bsz, L, H, P))
+    z = rng.normal(size=(Bsz, L, H, P))
+    dt = rng.normal(-0.5, 0.8, size=(Bsz, L, H))
+    A = -rng.uniform(0.2, 3.0, size=H)
+    if zero_head:
+        A[1] = 0.0  # no decay: the ZOH coefficient's limit Δ
+    Bm, Cm = rng.normal(size=(Bsz, L, G, N)), rng.normal(size=(Bsz, L, G, N))
+    bias, Dv = rng.normal(size=H), rng.normal(size=H)
+    h0 = rng.normal(size=(Bsz, H, P, N))
+    return x, dt, A, Bm, Cm, bias, Dv, z, h0
+
+
+def pin_ssd_matrix_form(orc):
+    """Mamba-2 form against its structured-matrix (quadratic) form, built here
+    in numpy: y_t = sum_{s<=t} (C_t . B_s) exp(sum_{k=s+1..t} Δ_k a) β_s x_s
+    + C_t . exp(sum_{k<=t} Δ_k a) h0 + D x_t, gated; β = expm1(Δa)/a (Δ at a = 0)
+    ("Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式", §4.2:
+    the SSM as a structured matrix multiplication)."""
+    rng = np.random.default_rng(41)
+    Bsz, L, H, P, G, N = 2, 7, 4, 3, 2, 5
+    x, dt, A, Bm, Cm, bias, Dv, z, h0 = _ssd_problem(rng, Bsz, L, H, P, G, N)
+    y, hl = orc.ssd_scan(x, dt, A, Bm, Cm, bias, Dv, z, h0)
+    for b in range(Bsz):
+        for h in range(H):
+            g = h // (H // G)
+            delta = np.log1p(np.exp(dt[b, :, h] + bias[h]))
+            ell = delta * A[h]
+            beta = delta if A[h] == 0.0 else np.expm1(ell) / A[h]
+            cum = np.cumsum(ell)  # sum_{k<=t}
+            M = np.zeros((L, L))
+            for t in range(L):
+                for s_ in range(t + 1):
+                    M[t, s_] = (Cm[b, t, g] @ Bm[b, s_, g]) * np.exp(cum[t] - cum[s_]) * beta[s_]
+            yy = M @ x[b, :, h, :]                                   # [L, P]
+            yy += np.exp(cum)[:, None] * (Cm[b, :, g] @ h0[b, h].T)  # carried state
+            yy += Dv[h] * x[b, :, h, :]
+            yy *= z[b, :, h, :] * expit(z[b, :, h, :])
+            _close(y[b, :, h, :], yy, 1e-12, 1e-12, f"ssd matrix form y b={b} h={h}")
+            hh = np.exp(cum[-1]) * h0[b, h]
+            for s_ in range(L):
+                hh = hh + np.exp(cum[-1] - cum[s_]) * beta[s_] * np.outer(x[b, s_, h], Bm[b, s_, g])
+            _close(hl[b, h], hh, 1e-12, 1e-12, f"ssd matrix form h_last b={b} h={h}")
+
+
+def pin_ssd_reduces_to_scan(orc):
+    """With one decay per head, the Mamba-2 form is the selective scan of the
+    head's channels with A[d, n] = a_h for every state n and the group's B, C:
+    G = 1 is one scan over all H*P channels; G = H is one scan per head."""
+    rng = np.random.default_rng(43)
+    Bsz, L, H, P, N = 2, 9, 4, 3, 6
+    for G in (1, H):
+        x, dt, A, Bm, Cm, bias, Dv, z, h0 = _ssd_problem(rng, Bsz, L, H, P, G, N)
+        y, hl = orc.ssd_scan(x, dt, A, Bm, Cm, bias, Dv, z, h0)
+        for h in range(H):
+            g = h // (H // G)
+            x1 = np.ascontiguousarray(x[:, :, h, :].transpose(0, 2, 1))      # [B, P, L]
+            z1 = np.ascontiguousarray(z[:, :, h, :].transpose(0, 2, 1))
+            dt1 = np.repeat(dt[:, None, :, h], P, axis=1)                   # [B, P, L]
+            A1 = np.full((P, N), A[h])
+            y1, h1 = orc.selective_scan(x1, dt1, A1, np.ascontiguousarray(Bm[:, :, g]),
+                                        np.ascontiguousarray(Cm[:, :, g]), np.full(P, bias[h]),
+                                        np.full(P, Dv[h]), z1, np.ascontiguousarray(h0[:, h]))
+            _close(y[:, :, h, :], y1.transpose(0, 2, 1), 1e-12, 1e-12, f"ssd vs scan y G={G} h={h}")
+            _close(hl[:, h], h1, 1e-12, 1e-12, f"ssd vs scan h_last G={G} h={h}")
+
+
+ALL_PINS = [pin_ssd_matrix_form, pin_ssd_reduces_to_scan, pin_backward_fd, pin_reverse, pin_conv_update, pin_softplus, pin_silu, pin_zoh_van_loan, pin_scan_single_step_van_loan, pin_ode,
             pin_dc_gain, pin_lti_convolution, pin_chunked_carry, pin_special_cases,
             pin_hand_expansions, pin_golden_ln2, pin_conv, pin_decode_step, pin_threads]

@@ -46,6 +46,19 @@ MUTANTS = [
      "dCt[n] += dy * hist[t * N + n];"),
     ("conv_window_not_moved", "                st[k] = st[k + 1];", "                st[k] = st[k];"),
     ("conv_update_new_input_tap", "acc += w[d * K + K - 1] * x[c];", "acc += w[d * K] * x[c];"),
+    ("ssd_group_index", "const int64_t g = h / heads_per_group;",
+     "const int64_t g = h % G;"),
+    ("ssd_readout_before_update",
+     "                        S[p * N + n] = abar * S[p * N + n] + bcoef * Bt[n] * xv;\n"
+     "                        acc += Ct[n] * S[p * N + n];",
+     "                        acc += Ct[n] * S[p * N + n];\n"
+     "                        S[p * N + n] = abar * S[p * N + n] + bcoef * Bt[n] * xv;"),
+    ("ssd_dt_per_channel", "oracle_softplus(dt[(b * L + t) * H + h] + bias)",
+     "oracle_softplus(dt[(b * L + t) * H] + bias)"),
+    ("ssd_h0_transposed", "S[i] = h0 ? h0[(b * H + h) * P * N + i] : 0.0;",
+     "S[i] = h0 ? h0[(b * H + h) * P * N + (i % N) * P + i / N] : 0.0;"),
+    ("ssd_skip_head_index", "const double Dv = Dskip ? Dskip[h] : 0.0;",
+     "const double Dv = Dskip ? Dskip[0] : 0.0;"),
 ]
 
 
