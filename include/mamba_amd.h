@@ -9,7 +9,8 @@
  * and two that join the front end to the scan:
  *   mamba_conv1d_selective_scan_fwd  conv1d + SiLU fused into the scan
  *   mamba_conv1d_update              single-token conv step with its state
- * the scan's backward pass (mamba_selective_scan_bwd),
+ * the scan's backward pass (mamba_selective_scan_bwd), the Mamba-2 form of
+ * the scan on the matrix cores (mamba_ssd_scan_fwd),
  * plus workspace sizing and status helpers.
  *
  * Conventions shared by every entry point
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 4
+#define MAMBA_AMD_ABI_VERSION 5
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
@@ -247,11 +248,44 @@ mamba_status mamba_selective_scan_bwd(
     int64_t D, int64_t L, int64_t N, mamba_dtype io, void *stream);
 
 /*
+ * Mamba-2 form of the scan ("SSD"): one decay value per head, shared by the
+ * head's P channels and all N states, and B, C shared by a group of H/G heads.
+ * The sequence map of a head is then a structured lower-triangular matrix and
+ * is applied with matrix multiplications on the matrix cores
+ * ("Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式", §4.2:
+ * Mamba-2 restates the SSM as structured matrix multiplication to use the
+ * GPU's matrix units).  Per (b, h, p) it computes the same recurrence as
+ * mamba_selective_scan_fwd with A[d, n] = A[h] for every state n:
+ *   Δ = softplus(dt[b,t,h] + dt_bias[h]),  Abar = exp(Δ A[h]),
+ *   Bbar_n = (exp(Δ A[h]) - 1)/A[h] B[b,t,g,n]  (Δ B at A[h] = 0),  g = h / (H/G)
+ *   h[p][n] <- Abar h[p][n] + Bbar_n x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n C[b,t,g,n] h[p][n] + Dskip[h] x[b,t,h,p]) * SiLU(z[b,t,h,p])
+ *   x, z, y : [B, L, H, P] bf16 (io must be MAMBA_BF16), 16-byte aligned
+ *   dt      : [B, L, H] bf16
+ *   Bm, Cm  : [B, L, G, N] bf16, 16-byte aligned
+ *   A       : [H] float;  dt_bias, Dskip : [H] float or NULL (= 0)
+ *   z       : or NULL (= no gate)
+ *   h0      : [B, H, P, N] float, 16-byte aligned, or NULL (= zeros)
+ *   h_last  : [B, H, P, N] float, 16-byte aligned, or NULL (= not returned)
+ * Supported: P = 64, N in {16, 32, 64, 128}, H a multiple of G; anything else
+ * returns MAMBA_ERR_UNSUPPORTED (P, N, io) or MAMBA_ERR_SHAPE (G).  Needs no
+ * workspace.  Products run as bf16 matrix operations with fp32 accumulation;
+ * the operands that are not inputs (the scaled chunk matrix, the state, the
+ * scaled x) are split into two bf16 parts, so their rounding stays near 1e-5
+ * relative.  With L = 0, h_last = h0 (or zeros).
+ */
+mamba_status mamba_ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias,
+                                const float *A, const void *Bm, const void *Cm,
+                                const float *Dskip, const void *z, const float *h0, void *y,
+                                float *h_last, int64_t B, int64_t L, int64_t H, int64_t P,
+                                int64_t G, int64_t N, mamba_dtype io, void *stream);
+
+/*
  * Profiling hook.  When both are non-NULL hipEvent_t handles (passed as
  * void*), later calls made from this host thread record `start` right before
  * and `stop` right after the main scan kernel of mamba_selective_scan_fwd (and
- * its variants), or the chunk-gradient kernel of mamba_selective_scan_bwd, on
- * the call's stream.  Pass NULL, NULL to turn it off.
+ * its variants), the chunk-gradient kernel of mamba_selective_scan_bwd, or the
+ * kernel of mamba_ssd_scan_fwd, on the call's stream.  Pass NULL, NULL to turn it off.
  */
 void mamba_set_scan_timing_events(void *start, void *stop);
 

@@ -18,6 +18,8 @@ Entry points (same names as the C ABI, without the ``mamba_`` prefix):
   selective_scan_bwd(x, dt, A, Bm, Cm, dout, dt_bias=None, Dskip=None, z=None, h0=None,
                      dh_last=None, workspace=None)
   selective_scan_bwd_workspace_size(B, D, L, N, dtype)
+  ssd_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+               return_last_state=False, out=None, h_last=None)
 """
 from __future__ import annotations
 
@@ -42,7 +44,8 @@ EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_selective_state_update", "mamba_selective_scan_fwd_ex",
             "mamba_conv1d_selective_scan_fwd",
             "mamba_conv1d_update", "mamba_set_scan_timing_events",
-            "mamba_selective_scan_bwd_workspace_size", "mamba_selective_scan_bwd"]
+            "mamba_selective_scan_bwd_workspace_size", "mamba_selective_scan_bwd",
+            "mamba_ssd_scan_fwd"]
 
 _lib = None
 
@@ -87,6 +90,8 @@ def load_library(path: str = LIBRARY):
     lib.mamba_selective_scan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I32]
     lib.mamba_selective_scan_bwd.restype = I32
     lib.mamba_selective_scan_bwd.argtypes = [P] * 21 + [SZ, I64, I64, I64, I64, I32, P]
+    lib.mamba_ssd_scan_fwd.restype = I32
+    lib.mamba_ssd_scan_fwd.argtypes = [P] * 11 + [I64] * 6 + [I32, P]
     lib.mamba_set_scan_timing_events.restype = None
     lib.mamba_set_scan_timing_events.argtypes = [P, P]
     _lib = lib
@@ -365,6 +370,41 @@ def selective_scan_bwd(x, dt, A, Bm, Cm, dout, dt_bias=None, Dskip=None, z=None,
         _ptr(g["dh0"]), _ptr(workspace), workspace.numel(), B, D, L, N, io, _stream(dev))
     _raise(st, "mamba_selective_scan_bwd")
     return g
+
+
+def ssd_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+                 return_last_state=False, out=None, h_last=None):
+    """Mamba-2 form of the scan (one decay per head, B/C per group of heads) on
+    the matrix cores.  x, z [B,L,H,P], dt [B,L,H], Bm, Cm [B,L,G,N] bf16;
+    A, dt_bias, Dskip [H] f32; h0 [B,H,P,N] f32.  Returns y [B,L,H,P] bf16,
+    and h_last [B,H,P,N] f32 if return_last_state."""
+    torch = _torch()
+    lib = load_library()
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev, io_t = x.device, x.dtype
+    _check(x, "x", (B, L, H, P), io_t, dev)
+    _check(dt, "dt", (B, L, H), io_t, dev)
+    _check(z, "z", (B, L, H, P), io_t, dev, optional=True)
+    _check(Bm, "Bm", (B, L, G, N), io_t, dev)
+    _check(Cm, "Cm", (B, L, G, N), io_t, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (H,), torch.float32, dev, optional=True)
+    _check(h0, "h0", (B, H, P, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (B, L, H, P), io_t, dev)
+    if return_last_state and h_last is None:
+        h_last = torch.empty((B, H, P, N), dtype=torch.float32, device=dev)
+    _check(h_last, "h_last", (B, H, P, N), torch.float32, dev, optional=True)
+    st = lib.mamba_ssd_scan_fwd(
+        _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+        _ptr(h0), _ptr(out), _ptr(h_last), B, L, H, P, G, N, _io_dtype(x), _stream(dev))
+    _raise(st, "mamba_ssd_scan_fwd")
+    if return_last_state:
+        return out, h_last
+    return out
 
 
 def set_scan_timing_events_raw(start=None, stop=None):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libmamba_amd.so")
-SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d_silu.hip", "state_update.hip"]
+SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip", "conv1d_silu.hip", "state_update.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled on purpose: the kernels are written for

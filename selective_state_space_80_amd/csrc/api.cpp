@@ -83,7 +83,9 @@ const char *mamba_status_string(int status)
     case MAMBA_ERR_SHAPE: return "MAMBA_ERR_SHAPE: negative size or problem too large";
     case MAMBA_ERR_DTYPE: return "MAMBA_ERR_DTYPE: dtype must be MAMBA_F32 or MAMBA_BF16";
     case MAMBA_ERR_UNSUPPORTED:
-        return "MAMBA_ERR_UNSUPPORTED: N must be 1..16, K 1..8 (1..4 when fused into the scan)";
+        return "MAMBA_ERR_UNSUPPORTED: a size, type or flag this entry point does not take "
+               "(scan: N 1..16; conv: K 1..8, 1..4 fused; Mamba-2 form: bf16, P 64, "
+               "N 16/32/64/128)";
     case MAMBA_ERR_ALIGN: return "MAMBA_ERR_ALIGN: pointer not aligned to its element size";
     case MAMBA_ERR_ALIAS: return "MAMBA_ERR_ALIAS: an output overlaps an input";
     case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE: workspace missing, misaligned or too small";
@@ -517,6 +519,67 @@ mamba_status mamba_selective_scan_bwd(
     a.ev_start = g_ev_start;
     a.ev_stop = g_ev_stop;
     return launched(mamba::launch_selective_scan_bwd(a, (hipStream_t)stream));
+}
+
+mamba_status mamba_ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias,
+                                const float *A, const void *Bm, const void *Cm,
+                                const float *Dskip, const void *z, const float *h0, void *y,
+                                float *h_last, int64_t B, int64_t L, int64_t H, int64_t P,
+                                int64_t G, int64_t N, mamba_dtype io, void *stream)
+{
+    if (!valid_dtype(io))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, L, H) || P < 0 || N < 0 || G < 0 || !sizes_ok(B * L, H, P))
+        return MAMBA_ERR_SHAPE;
+    if (io != MAMBA_BF16 || P != mamba::kSsdHeadDim || !(N == 16 || N == 32 || N == 64 || N == 128))
+        return MAMBA_ERR_UNSUPPORTED;
+    if (G < 1 || H % G != 0 || B * H >= (int64_t(1) << 31))
+        return MAMBA_ERR_SHAPE;
+    if (B * H == 0)
+        return MAMBA_OK;
+    if (!A || (L > 0 && (!x || !dt || !Bm || !Cm || !y)))
+        return MAMBA_ERR_NULL;
+    if (L == 0 && !h_last)
+        return MAMBA_OK;
+    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(Bm, 16) ||
+        !aligned(Cm, 16) || !aligned(dt, 2) || !aligned(A, 4) || !aligned(dt_bias, 4) ||
+        !aligned(Dskip, 4) || !aligned(h0, 16) || !aligned(h_last, 16))
+        return MAMBA_ERR_ALIGN;
+    const size_t nx = (size_t)(B * L * H * P) * 2, nbc = (size_t)(B * L * G * N) * 2,
+                 ns = (size_t)(B * H * P * N) * 4;
+    const Range ry = rng(y, L > 0 ? nx : 0), rh = rng(h_last, h_last ? ns : 0);
+    const Range ins[] = {rng(x, L > 0 ? nx : 0), rng(dt, (size_t)(B * L * H) * 2),
+                         rng(z, z && L > 0 ? nx : 0), rng(Bm, nbc), rng(Cm, nbc),
+                         rng(A, (size_t)H * 4), rng(dt_bias, dt_bias ? (size_t)H * 4 : 0),
+                         rng(Dskip, Dskip ? (size_t)H * 4 : 0), rng(h0, h0 ? ns : 0)};
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rh, r))
+            return MAMBA_ERR_ALIAS;
+    if (overlap(ry, rh))
+        return MAMBA_ERR_ALIAS;
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::SsdArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.Bm = Bm;
+    a.Cm = Cm;
+    a.z = z;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.Dskip = Dskip;
+    a.h0 = h0;
+    a.y = y;
+    a.h_last = h_last;
+    a.B = B;
+    a.L = L;
+    a.H = H;
+    a.G = G;
+    a.N = (int)N;
+    a.ev_start = g_ev_start;
+    a.ev_stop = g_ev_stop;
+    return launched(mamba::launch_ssd_fwd(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

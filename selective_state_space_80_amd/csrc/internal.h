@@ -83,6 +83,19 @@ struct BwdArgsHost {
 };
 hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s);
 
+// Mamba-2 form (ssd_fwd.hip): one decay per head, B/C per group of heads.
+constexpr int kSsdHeadDim = 64;  // channels per head (P)
+struct SsdArgs {
+    const void *x, *dt, *Bm, *Cm, *z;  // bf16: x, z, y [B, L, H, P]; dt [B, L, H]; B, C [B, L, G, N]
+    const float *dt_bias, *A, *Dskip, *h0;  // [H], [H], [H], [B, H, P, N]
+    void *y;
+    float *h_last;  // [B, H, P, N] or NULL
+    int64_t B, L, H, G;
+    int N;
+    hipEvent_t ev_start, ev_stop;  // optional timing of the kernel
+};
+hipError_t launch_ssd_fwd(const SsdArgs &a, hipStream_t s);
+
 struct ConvArgs {
     const void *x;
     const float *w, *bias;

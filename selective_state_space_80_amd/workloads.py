@@ -16,6 +16,10 @@ Recipe (every distribution is drawn with ``numpy.random.default_rng``):
                  depthwise conv, whose weights are conv_w ~ N(0, 0.5) [D, 4]
   decode config: h0 ~ N(0, 1) [B, D, N] fp32; every step draws fresh
                  x, z, dt [B, D] and Bm, Cm [B, N] from its own stream.
+  Mamba-2 form:  x, z ~ N(0, 1) [B, L, H, P]; dt ~ N(0, 0.25) [B, L, H];
+                 u_h log-uniform in [1e-3, 1e-1] and dt_bias_h = log(expm1(u_h))
+                 per head; A_h ~ -U(1, 16) per head; Bm, Cm ~ N(0, 1)
+                 [B, L, G, N]; Dskip_h = 1 (draw order: x, z, dt, u, A, Bm, Cm).
 Draw order: x (or x_raw), z, dt, u, Bm, Cm, conv_w.  bf16 tensors are drawn in
 fp32 and rounded to bf16 (round-to-nearest-even); the arrays returned here
 hold those rounded values in float32, so they convert to bf16 exactly.
@@ -53,6 +57,27 @@ class DecodeWorkload:
     steps: int
     check_every: int
     seed: int = 0
+
+
+@dataclass(frozen=True)
+class SsdWorkload:
+    name: str
+    B: int
+    L: int
+    H: int
+    P: int
+    G: int
+    N: int
+    seed: int = 0
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.L * self.H * self.P
+
+
+# The Mamba-2 form at the 2.8B-layer scale of the bf16 scan workload:
+# d_inner 5120 = 80 heads of 64 channels, one B/C group, state size 64.
+SSD_WORKLOAD = SsdWorkload("ssd_b8_l2048_h80_p64_g1_n64_bf16", 8, 2048, 80, 64, 1, 64, 1005)
 
 
 WORKLOADS = {
@@ -143,3 +168,25 @@ def decode_step_inputs(wl: DecodeWorkload, step: int, seed: int | None = None):
     if wl.io == "bf16":
         out = {k: round_bf16(v) for k, v in out.items()}
     return out
+
+
+def make_ssd_inputs(B: int, L: int, H: int, P: int, G: int, N: int, seed: int = 0):
+    """Draw one Mamba-2-form problem (bf16 I/O).  Returns float32 numpy arrays
+    holding bf16-exact values: x, z [B,L,H,P]; dt [B,L,H]; Bm, Cm [B,L,G,N];
+    and fp32 per-head dt_bias, A, Dskip [H]."""
+    rng = np.random.default_rng(seed)
+    out = {"x": round_bf16(_normal(rng, (B, L, H, P))),
+           "z": round_bf16(_normal(rng, (B, L, H, P))),
+           "dt": round_bf16(_normal(rng, (B, L, H), 0.25))}
+    u = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=H))
+    out["dt_bias"] = np.log(np.expm1(u)).astype(np.float32)
+    out["A"] = (-rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    out["Bm"] = round_bf16(_normal(rng, (B, L, G, N)))
+    out["Cm"] = round_bf16(_normal(rng, (B, L, G, N)))
+    out["Dskip"] = np.ones(H, dtype=np.float32)
+    return out
+
+
+def ssd_inputs(wl: SsdWorkload, seed: int | None = None):
+    return make_ssd_inputs(wl.B, wl.L, wl.H, wl.P, wl.G, wl.N,
+                           wl.seed if seed is None else seed)

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 4
+    assert lib.mamba_abi_version() == 5
     for st in range(10):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -241,6 +241,33 @@ def test_bwd_workspace_size(lib):
     assert small > lib.mamba_selective_scan_fwd_workspace_size(1, 64, 256, 16, F32)
 
 
+def ssd(lib, **kw):
+    a = dict(x=P(1), dt=P(2), dt_bias=P(3), A=P(4), Bm=P(5), Cm=P(6), Dskip=P(7), z=P(8),
+             h0=P(9), y=P(10), h_last=P(11), B=2, L=256, H=8, Pd=64, G=2, N=64, io=BF16)
+    a.update(kw)
+    return lib.mamba_ssd_scan_fwd(a["x"], a["dt"], a["dt_bias"], a["A"], a["Bm"], a["Cm"],
+                                  a["Dskip"], a["z"], a["h0"], a["y"], a["h_last"], a["B"],
+                                  a["L"], a["H"], a["Pd"], a["G"], a["N"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(io=9), EDTYPE), (dict(io=F32), EUNSUP), (dict(Pd=32), EUNSUP), (dict(N=48), EUNSUP),
+    (dict(N=256), EUNSUP), (dict(G=3), ESHAPE), (dict(G=0), ESHAPE), (dict(L=-1), ESHAPE),
+    (dict(x=None), ENULL), (dict(A=None), ENULL), (dict(Cm=None), ENULL), (dict(y=None), ENULL),
+    (dict(x=ctypes.c_void_p(0x10000000000 + 1 * 0x100000000 + 8)), EALIGN),
+    (dict(h_last=ctypes.c_void_p(0x10000000000 + 11 * 0x100000000 + 4)), EALIGN),
+    (dict(dt=ctypes.c_void_p(0x10000000000 + 2 * 0x100000000 + 1)), EALIGN),
+    (dict(y=P(1)), EALIAS), (dict(h_last=P(9)), EALIAS), (dict(h_last=P(10)), EALIAS),
+])
+def test_ssd_rejects(lib, kw, want):
+    assert ssd(lib, **kw) == want
+
+
+def test_ssd_empty_is_ok(lib):
+    assert ssd(lib, B=0) == OK and ssd(lib, H=0, G=1) == OK
+    assert ssd(lib, L=0, h_last=None, x=None, y=None) == OK
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="valid fake pointers must never reach a GPU")
 def test_valid_arguments_without_gpu_report_device(lib):
     assert fused(lib) == EDEV
@@ -252,6 +279,8 @@ def test_valid_arguments_without_gpu_report_device(lib):
     assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
                                             P(9), P(10), 4, 64, 16, F32, None) == EDEV
     assert bwd(lib) == EDEV
+    assert ssd(lib) == EDEV
+    assert ssd(lib, L=0, x=None, y=None, dt=None, Bm=None, Cm=None) == EDEV  # h_last = h0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
