@@ -375,6 +375,69 @@ def run_bwd(args, torch, mamba, W):
                         "chunk_grad_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
 
 
+def run_ssd(args, torch, mamba, W):
+    """The Mamba-2 form of the scan (one decay per head, B/C per group) on the
+    matrix cores: B=8, L=2048, 80 heads of 64 channels (d_inner 5120), G=1,
+    N=64, bf16 I/O."""
+    wl = W.SSD_WORKLOAD
+    p = W.ssd_inputs(wl)
+    dev = torch.device("cuda:0")
+    T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    bf = torch.bfloat16
+    x, z, dt = T(p["x"], bf), T(p["z"], bf), T(p["dt"], bf)
+    Bm, Cm = T(p["Bm"], bf), T(p["Cm"], bf)
+    A, bias, Dk = T(p["A"]), T(p["dt_bias"]), T(p["Dskip"])
+    y = torch.empty_like(x)
+
+    def step(pair=None):
+        if pair is not None:
+            mamba.set_scan_timing_events_raw(pair[0], pair[1])
+        mamba.ssd_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mamba.set_scan_timing_events_raw(None, None)
+    k_all = [ev.elapsed_ms(a, b) for a, b in pairs]
+    k_ms = float(np.mean(k_all))
+    ms_step = elapsed / args.steps * 1e3
+    elems = wl.elems
+    # algorithmic bytes: x, z read and y written (bf16), dt per (b, t, h), B and C
+    # per (b, t, g), A / dt_bias / D per head
+    nbytes = (3 * elems * 2 + wl.B * wl.L * wl.H * 2 + 2 * wl.B * wl.L * wl.G * wl.N * 2
+              + 3 * wl.H * 4)
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    # matrix work of the chunked form per 64-step chunk and head: the causal
+    # C B^T and M x (Q(Q+1)/2 entries each), the chunk state and C H
+    Q = 64
+    chunks = wl.B * wl.H * ((wl.L + Q - 1) // Q)
+    flops = chunks * (2 * (Q * (Q + 1) // 2) * (wl.N + wl.P) + 2 * 2 * Q * wl.N * wl.P)
+    return {"metric": "Mamba-2 form scan Gelem/s (B*L*H*P) and HBM GB/s as % of MI355X peak",
+            "value": round(elems / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16-io/f32", "data": "synthetic",
+            "config": {"workload": wl.name, "batch": wl.B, "seq_len": wl.L, "heads": wl.H,
+                       "head_dim": wl.P, "groups": wl.G, "d_state": wl.N,
+                       "step": "ssd_scan_fwd (chunked Mamba-2 form, bf16 MFMA)"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "ssd_fwd_kernel<64>", "kernel_ms": round(k_ms, 4),
+                         "algorithmic_bytes": nbytes},
+            "mfma": {"achieved_tflops": round(flops / (k_ms * 1e-3) / 1e12, 2),
+                     "peak_tflops": 2500.0, "frac": round(flops / (k_ms * 1e-3) / 2.5e15, 4),
+                     "algorithmic_flops": flops},
+            "kernels": {"ssd_ms": quantiles(k_all),
+                        "ssd_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
+
+
 def run_decode(args, torch, mamba, W):
     wl = W.WORKLOADS[4]
     dev = torch.device("cuda:0")
@@ -425,7 +488,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="block",
                     choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode",
-                             "bidir_bf16_l2048", "bwd"])
+                             "bidir_bf16_l2048", "bwd", "ssd"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--unfused", action="store_true",
                     help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
@@ -464,6 +527,8 @@ def main():
         out = run_scan(args, torch, mamba, W, 2, bidir=True)
     elif args.workload == "bwd":
         out = run_bwd(args, torch, mamba, W)
+    elif args.workload == "ssd":
+        out = run_ssd(args, torch, mamba, W)
     else:
         out = run_decode(args, torch, mamba, W)
     print(json.dumps(out), flush=True)

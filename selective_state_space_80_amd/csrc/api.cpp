@@ -535,6 +535,8 @@ mamba_status mamba_ssd_scan_fwd(const void *x, const void *dt, const float *dt_b
         return MAMBA_ERR_UNSUPPORTED;
     if (G < 1 || H % G != 0 || B * H >= (int64_t(1) << 31))
         return MAMBA_ERR_SHAPE;
+    if (H * P * 64 >= (int64_t(1) << 31) || G * N * 64 >= (int64_t(1) << 31))
+        return MAMBA_ERR_SHAPE;  // 32-bit offsets within a 64-step chunk
     if (B * H == 0)
         return MAMBA_OK;
     if (!A || (L > 0 && (!x || !dt || !Bm || !Cm || !y)))

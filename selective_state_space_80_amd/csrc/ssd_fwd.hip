@@ -52,19 +52,23 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
-// v ≈ hi + lo, both bf16 (round to nearest even)
-__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo)
+// two floats -> a packed bf16 pair (a in the low half), round to nearest even
+// (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt2(float a, float b)
 {
-    hi = f32_to_bf16_bits(v);
-    lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ float bf16_at(const uint4 &v, int j)
+// (a, b) ≈ hi + lo, each a packed bf16 pair: hi the rounded values, lo the
+// rounded remainders
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo)
 {
-    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-    return bf16_bits_to_f32((j & 1) ? (w >> 16) : (w & 0xffffu));
+    hi = cvt2(a, b);
+    lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 struct SsdKArgs {
@@ -81,23 +85,25 @@ __device__ constexpr int kTB[kTiles] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __device__ constexpr int kSB[kTiles] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 template <int N>
-__global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
+__global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
 {
-    constexpr int NP = N + 8;  // row of an n-contiguous bf16 array
+    constexpr int NP = N + 8;           // row of an n-contiguous bf16 array
     constexpr int NB = N / 16;
-    constexpr size_t kBRegion = (size_t)kQ * NP * 2 + (size_t)N * kQP * 2;
-    constexpr size_t kYRegion = (size_t)kQ * kYP * 4;
-    constexpr size_t kRegion = kBRegion > kYRegion ? kBRegion : kYRegion;
-    __shared__ __align__(16) uint16_t sC[kQ * NP];          // C[t][n]
-    __shared__ __align__(16) unsigned char sR[kRegion];     // B[s][n], B^T[n][s]; later Y
-    __shared__ __align__(16) uint16_t sXt[kP * kQP];        // x^T[p][s]
-    __shared__ __align__(16) uint16_t sXw[2][kP * kQP];     // (w x)^T[p][s], hi and lo
+    constexpr int kPer = (kQ * N / 8 + kT - 1) / kT;  // 16-byte B, C pieces per thread
+    constexpr int kBtPer = kQ * N / kT;               // B^T values per thread (N/4)
+    __shared__ __align__(16) uint16_t sC[kQ * NP];         // C[t][n]
+    __shared__ __align__(16) uint16_t sB[kQ * NP];         // B[s][n]
+    __shared__ __align__(16) uint16_t sBt[N * kQP];        // B^T[n][s]
+    __shared__ __align__(16) uint16_t sX[kQ * (kP + 8)];   // x[s][p]
+    __shared__ __align__(16) uint16_t sXt[kP * kQP];       // x^T[p][s]
+    // (w x)^T[p][s] hi and lo; once the chunk's products are done, the fp32
+    // output tile Y[t][p] (row kYP) takes its place
+    __shared__ __align__(16) uint16_t sXw[2][kP * kQP];
+    float *sY = reinterpret_cast<float *>(&sXw[0][0]);
+    static_assert(kQ * kYP * 4 <= 2 * kP * kQP * 2, "output tile fits the w x buffer");
     __shared__ __align__(16) uint16_t sM[kTiles][2][64 * 4];  // M tiles, hi and lo, A layout
     __shared__ float sLam[kQ], sBeta[kQ], sW[kQ], sEL[kQ];
     __shared__ float sDecay;
-    uint16_t *sB = reinterpret_cast<uint16_t *>(sR);
-    uint16_t *sBt = sB + kQ * NP;
-    float *sY = reinterpret_cast<float *>(sR);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -108,6 +114,7 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.f;
     const float Dv = p.Dskip ? p.Dskip[h] : 0.f;
     const int pcol = 16 * w + l16;  // this lane's channel in the S, H and Y tiles
+    const int64_t tstride = p.H * kP;  // x, z, y: elements between consecutive steps
 
     // Hs[nb][i] = H[n = 16 nb + 4 g4 + i][p = pcol]
     float Hs[NB][4];
@@ -124,46 +131,77 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
         }
     }
 
+    // Global loads of chunk c+1 are issued while chunk c is computed: per
+    // thread, B and C rows as 16-byte pieces e = tid + k kT, and x and z as the
+    // two 16-byte pieces of step xr, channels xc .. xc+15 (the step and
+    // channels this thread gates and stores); wave 0 lane t: dt of step t.
+    // Steps past L load nothing and stage zeros.  Offsets within a chunk are
+    // 32-bit (the entry point bounds H P kQ below 2^31).
+    constexpr int kXP = kP + 8;  // row of the staged x[s][p]
+    uint4 pB[kPer], pC[kPer], pX[2], pZ[2];
+    uint32_t pdt = 0;
+    const int btn = tid % N, bts = (tid / N) * kBtPer;  // this thread's B^T column and steps
+    const int xr = tid >> 2, xc = (tid & 3) * 16;
+    const int gN = (int)(p.G * N), ts = (int)tstride;
+    auto load_chunk = [&](int64_t cc) {
+        const int64_t tc = cc * kQ;
+        const int ncur = (int)min((int64_t)kQ, p.L - tc);
+        const uint16_t *Bb = p.Bm + ((b * p.L + tc) * p.G + grp) * N;
+        const uint16_t *Cb = p.Cm + ((b * p.L + tc) * p.G + grp) * N;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int e = tid + k * kT;
+            const int r = e / (N / 8), c8 = (e % (N / 8)) * 8;
+            pB[k] = pC[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (e < kQ * N / 8 && r < ncur) {
+                pB[k] = *reinterpret_cast<const uint4 *>(Bb + (r * gN + c8));
+                pC[k] = *reinterpret_cast<const uint4 *>(Cb + (r * gN + c8));
+            }
+        }
+        const int64_t xo = ((b * p.L + tc) * p.H + h) * kP;
+        pX[0] = pX[1] = pZ[0] = pZ[1] = make_uint4(0u, 0u, 0u, 0u);
+        if (xr < ncur) {
+            const int off = xr * ts + xc;
+            pX[0] = *reinterpret_cast<const uint4 *>(p.x + xo + off);
+            pX[1] = *reinterpret_cast<const uint4 *>(p.x + xo + off + 8);
+            if (p.z) {
+                pZ[0] = *reinterpret_cast<const uint4 *>(p.z + xo + off);
+                pZ[1] = *reinterpret_cast<const uint4 *>(p.z + xo + off + 8);
+            }
+        }
+        if (w == 0 && lane < ncur)
+            pdt = p.dt[(b * p.L + tc + lane) * p.H + h];
+    };
+
     const int64_t n_chunks = (p.L + kQ - 1) / kQ;
+    if (n_chunks > 0)
+        load_chunk(0);
     for (int64_t c = 0; c < n_chunks; ++c) {
         const int64_t t0 = c * kQ;
         const int nt = (int)min((int64_t)kQ, p.L - t0);
 
-        // ---- 1. stage B (both layouts), C and x^T; steps past L are zero ---
-        for (int e = tid; e < kQ * (N / 8); e += kT) {
-            const int r = e / (N / 8), c8 = (e % (N / 8)) * 8;
-            uint4 vb = make_uint4(0u, 0u, 0u, 0u), vc = vb;
-            if (r < nt) {
-                const int64_t o = ((b * p.L + t0 + r) * p.G + grp) * N + c8;
-                vb = *reinterpret_cast<const uint4 *>(p.Bm + o);
-                vc = *reinterpret_cast<const uint4 *>(p.Cm + o);
-            }
-            *reinterpret_cast<uint4 *>(sB + r * NP + c8) = vb;
-            *reinterpret_cast<uint4 *>(sC + r * NP + c8) = vc;
-            const uint32_t wv[4] = {vb.x, vb.y, vb.z, vb.w};
+        // ---- 1. stage B, C, B^T, x^T from the registers ---------------------
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sBt[(c8 + 2 * k) * kQP + r] = (uint16_t)(wv[k] & 0xffffu);
-                sBt[(c8 + 2 * k + 1) * kQP + r] = (uint16_t)(wv[k] >> 16);
+        for (int k = 0; k < kPer; ++k) {
+            const int e = tid + k * kT;
+            if (e < kQ * N / 8) {
+                const int r = e / (N / 8), c8 = (e % (N / 8)) * 8;
+                *reinterpret_cast<uint4 *>(sB + r * NP + c8) = pB[k];
+                *reinterpret_cast<uint4 *>(sC + r * NP + c8) = pC[k];
             }
         }
-        for (int e = tid; e < kQ * (kP / 8); e += kT) {
-            const int r = e / (kP / 8), c8 = (e % (kP / 8)) * 8;
-            uint4 vx = make_uint4(0u, 0u, 0u, 0u);
-            if (r < nt)
-                vx = *reinterpret_cast<const uint4 *>(p.x + ((b * p.L + t0 + r) * p.H + h) * kP + c8);
-            const uint32_t wv[4] = {vx.x, vx.y, vx.z, vx.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sXt[(c8 + 2 * k) * kQP + r] = (uint16_t)(wv[k] & 0xffffu);
-                sXt[(c8 + 2 * k + 1) * kQP + r] = (uint16_t)(wv[k] >> 16);
-            }
-        }
+        *reinterpret_cast<uint4 *>(sX + xr * kXP + xc) = pX[0];
+        *reinterpret_cast<uint4 *>(sX + xr * kXP + xc + 8) = pX[1];
+        const uint4 cZ0 = pZ[0], cZ1 = pZ[1];
+        const uint32_t cdt = pdt;
+        if (c + 1 < n_chunks)
+            load_chunk(c + 1);
+
         // ---- 2. per step (wave 0, lane = step): Δ, ℓ = Δ a, β, Λ ------------
         if (w == 0) {
             float ell = 0.f, beta = 0.f;  // steps past L: no decay, no input
             if (lane < nt) {
-                const float v = bf16_bits_to_f32(p.dt[(b * p.L + t0 + lane) * p.H + h]) + bias;
+                const float v = bf16_bits_to_f32(cdt) + bias;
                 const float delta = softplus_log2(v * kLog2e) * kLn2;
                 ell = delta * a;
                 beta = zoh_input_coef(a, delta, hw_exp2(ell * kLog2e));
@@ -185,15 +223,35 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
         }
         __syncthreads();
 
-        // ---- 3. w_s x_s[p] split into bf16 hi + lo, s-contiguous ------------
-        for (int e = tid; e < kP * (kQ / 2); e += kT) {
-            const int pp = e / (kQ / 2), s2 = (e % (kQ / 2)) * 2;
-            const uint32_t xv = *reinterpret_cast<const uint32_t *>(sXt + pp * kQP + s2);
-            uint32_t h0b, l0b, h1b, l1b;
-            split_bf16(bf16_bits_to_f32(xv & 0xffffu) * sW[s2], h0b, l0b);
-            split_bf16(bf16_bits_to_f32(xv >> 16) * sW[s2 + 1], h1b, l1b);
-            *reinterpret_cast<uint32_t *>(sXw[0] + pp * kQP + s2) = pack2(h0b, h1b);
-            *reinterpret_cast<uint32_t *>(sXw[1] + pp * kQP + s2) = pack2(l0b, l1b);
+        // ---- 3. transposes: x^T, (w x)^T split into bf16 hi + lo, and B^T ----
+        {
+            // lane = channel, wave w = steps 16w .. 16w+15: column reads of x,
+            // 16-byte row stores of the transposes
+            uint32_t xs[8], hs[8], ls[8];
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                const int s0 = 16 * w + j;
+                const uint32_t x0 = sX[s0 * kXP + lane], x1 = sX[(s0 + 1) * kXP + lane];
+                xs[j / 2] = x0 | (x1 << 16);
+                split2(__uint_as_float(x0 << 16) * sW[s0], __uint_as_float(x1 << 16) * sW[s0 + 1],
+                       hs[j / 2], ls[j / 2]);
+            }
+            uint16_t *xt = sXt + lane * kQP + 16 * w;
+            uint16_t *wh = sXw[0] + lane * kQP + 16 * w, *wl = sXw[1] + lane * kQP + 16 * w;
+            *reinterpret_cast<uint4 *>(xt) = make_uint4(xs[0], xs[1], xs[2], xs[3]);
+            *reinterpret_cast<uint4 *>(xt + 8) = make_uint4(xs[4], xs[5], xs[6], xs[7]);
+            *reinterpret_cast<uint4 *>(wh) = make_uint4(hs[0], hs[1], hs[2], hs[3]);
+            *reinterpret_cast<uint4 *>(wh + 8) = make_uint4(hs[4], hs[5], hs[6], hs[7]);
+            *reinterpret_cast<uint4 *>(wl) = make_uint4(ls[0], ls[1], ls[2], ls[3]);
+            *reinterpret_cast<uint4 *>(wl + 8) = make_uint4(ls[4], ls[5], ls[6], ls[7]);
+            // B^T: column btn, steps bts .. bts + kBtPer - 1 (kBtPer = N/4 >= 4)
+#pragma unroll
+            for (int j = 0; j < kBtPer; j += 4) {
+                const uint32_t b0 = sB[(bts + j) * NP + btn], b1 = sB[(bts + j + 1) * NP + btn];
+                const uint32_t b2 = sB[(bts + j + 2) * NP + btn], b3 = sB[(bts + j + 3) * NP + btn];
+                *reinterpret_cast<uint2 *>(sBt + btn * kQP + bts + j) =
+                    make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            }
         }
         // ---- 4. causal tiles M^T[s][t] = (B_s . C_t) e^(Λ_t - Λ_s) β_s, s <= t
 #pragma unroll
@@ -224,18 +282,17 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
             // lane: G^T[s = 16 sb + 4 g4 + i][t = 16 tb + l16]
             const int t = 16 * tb + l16;
             const float lt = sLam[t];
-            uint32_t hi[4], lo[4];
+            float m[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * g4 + i;
-                const float m =
-                    s <= t ? acc[i] * hw_exp2((lt - sLam[s]) * kLog2e) * sBeta[s] : 0.f;
-                split_bf16(m, hi[i], lo[i]);
+                m[i] = s <= t ? acc[i] * hw_exp2((lt - sLam[s]) * kLog2e) * sBeta[s] : 0.f;
             }
-            *reinterpret_cast<uint2 *>(&sM[k][0][lane * 4]) =
-                make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-            *reinterpret_cast<uint2 *>(&sM[k][1][lane * 4]) =
-                make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+            uint32_t hi0, lo0, hi1, lo1;
+            split2(m[0], m[1], hi0, lo0);
+            split2(m[2], m[3], hi1, lo1);
+            *reinterpret_cast<uint2 *>(&sM[k][0][lane * 4]) = make_uint2(hi0, hi1);
+            *reinterpret_cast<uint2 *>(&sM[k][1][lane * 4]) = make_uint2(lo0, lo1);
         }
         __syncthreads();
 
@@ -259,14 +316,8 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
         uint32_t Hh[NB][2], Hl[NB][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                split_bf16(Hs[nb][i], hi[i], lo[i]);
-            Hh[nb][0] = pack2(hi[0], hi[1]);
-            Hh[nb][1] = pack2(hi[2], hi[3]);
-            Hl[nb][0] = pack2(lo[0], lo[1]);
-            Hl[nb][1] = pack2(lo[2], lo[3]);
+            split2(Hs[nb][0], Hs[nb][1], Hh[nb][0], Hl[nb][0]);
+            split2(Hs[nb][2], Hs[nb][3], Hh[nb][1], Hl[nb][1]);
         }
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -313,9 +364,9 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
                 sa[nb] = mma32(av, xl, sa[nb]);
             }
         }
-        __syncthreads();  // every wave is done with B before Y takes its place
 
-        // ---- 6. Y to LDS, state update, then gate and store -----------------
+        // ---- 6. output tile to LDS (in the w x buffer), state update ---------
+        __syncthreads();  // every wave is done reading w x
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
@@ -332,35 +383,28 @@ __global__ void __launch_bounds__(kT) ssd_fwd_kernel(SsdKArgs p)
                 Hs[nb][i] = fmaf(decay, Hs[nb][i], sa[nb][i]);
         }
         __syncthreads();
-        {
-            const int t = tid >> 2, pp = (tid & 3) * 16;  // 16 channels of one step
-            if (t < nt) {
-                const int64_t o = ((b * p.L + t0 + t) * p.H + h) * kP + pp;
-                const uint4 x0 = *reinterpret_cast<const uint4 *>(p.x + o);
-                const uint4 x1 = *reinterpret_cast<const uint4 *>(p.x + o + 8);
-                uint4 z0 = make_uint4(0u, 0u, 0u, 0u), z1 = z0;
-                if (p.z) {
-                    z0 = *reinterpret_cast<const uint4 *>(p.z + o);
-                    z1 = *reinterpret_cast<const uint4 *>(p.z + o + 8);
-                }
-                uint32_t out[8];
+        // ---- 7. skip, gate and store: step xr, channels xc .. xc+15 ----------
+        if (xr < nt) {
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(sX + xr * kXP + xc);
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(sX + xr * kXP + xc + 8);
+            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const uint32_t zw[8] = {cZ0.x, cZ0.y, cZ0.z, cZ0.w, cZ1.x, cZ1.y, cZ1.z, cZ1.w};
+            uint32_t out[8];
 #pragma unroll
-                for (int j = 0; j < 16; j += 2) {
-                    const uint4 &xs = j < 8 ? x0 : x1;
-                    const uint4 &zs = j < 8 ? z0 : z1;
-                    float v0 = fmaf(Dv, bf16_at(xs, j & 7), sY[t * kYP + pp + j]);
-                    float v1 = fmaf(Dv, bf16_at(xs, (j & 7) + 1), sY[t * kYP + pp + j + 1]);
-                    if (p.z) {
-                        v0 *= silu_hw(bf16_at(zs, j & 7));
-                        v1 *= silu_hw(bf16_at(zs, (j & 7) + 1));
-                    }
-                    out[j / 2] = pack2(f32_to_bf16_bits(v0), f32_to_bf16_bits(v1));
+            for (int j = 0; j < 8; ++j) {
+                float v0 = fmaf(Dv, __uint_as_float(xw[j] << 16), sY[xr * kYP + xc + 2 * j]);
+                float v1 = fmaf(Dv, __uint_as_float(xw[j] & 0xffff0000u), sY[xr * kYP + xc + 2 * j + 1]);
+                if (p.z) {
+                    v0 *= silu_hw(__uint_as_float(zw[j] << 16));
+                    v1 *= silu_hw(__uint_as_float(zw[j] & 0xffff0000u));
                 }
-                *reinterpret_cast<uint4 *>(p.y + o) = make_uint4(out[0], out[1], out[2], out[3]);
-                *reinterpret_cast<uint4 *>(p.y + o + 8) = make_uint4(out[4], out[5], out[6], out[7]);
+                out[j] = cvt2(v0, v1);
             }
+            uint16_t *yp = p.y + ((b * p.L + t0) * p.H + h) * kP + (xr * ts + xc);
+            *reinterpret_cast<uint4 *>(yp) = make_uint4(out[0], out[1], out[2], out[3]);
+            *reinterpret_cast<uint4 *>(yp + 8) = make_uint4(out[4], out[5], out[6], out[7]);
         }
-        __syncthreads();  // Y's LDS is B's again for the next chunk
+        __syncthreads();  // the next chunk's staging overwrites every array
     }
     if (p.h_last) {
         float *hl = p.h_last + ((b * p.H + h) * kP + pcol) * N;
