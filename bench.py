@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # fp32 VALU lane-ops/s without packed math
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
 SCAN_SRC = os.path.join(ROOT, "selective_state_space_80_amd", "csrc", "scan_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
 
@@ -137,6 +138,68 @@ def cpu_baseline(p, B, D, L, target_s=20.0):
             "single_thread_value": round(single, 6),
             "single_thread_sample": f"batch row 0, channels 0..3, all {L} steps, 1 thread",
             "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def _pool_time(jobs, threads):
+    """Run oracle calls (ctypes, so they release the GIL) on a thread pool;
+    return the wall-clock seconds."""
+    import concurrent.futures as cf
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for f in [ex.submit(j) for j in jobs]:
+            f.result()
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_bwd(p, dout, B, D, L, target_s=15.0):
+    """The fp64 oracle's backward on a bounded sample: batch row 0, whole
+    sequences of the first channels, one oracle call per channel on a pool of
+    host threads, sized for about target_s seconds."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+
+    def job(d):
+        sl = slice(d, d + 1)
+        return lambda: oracle.selective_scan_bwd(
+            p["x"][0:1, sl], p["dt"][0:1, sl], p["A"][sl], p["Bm"][0:1], p["Cm"][0:1],
+            dout[0:1, sl], dt_bias=p["dt_bias"][sl], Dskip=p["Dskip"][sl], z=p["z"][0:1, sl])
+
+    t1 = _pool_time([job(0)], 1)
+    ch = int(min(D, max(threads, target_s / max(t1, 1e-6) * threads)) // threads * threads)
+    dt = _pool_time([job(d) for d in range(ch)], threads)
+    elems = ch * L
+    return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"batch row 0, channels 0..{ch - 1} of {D}, all {L} steps: the fp64 "
+                      f"backward, one channel per call on {threads} host threads",
+            "single_thread_value": round(L / t1 / 1e9, 6), "cpu_model": cpu_model()}
+
+
+def cpu_baseline_ssd(p, wl, target_s=15.0):
+    """The fp64 oracle's Mamba-2-form recurrence on a bounded sample: whole
+    sequences of (batch row, head) pairs, one call per pair on a pool of host
+    threads, sized for about target_s seconds."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+
+    def job(b, h):
+        def run():
+            oracle.ssd_scan(p["x"][b:b + 1, :, h:h + 1], p["dt"][b:b + 1, :, h:h + 1],
+                            p["A"][h:h + 1], p["Bm"][b:b + 1], p["Cm"][b:b + 1],
+                            p["dt_bias"][h:h + 1], p["Dskip"][h:h + 1],
+                            p["z"][b:b + 1, :, h:h + 1])
+        return run
+
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    t1 = _pool_time([job(0, 0)], 1)
+    n = int(min(len(pairs), max(threads, target_s / max(t1, 1e-6) * threads)) // threads * threads)
+    dt = _pool_time([job(b, h) for b, h in pairs[:n]], threads)
+    elems = n * wl.L * wl.P
+    return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the first {n} of {len(pairs)} (batch row, head) pairs, all {wl.L} steps, "
+                      f"fp64 recurrence, one pair per call on {threads} host threads",
+            "single_thread_value": round(wl.L * wl.P / t1 / 1e9, 6), "cpu_model": cpu_model()}
 
 
 def quantiles(ms):
@@ -371,8 +434,17 @@ def run_bwd(args, torch, mamba, W):
             "config": {"workload": f"scan_bwd_b{B}_d{D}_l{L}_n{N}_f32", "batch": B,
                        "d_inner": D, "seq_len": L, "d_state": N, "io": "f32",
                        "step": "forward recompute, adjoint scan, chunk gradients, reductions"},
+            # the chunk-gradient kernel is bound by fp32 arithmetic: 30 flops of the
+            # formulas per (element, state) (recompute 7, gradients 23; an fma counts
+            # 2, exp and reciprocal 1), against the fp32 vector peak
+            "roofline": {"bound": "alu", "achieved": round(30 * elems * N / (k_ms * 1e-3) / 1e12, 2),
+                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(30 * elems * N / (k_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "scan_bwd_chunk_kernel<fp32>",
+                         "kernel_ms": round(k_ms, 4), "algorithmic_flops": 30 * elems * N},
             "kernels": {"chunk_grad_ms": quantiles(k_all),
-                        "chunk_grad_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
+                        "chunk_grad_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)},
+            **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_bwd(p, dout_np, B, D, L)})}
 
 
 def run_ssd(args, torch, mamba, W):
@@ -435,7 +507,8 @@ def run_ssd(args, torch, mamba, W):
                      "peak_tflops": 2500.0, "frac": round(flops / (k_ms * 1e-3) / 2.5e15, 4),
                      "algorithmic_flops": flops},
             "kernels": {"ssd_ms": quantiles(k_all),
-                        "ssd_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
+                        "ssd_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)},
+            **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_ssd(p, wl)})}
 
 
 def run_decode(args, torch, mamba, W):
