@@ -486,9 +486,10 @@ def run_ssd(args, torch, mamba, W):
     nbytes = (3 * elems * 2 + wl.B * wl.L * wl.H * 2 + 2 * wl.B * wl.L * wl.G * wl.N * 2
               + 3 * wl.H * 4)
     gbs = nbytes / (k_ms * 1e-3) / 1e9
-    # matrix work of the chunked form per 64-step chunk and head: the causal
-    # C B^T and M x (Q(Q+1)/2 entries each), the chunk state and C H
-    Q = 64
+    # matrix work of the chunked form per Q-step chunk and head (the kernel's
+    # chunk: 32 steps for N >= 32): the causal C B^T and M x (Q(Q+1)/2 entries
+    # each), the chunk state and C H
+    Q = 64 if wl.N == 16 else 32
     chunks = wl.B * wl.H * ((wl.L + Q - 1) // Q)
     flops = chunks * (2 * (Q * (Q + 1) // 2) * (wl.N + wl.P) + 2 * 2 * Q * wl.N * wl.P)
     return {"metric": "Mamba-2 form scan Gelem/s (B*L*H*P) and HBM GB/s as % of MI355X peak",
@@ -501,7 +502,7 @@ def run_ssd(args, torch, mamba, W):
                        "step": "ssd_scan_fwd (chunked Mamba-2 form, bf16 MFMA)"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "kernel": "ssd_fwd_kernel<64>", "kernel_ms": round(k_ms, 4),
+                         "kernel": f"ssd_fwd_kernel<N={wl.N}, Q={Q}>", "kernel_ms": round(k_ms, 4),
                          "algorithmic_bytes": nbytes},
             "mfma": {"achieved_tflops": round(flops / (k_ms * 1e-3) / 1e12, 2),
                      "peak_tflops": 2500.0, "frac": round(flops / (k_ms * 1e-3) / 2.5e15, 4),

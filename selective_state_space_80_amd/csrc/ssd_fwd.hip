@@ -5,7 +5,7 @@
 // map from a head's inputs to its outputs is a structured lower-triangular
 // matrix, so the scan can be done with matrix multiplications
 // ("Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式" §4.2).
-// Per head and chunk of kQ = 64 steps, with Δ_t = softplus(dt_t + bias),
+// Per head and chunk of Q steps (32 or 64), with Δ_t = softplus(dt_t + bias),
 // ℓ_t = Δ_t a, exact ZOH coefficient β_t = (e^ℓ_t - 1)/a (Δ_t at a = 0), and
 // the chunk-local cumulative log decay Λ_t = Σ_{k<=t} ℓ_k:
 //   Y_diag[t][p] = Σ_{s<=t} (C_t . B_s) e^(Λ_t - Λ_s) β_s x_s[p]   (within the chunk)
@@ -33,10 +33,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kQ = 64;        // chunk length
 constexpr int kP = kSsdHeadDim;  // channels per head
 constexpr int kT = 256;       // threads per workgroup
-constexpr int kQP = kQ + 8;   // row of an s-contiguous bf16 array (16-byte aligned rows)
 constexpr int kYP = kP + 1;   // row of the fp32 output tile
 
 // MFMA lane layouts (64 lanes, l16 = lane % 16, g4 = lane / 16), D = A B:
@@ -79,18 +77,34 @@ struct SsdKArgs {
     int64_t B, L, H, G;
 };
 
-// causal 16 x 16 tiles (t-block, s-block) of a chunk's 64 x 64 matrix
-constexpr int kTiles = 10;
-__device__ constexpr int kTB[kTiles] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__device__ constexpr int kSB[kTiles] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-
-template <int N>
-__global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
+// The causal 16 x 16 tiles (t-block, s-block), s-block <= t-block, of a
+// chunk's Q x Q matrix, numbered row by row: k -> (tile_tb(k), tile_sb(k)).
+__host__ __device__ constexpr int tile_tb(int k)
 {
+    int tb = 0;
+    while ((tb + 1) * (tb + 2) / 2 <= k)
+        ++tb;
+    return tb;
+}
+__host__ __device__ constexpr int tile_sb(int k) { return k - tile_tb(k) * (tile_tb(k) + 1) / 2; }
+
+// chunk length per state size: 32-step chunks keep the workgroup's LDS and
+// registers small enough for three workgroups per CU where N allows
+template <int N> constexpr int ssd_chunk() { return N == 16 ? 64 : 32; }
+
+template <int N, int Q>
+__global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kernel(SsdKArgs p)
+{
+    constexpr int kQ = Q;               // chunk length
+    constexpr int kQP = Q + 8;          // row of an s-contiguous bf16 array (16-byte aligned rows)
+    constexpr int TB = Q / 16;          // 16-step blocks per chunk
+    constexpr int kTiles = TB * (TB + 1) / 2;
+    constexpr int kXPer = Q * kP / kT;  // x, z, y values per thread (one step, kXPer channels)
     constexpr int NP = N + 8;           // row of an n-contiguous bf16 array
     constexpr int NB = N / 16;
     constexpr int kPer = (kQ * N / 8 + kT - 1) / kT;  // 16-byte B, C pieces per thread
-    constexpr int kBtPer = kQ * N / kT;               // B^T values per thread (N/4)
+    constexpr int kBtPer = kQ * N / kT;               // B^T values per thread
+    static_assert(kBtPer % 4 == 0 && kXPer % 8 == 0, "whole 8-byte / 16-byte pieces");
     __shared__ __align__(16) uint16_t sC[kQ * NP];         // C[t][n]
     __shared__ __align__(16) uint16_t sB[kQ * NP];         // B[s][n]
     __shared__ __align__(16) uint16_t sBt[N * kQP];        // B^T[n][s]
@@ -138,10 +152,10 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
     // Steps past L load nothing and stage zeros.  Offsets within a chunk are
     // 32-bit (the entry point bounds H P kQ below 2^31).
     constexpr int kXP = kP + 8;  // row of the staged x[s][p]
-    uint4 pB[kPer], pC[kPer], pX[2], pZ[2];
+    uint4 pB[kPer], pC[kPer], pX[kXPer / 8], pZ[kXPer / 8];
     uint32_t pdt = 0;
     const int btn = tid % N, bts = (tid / N) * kBtPer;  // this thread's B^T column and steps
-    const int xr = tid >> 2, xc = (tid & 3) * 16;
+    const int xr = tid / (kP / kXPer), xc = (tid % (kP / kXPer)) * kXPer;
     const int gN = (int)(p.G * N), ts = (int)tstride;
     auto load_chunk = [&](int64_t cc) {
         const int64_t tc = cc * kQ;
@@ -159,14 +173,16 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
             }
         }
         const int64_t xo = ((b * p.L + tc) * p.H + h) * kP;
-        pX[0] = pX[1] = pZ[0] = pZ[1] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int k = 0; k < kXPer / 8; ++k)
+            pX[k] = pZ[k] = make_uint4(0u, 0u, 0u, 0u);
         if (xr < ncur) {
             const int off = xr * ts + xc;
-            pX[0] = *reinterpret_cast<const uint4 *>(p.x + xo + off);
-            pX[1] = *reinterpret_cast<const uint4 *>(p.x + xo + off + 8);
-            if (p.z) {
-                pZ[0] = *reinterpret_cast<const uint4 *>(p.z + xo + off);
-                pZ[1] = *reinterpret_cast<const uint4 *>(p.z + xo + off + 8);
+#pragma unroll
+            for (int k = 0; k < kXPer / 8; ++k) {
+                pX[k] = *reinterpret_cast<const uint4 *>(p.x + xo + off + 8 * k);
+                if (p.z)
+                    pZ[k] = *reinterpret_cast<const uint4 *>(p.z + xo + off + 8 * k);
             }
         }
         if (w == 0 && lane < ncur)
@@ -190,9 +206,12 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
                 *reinterpret_cast<uint4 *>(sC + r * NP + c8) = pC[k];
             }
         }
-        *reinterpret_cast<uint4 *>(sX + xr * kXP + xc) = pX[0];
-        *reinterpret_cast<uint4 *>(sX + xr * kXP + xc + 8) = pX[1];
-        const uint4 cZ0 = pZ[0], cZ1 = pZ[1];
+        uint4 cZ[kXPer / 8];
+#pragma unroll
+        for (int k = 0; k < kXPer / 8; ++k) {
+            *reinterpret_cast<uint4 *>(sX + xr * kXP + xc + 8 * k) = pX[k];
+            cZ[k] = pZ[k];
+        }
         const uint32_t cdt = pdt;
         if (c + 1 < n_chunks)
             load_chunk(c + 1);
@@ -213,11 +232,13 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
                 if (lane >= off)
                     cum += o;
             }
-            const float lend = __shfl(cum, 63);
-            sLam[lane] = cum;
-            sBeta[lane] = beta;
-            sW[lane] = hw_exp2((lend - cum) * kLog2e) * beta;
-            sEL[lane] = hw_exp2(cum * kLog2e);
+            const float lend = __shfl(cum, kQ - 1);
+            if (lane < kQ) {
+                sLam[lane] = cum;
+                sBeta[lane] = beta;
+                sW[lane] = hw_exp2((lend - cum) * kLog2e) * beta;
+                sEL[lane] = hw_exp2(cum * kLog2e);
+            }
             if (lane == 0)
                 sDecay = hw_exp2(lend * kLog2e);
         }
@@ -225,25 +246,27 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
 
         // ---- 3. transposes: x^T, (w x)^T split into bf16 hi + lo, and B^T ----
         {
-            // lane = channel, wave w = steps 16w .. 16w+15: column reads of x,
-            // 16-byte row stores of the transposes
-            uint32_t xs[8], hs[8], ls[8];
+            // lane = channel, wave w = steps kQ/4 w .. kQ/4 (w+1) - 1: column
+            // reads of x, 16-byte row stores of the transposes
+            constexpr int kS = kQ / 4;
+            uint32_t xs[kS / 2], hs[kS / 2], ls[kS / 2];
 #pragma unroll
-            for (int j = 0; j < 16; j += 2) {
-                const int s0 = 16 * w + j;
+            for (int j = 0; j < kS; j += 2) {
+                const int s0 = kS * w + j;
                 const uint32_t x0 = sX[s0 * kXP + lane], x1 = sX[(s0 + 1) * kXP + lane];
                 xs[j / 2] = x0 | (x1 << 16);
                 split2(__uint_as_float(x0 << 16) * sW[s0], __uint_as_float(x1 << 16) * sW[s0 + 1],
                        hs[j / 2], ls[j / 2]);
             }
-            uint16_t *xt = sXt + lane * kQP + 16 * w;
-            uint16_t *wh = sXw[0] + lane * kQP + 16 * w, *wl = sXw[1] + lane * kQP + 16 * w;
-            *reinterpret_cast<uint4 *>(xt) = make_uint4(xs[0], xs[1], xs[2], xs[3]);
-            *reinterpret_cast<uint4 *>(xt + 8) = make_uint4(xs[4], xs[5], xs[6], xs[7]);
-            *reinterpret_cast<uint4 *>(wh) = make_uint4(hs[0], hs[1], hs[2], hs[3]);
-            *reinterpret_cast<uint4 *>(wh + 8) = make_uint4(hs[4], hs[5], hs[6], hs[7]);
-            *reinterpret_cast<uint4 *>(wl) = make_uint4(ls[0], ls[1], ls[2], ls[3]);
-            *reinterpret_cast<uint4 *>(wl + 8) = make_uint4(ls[4], ls[5], ls[6], ls[7]);
+            uint16_t *xt = sXt + lane * kQP + kS * w;
+            uint16_t *wh = sXw[0] + lane * kQP + kS * w, *wl = sXw[1] + lane * kQP + kS * w;
+#pragma unroll
+            for (int c8 = 0; c8 < kS; c8 += 8) {
+                const int q = c8 / 2;
+                *reinterpret_cast<uint4 *>(xt + c8) = make_uint4(xs[q], xs[q + 1], xs[q + 2], xs[q + 3]);
+                *reinterpret_cast<uint4 *>(wh + c8) = make_uint4(hs[q], hs[q + 1], hs[q + 2], hs[q + 3]);
+                *reinterpret_cast<uint4 *>(wl + c8) = make_uint4(ls[q], ls[q + 1], ls[q + 2], ls[q + 3]);
+            }
             // B^T: column btn, steps bts .. bts + kBtPer - 1 (kBtPer = N/4 >= 4)
 #pragma unroll
             for (int j = 0; j < kBtPer; j += 4) {
@@ -258,7 +281,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
         for (int k = 0; k < kTiles; ++k) {
             if (k % 4 != w)
                 continue;
-            const int tb = kTB[k], sb = kSB[k];
+            const int tb = tile_tb(k), sb = tile_sb(k);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if constexpr (N % 32 == 0) {
 #pragma unroll
@@ -297,15 +320,15 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
         __syncthreads();
 
         // ---- 5. this wave's channels: Y = M x + e^Λ C H, S = B^T (w x) -----
-        f32x4 yd[4], yo[4];
+        f32x4 yd[TB], yo[TB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
             yd[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
             yo[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int k = 0; k < kTiles; ++k) {
-            const int tb = kTB[k], sb = kSB[k];
+            const int tb = tile_tb(k), sb = tile_sb(k);
             const s16x4 mh = *reinterpret_cast<const s16x4 *>(&sM[k][0][lane * 4]);
             const s16x4 ml = *reinterpret_cast<const s16x4 *>(&sM[k][1][lane * 4]);
             const s16x4 xv = *reinterpret_cast<const s16x4 *>(sXt + pcol * kQP + 16 * sb + 4 * g4);
@@ -320,7 +343,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
             split2(Hs[nb][2], Hs[nb][3], Hh[nb][1], Hl[nb][1]);
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
             const uint16_t *crow = sC + (16 * tb + l16) * NP + 4 * g4;
             if constexpr (NB % 2 == 0) {
                 // k slot j of lane group g4: n = 16 nb + 4 g4 + j (j < 4), then
@@ -368,7 +391,7 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
         // ---- 6. output tile to LDS (in the w x buffer), state update ---------
         __syncthreads();  // every wave is done reading w x
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * g4 + i;
@@ -383,26 +406,28 @@ __global__ void __launch_bounds__(kT, 2) ssd_fwd_kernel(SsdKArgs p)
                 Hs[nb][i] = fmaf(decay, Hs[nb][i], sa[nb][i]);
         }
         __syncthreads();
-        // ---- 7. skip, gate and store: step xr, channels xc .. xc+15 ----------
+        // ---- 7. skip, gate and store: step xr, channels xc .. xc + kXPer - 1 --
         if (xr < nt) {
-            const uint4 x0 = *reinterpret_cast<const uint4 *>(sX + xr * kXP + xc);
-            const uint4 x1 = *reinterpret_cast<const uint4 *>(sX + xr * kXP + xc + 8);
-            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            const uint32_t zw[8] = {cZ0.x, cZ0.y, cZ0.z, cZ0.w, cZ1.x, cZ1.y, cZ1.z, cZ1.w};
-            uint32_t out[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v0 = fmaf(Dv, __uint_as_float(xw[j] << 16), sY[xr * kYP + xc + 2 * j]);
-                float v1 = fmaf(Dv, __uint_as_float(xw[j] & 0xffff0000u), sY[xr * kYP + xc + 2 * j + 1]);
-                if (p.z) {
-                    v0 *= silu_hw(__uint_as_float(zw[j] << 16));
-                    v1 *= silu_hw(__uint_as_float(zw[j] & 0xffff0000u));
-                }
-                out[j] = cvt2(v0, v1);
-            }
             uint16_t *yp = p.y + ((b * p.L + t0) * p.H + h) * kP + (xr * ts + xc);
-            *reinterpret_cast<uint4 *>(yp) = make_uint4(out[0], out[1], out[2], out[3]);
-            *reinterpret_cast<uint4 *>(yp + 8) = make_uint4(out[4], out[5], out[6], out[7]);
+#pragma unroll
+            for (int k = 0; k < kXPer / 8; ++k) {
+                const uint4 xq = *reinterpret_cast<const uint4 *>(sX + xr * kXP + xc + 8 * k);
+                const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+                const uint32_t zw[4] = {cZ[k].x, cZ[k].y, cZ[k].z, cZ[k].w};
+                uint32_t out[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float *yr = sY + xr * kYP + xc + 8 * k + 2 * j;
+                    float v0 = fmaf(Dv, __uint_as_float(xw[j] << 16), yr[0]);
+                    float v1 = fmaf(Dv, __uint_as_float(xw[j] & 0xffff0000u), yr[1]);
+                    if (p.z) {
+                        v0 *= silu_hw(__uint_as_float(zw[j] << 16));
+                        v1 *= silu_hw(__uint_as_float(zw[j] & 0xffff0000u));
+                    }
+                    out[j] = cvt2(v0, v1);
+                }
+                *reinterpret_cast<uint4 *>(yp + 8 * k) = make_uint4(out[0], out[1], out[2], out[3]);
+            }
         }
         __syncthreads();  // the next chunk's staging overwrites every array
     }
@@ -439,10 +464,10 @@ hipError_t launch_ssd_fwd(const SsdArgs &a, hipStream_t s)
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, s);
     switch (a.N) {
-    case 16: hipLaunchKernelGGL(ssd_fwd_kernel<16>, grid, block, 0, s, k); break;
-    case 32: hipLaunchKernelGGL(ssd_fwd_kernel<32>, grid, block, 0, s, k); break;
-    case 64: hipLaunchKernelGGL(ssd_fwd_kernel<64>, grid, block, 0, s, k); break;
-    case 128: hipLaunchKernelGGL(ssd_fwd_kernel<128>, grid, block, 0, s, k); break;
+    case 16: hipLaunchKernelGGL((ssd_fwd_kernel<16, ssd_chunk<16>()>), grid, block, 0, s, k); break;
+    case 32: hipLaunchKernelGGL((ssd_fwd_kernel<32, ssd_chunk<32>()>), grid, block, 0, s, k); break;
+    case 64: hipLaunchKernelGGL((ssd_fwd_kernel<64, ssd_chunk<64>()>), grid, block, 0, s, k); break;
+    case 128: hipLaunchKernelGGL((ssd_fwd_kernel<128, ssd_chunk<128>()>), grid, block, 0, s, k); break;
     default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
