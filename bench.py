@@ -99,23 +99,31 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(p, B, D, L, target_s=20.0):
+def cpu_baseline(p, B, D, L, target_s=20.0, y_gpu=None, tol=1e-4):
     """The fp64 oracle (conv then scan) on a bounded sample of the workload:
     whole sequences of the first channels, batch row by batch row, sized for at
     most ~target_s seconds (the whole workload when it fits).  Also the rate of
-    one thread on a few whole sequences."""
+    one thread on a few whole sequences, and (given the benchmarked output
+    y_gpu) the largest error of that output on those few sequences,
+    |y_gpu - y_oracle| / (1 + |y_oracle|), against the tolerance."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
 
     def run(b, ch, nthreads):
         xs = oracle.conv1d_silu(p["x_raw"][b:b + 1, :ch], p["conv_w"][:ch])
-        oracle.selective_scan(xs, p["dt"][b:b + 1, :ch], p["A"][:ch], p["Bm"][b:b + 1],
-                              p["Cm"][b:b + 1], p["dt_bias"][:ch], p["Dskip"][:ch],
-                              p["z"][b:b + 1, :ch], nthreads=nthreads)
+        return oracle.selective_scan(xs, p["dt"][b:b + 1, :ch], p["A"][:ch], p["Bm"][b:b + 1],
+                                     p["Cm"][b:b + 1], p["dt_bias"][:ch], p["Dskip"][:ch],
+                                     p["z"][b:b + 1, :ch], nthreads=nthreads)[0]
 
     t0 = time.perf_counter()
-    run(0, 4, 1)
+    y_small = run(0, 4, 1)
     single = 4 * L / (time.perf_counter() - t0) / 1e9
+    check = None
+    if y_gpu is not None:
+        err = np.abs(y_gpu - y_small) / (1.0 + np.abs(y_small))
+        check = {"max_rel_err": float(err.max()), "tolerance": tol,
+                 "sample": f"batch row 0, channels 0..3, all {L} steps of the benchmarked output",
+                 "within": bool(err.max() <= tol)}
     t0 = time.perf_counter()
     run(0, threads, threads)
     per_ch = (time.perf_counter() - t0) / threads
@@ -137,7 +145,8 @@ def cpu_baseline(p, B, D, L, target_s=20.0):
                       f"host threads ({elems} elements)",
             "single_thread_value": round(single, 6),
             "single_thread_sample": f"batch row 0, channels 0..3, all {L} steps, 1 thread",
-            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            **({"check": check} if check is not None else {})}
 
 
 def _pool_time(jobs, threads):
@@ -322,7 +331,8 @@ def run_block(args, torch, mamba, W):
         "kernels": kernels,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(p, B, D, L)
+        y0 = y[0:1, :4].double().cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(p, B, D, L, y_gpu=y0)
     return out
 
 
