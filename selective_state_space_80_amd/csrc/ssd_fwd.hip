@@ -110,11 +110,8 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
     __shared__ __align__(16) uint16_t sBt[N * kQP];        // B^T[n][s]
     __shared__ __align__(16) uint16_t sX[kQ * (kP + 8)];   // x[s][p]
     __shared__ __align__(16) uint16_t sXt[kP * kQP];       // x^T[p][s]
-    // (w x)^T[p][s] hi and lo; once the chunk's products are done, the fp32
-    // output tile Y[t][p] (row kYP) takes its place
-    __shared__ __align__(16) uint16_t sXw[2][kP * kQP];
-    float *sY = reinterpret_cast<float *>(&sXw[0][0]);
-    static_assert(kQ * kYP * 4 <= 2 * kP * kQP * 2, "output tile fits the w x buffer");
+    __shared__ __align__(16) uint16_t sXw[2][kP * kQP];    // (w x)^T[p][s], hi and lo
+    __shared__ float sY[kQ * kYP];                         // output tile Y[t][p]
     __shared__ __align__(16) uint16_t sM[kTiles][2][64 * 4];  // M tiles, hi and lo, A layout
     __shared__ float sLam[kQ], sBeta[kQ], sW[kQ], sEL[kQ];
     __shared__ float sDecay;
@@ -206,10 +203,11 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
                 *reinterpret_cast<uint4 *>(sC + r * NP + c8) = pC[k];
             }
         }
-        uint4 cZ[kXPer / 8];
+        uint4 cX[kXPer / 8], cZ[kXPer / 8];  // kept for this thread's skip and gate
 #pragma unroll
         for (int k = 0; k < kXPer / 8; ++k) {
             *reinterpret_cast<uint4 *>(sX + xr * kXP + xc + 8 * k) = pX[k];
+            cX[k] = pX[k];
             cZ[k] = pZ[k];
         }
         const uint32_t cdt = pdt;
@@ -388,8 +386,7 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
             }
         }
 
-        // ---- 6. output tile to LDS (in the w x buffer), state update ---------
-        __syncthreads();  // every wave is done reading w x
+        // ---- 6. output tile to LDS, state update ------------------------------
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
 #pragma unroll
@@ -411,8 +408,7 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
             uint16_t *yp = p.y + ((b * p.L + t0) * p.H + h) * kP + (xr * ts + xc);
 #pragma unroll
             for (int k = 0; k < kXPer / 8; ++k) {
-                const uint4 xq = *reinterpret_cast<const uint4 *>(sX + xr * kXP + xc + 8 * k);
-                const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+                const uint32_t xw[4] = {cX[k].x, cX[k].y, cX[k].z, cX[k].w};
                 const uint32_t zw[4] = {cZ[k].x, cZ[k].y, cZ[k].z, cZ[k].w};
                 uint32_t out[4];
 #pragma unroll
@@ -429,7 +425,10 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
                 *reinterpret_cast<uint4 *>(yp + 8 * k) = make_uint4(out[0], out[1], out[2], out[3]);
             }
         }
-        __syncthreads();  // the next chunk's staging overwrites every array
+        // No barrier here: the next chunk's staging writes only B, C and x,
+        // which nothing reads after the barrier above; Y is next written after
+        // two more barriers, which every wave reaches only once its output is
+        // stored.
     }
     if (p.h_last) {
         float *hl = p.h_last + ((b * p.H + h) * kP + pcol) * N;
