@@ -582,8 +582,8 @@ def main():
                          "this many MiB (known traffic for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the hot path "
-              "shards over batch/channels with no communication, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hot path "
+              "shards over batch/channels with no communication between GPUs", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -8,7 +8,7 @@ import numpy as np
 
 import oracle
 
-# spec tolerances: |y_gpu - y_oracle| <= tau * (1 + |y_oracle|)
+# tolerances: |y_gpu - y_oracle| <= tau * (1 + |y_oracle|)
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 STATE_TOL = 1e-4  # fp32 state in both I/O modes
 
