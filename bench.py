@@ -336,12 +336,17 @@ def run_block(args, torch, mamba, W):
     return out
 
 
-def run_scan(args, torch, mamba, W, idx, bidir=False):
+def run_scan(args, torch, mamba, W, idx, bidir=False, general=False):
     """One workload's scan; bidir: the forward scan, then the reverse scan of
-    a second parameter set added into the same y (a bidirectional layer)."""
+    a second parameter set added into the same y (a bidirectional layer);
+    general: A[d, n] ~ -U(0.05, 5) with no structure across n (as after
+    training), which takes the general path."""
     wl = W.WORKLOADS[idx]
     B, D, L, N = wl.B, wl.D, wl.L, wl.N
     p = W.scan_inputs(wl)
+    if general:
+        p["A"] = (-np.random.default_rng(wl.seed + 77).uniform(0.05, 5.0, size=(D, N))).astype(
+            np.float32)
     dev = torch.device("cuda:0")
     bf = wl.io == "bf16"
     io_t = torch.bfloat16 if bf else torch.float32
@@ -389,7 +394,8 @@ def run_scan(args, torch, mamba, W, idx, bidir=False):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16-io/f32", "data": "synthetic",
-            "config": {"workload": wl.name + ("_bidirectional" if bidir else ""), "batch": B,
+            "config": {"workload": wl.name + ("_bidirectional" if bidir else "")
+                       + ("_general_A" if general else ""), "batch": B,
                        "d_inner": D, "seq_len": L, "d_state": N, "io": wl.io,
                        "step": ("forward scan, then reverse scan added into y" if bidir else
                                 "forward scan"),
@@ -572,7 +578,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="block",
                     choices=["block", "scan_bf16_l2048", "scan_bf16_l131072", "decode",
-                             "bidir_bf16_l2048", "bwd", "ssd"])
+                             "bidir_bf16_l2048", "bwd", "ssd", "scan_bf16_l2048_general"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--unfused", action="store_true",
                     help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
@@ -607,6 +613,8 @@ def main():
         out = run_scan(args, torch, mamba, W, 2)
     elif args.workload == "scan_bf16_l131072":
         out = run_scan(args, torch, mamba, W, 3)
+    elif args.workload == "scan_bf16_l2048_general":
+        out = run_scan(args, torch, mamba, W, 2, general=True)
     elif args.workload == "bidir_bf16_l2048":
         out = run_scan(args, torch, mamba, W, 2, bidir=True)
     elif args.workload == "bwd":

@@ -57,11 +57,12 @@ def test_ssd_optional_inputs(opt):
 
 
 def test_ssd_zero_decay_head_and_strong_decay():
-    """A head with A = 0 (no decay: the ZOH coefficient is Δ) and one with a
-    large |A| (the state forgets within a few steps)."""
-    say("ssd A = 0 and large |A|")
+    """A head with A = 0 (no decay: the ZOH coefficient is Δ), one with a
+    large |A| (the state forgets within a few steps) and one with A > 0 (the
+    state grows)."""
+    say("ssd A = 0, large |A|, A > 0")
     p = W.make_ssd_inputs(1, 300, 4, 64, 1, 64, seed=12)
-    p["A"] = np.array([0.0, -1.0, -60.0, -0.01], dtype=np.float32)
+    p["A"] = np.array([0.0, -1.0, -60.0, 0.02], dtype=np.float32)
     h0 = np.random.default_rng(3).standard_normal((1, 4, 64, 64)).astype(np.float32)
     y, hl = run(p, h0)
     yo, ho = want(p, h0)
