@@ -31,7 +31,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # fp32 VALU lane-ops/s without packed math
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
 SCAN_SRC = os.path.join(ROOT, "selective_state_space_80_amd", "csrc", "scan_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
@@ -221,11 +220,12 @@ def quantiles(ms):
 def valu_record(tr, elems, kernel_ms):
     """VALU issue utilisation of the main scan kernel: wave-level VALU
     instructions per launch (rocprofv3 SQ_INSTS_VALU on the same kernel source)
-    over the time of one launch, against the issue peak of one wave64 fp32
-    instruction per 4 cycles on each of 1024 SIMDs at 2.4 GHz."""
+    over the time of one launch, against the published fp32 vector peak in
+    wave64 instructions: 157.3 TFLOP/s / 2 flops per fma / 64 lanes, i.e. two
+    wave64 fp32 instructions per clock per CU (256 CUs at 2.4 GHz)."""
     if tr is None or "valu_insts" not in tr:
         return None
-    peak = 256 * 4 * 2.4e9 / 4
+    peak = FP32_VECTOR_PEAK_TFLOPS * 1e12 / 2 / 64
     per_s = tr["valu_insts"] / (kernel_ms * 1e-3)
     return {"wave_instr_per_launch": int(tr["valu_insts"]),
             "wave_instr_per_elem": round(tr["valu_insts"] * 64 / elems, 1),

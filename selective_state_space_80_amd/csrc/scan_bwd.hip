@@ -18,7 +18,7 @@
 //      saving every chunk's incoming ν (from the future) and writing dh0;
 //   3. this file's chunk kernel: per 64-channel tile and chunk, four lanes per
 //      channel (one quarter of the 16 states each) recompute the chunk's
-//      states a quarter chunk at a time from checkpoints, keeping each step's
+//      states four steps at a time from checkpoints, keeping each step's
 //      decay and input coefficient, walk them backwards, and write dx, ddt,
 //      dz and per-tile / per-chunk partial sums of dB, dC, dA, dD, ddt_bias;
 //   4. a reduction of those partial sums in a fixed order (deterministic).
@@ -30,8 +30,9 @@ namespace mamba {
 namespace {
 
 constexpr int kBT = 32;              // steps per chunk (the forward chunk grid)
-constexpr int kQuarter = kBT / 4;    // steps whose states stay in registers at a time
-constexpr int kBThreads = 256;       // 64 channels x 4 quarters
+constexpr int kSub = 4;              // steps whose states stay in registers at a time
+constexpr int kNSub = kBT / kSub;    // sub-chunks per chunk, each from its own checkpoint
+constexpr int kBThreads = 256;       // 64 channels x 4 lanes (4 states each)
 constexpr int kCh = kBThreads / 4;   // channels per workgroup (one tile)
 constexpr int kPad = kBT + 1;        // LDS row stride of the per-channel arrays
 constexpr int kTStride = 2 * kMaxN + 4;  // row of dB then dC values, 16-byte aligned
@@ -92,19 +93,22 @@ struct BwdArgs {
 };
 
 template <bool BF16>
-__global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
+__global__ void __launch_bounds__(kBThreads, 3) scan_bwd_chunk_kernel(BwdArgs p)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
+    // LDS stays under a third of the CU's 160 KB and the registers under 168,
+    // so that three workgroups (three waves per SIMD) share a CU.
     __shared__ __align__(16) float sB[kBT][kMaxN];
     __shared__ __align__(16) float sC[kBT][kMaxN];
-    // per channel and step: Δ, x, dy, σ(dt + bias); once a step is done its
-    // slots hold dx (sX), y + D x (sDY) and ddt (sSG)
-    __shared__ float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad], sSG[kCh][kPad];
+    // per channel and step: Δ, x, dy; once a step is done its slots hold dΔ
+    // (sDel, summed over the channel's states), dx (sX) and y + D x (sDY)
+    __shared__ float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad];
     // dB, dC of two steps per wave, channel-major, summed over the wave's 16
-    // channels by reading them back transposed; the wave sums go to sRed
+    // channels by reading them back transposed; the wave sums of a sub-chunk go
+    // to sRed (two buffers: sub-chunks alternate)
     __shared__ __align__(16) float sT[kBThreads / 64][2][16][kTStride];
-    __shared__ float sRed[kBThreads / 64][kBT][2 * kMaxN];
+    __shared__ float sRed[2][kBThreads / 64][kSub][2 * kMaxN];
 
     const int64_t wg = blockIdx.x;
     const int64_t c = wg % p.n_chunks;         // chunk
@@ -133,12 +137,11 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         const int64_t i = (b * p.D + dd) * p.L + t0 + r;
         // steps past L and channels past D are identity steps with zero
         // input and zero output gradient: they add nothing to dB, dC
-        float del = 0.f, xv = 0.f, dy = 0.f, sg = 0.f;
+        float del = 0.f, xv = 0.f, dy = 0.f;
         if (r < nt && dd < p.D) {
             const float bias = p.dt_bias ? p.dt_bias[dd] : 0.f;
             const float v = E::load(reinterpret_cast<const T *>(p.dt) + i) + bias;
             del = softplus_log2(v * kLog2e) * kLn2;
-            sg = hw_rcp(1.f + hw_exp2(-v * kLog2e));
             xv = E::load(reinterpret_cast<const T *>(p.x) + i);
             dy = E::load(reinterpret_cast<const T *>(p.dout) + i);
             if (p.z)
@@ -147,12 +150,12 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         sDel[cc][r] = del;
         sX[cc][r] = xv;
         sDY[cc][r] = dy;
-        sSG[cc][r] = sg;
     }
     __syncthreads();
 
     // ---- per-lane constants: states n = 4q + i of channel dc --------------
-    float a[4], rcpa[4], hin[4], nu[4], dAacc[4];
+    float a[4], rcpa[4], nu[4], dAacc[4];
+    float ck[kNSub][4];  // state at the start of each sub-chunk
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = 4 * q + i;
@@ -160,12 +163,12 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         a[i] = live ? p.A[dc * p.N + n] : 0.f;
         rcpa[i] = a[i] != 0.f ? hw_rcp(a[i]) : 0.f;
         const int64_t cs = ((g * p.n_cslots + c) * kMaxN + n) * 64 + ch;
-        hin[i] = live ? p.hsave[cs] : 0.f;
+        ck[0][i] = live ? p.hsave[cs] : 0.f;
         nu[i] = live ? p.nusave[cs] : 0.f;
         dAacc[i] = 0.f;
     }
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
-    float dDacc = 0.f, dbacc = 0.f;
+    float dDacc = 0.f;
 
     // one forward step of the lane's four states; e_n = exp(Δ A_n) and the
     // input coefficient β_n = (e_n - 1)/A_n are returned for the caller
@@ -183,14 +186,14 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         }
     };
 
-    // one quarter chunk [r0, r0 + kQuarter): states, decays and input
-    // coefficients from hstart kept in registers, then walked backwards
-    auto quarter = [&](int r0, const float (&hstart)[4]) {
-        float H[kQuarter][4], Ev[kQuarter][4], Bt[kQuarter][4];
+    // one sub-chunk [r0, r0 + kSub): states, decays and input coefficients
+    // from hstart kept in registers, then walked backwards
+    auto sub_chunk = [&](int r0, const float (&hstart)[4], float (*red)[kSub][2 * kMaxN]) {
+        float H[kSub][4], Ev[kSub][4], Bt[kSub][4];
         {
             float h[4] = {hstart[0], hstart[1], hstart[2], hstart[3]};
 #pragma unroll
-            for (int j = 0; j < kQuarter; ++j) {
+            for (int j = 0; j < kSub; ++j) {
                 __builtin_amdgcn_sched_barrier(0);
                 fwd(r0 + j, h, Ev[j], Bt[j]);
 #pragma unroll
@@ -199,7 +202,7 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
             }
         }
 #pragma unroll
-        for (int j = kQuarter - 1; j >= 0; --j) {
+        for (int j = kSub - 1; j >= 0; --j) {
             __builtin_amdgcn_sched_barrier(0);
             const int r = r0 + j;
             const float del = sDel[ch][r], xv = sX[ch][r], dy = sDY[ch][r];
@@ -231,13 +234,11 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
             ddel = quad_sum(ddel);
             yp = quad_sum(yp);
             // every lane of the quad holds the sums: all four store the same
-            // values, no branch
-            const float ddt = ddel * sSG[ch][r];
-            dDacc = fmaf(dy, xv, dDacc);  // padded steps have dy = x = 0
-            dbacc += ddt;                 // and σ = 0
+            // values, no branch.  Δ, x and dy of step r are not read again.
+            dDacc = fmaf(dy, xv, dDacc);     // padded steps have dy = x = 0
+            sDel[ch][r] = ddel;              // dΔ (times σ at the output)
             sX[ch][r] = fmaf(Dd, dy, dxp);   // dx
             sDY[ch][r] = fmaf(Dd, xv, yp);   // y + D x, for dz
-            sSG[ch][r] = ddt;                // ddt
             // dB, dC: sums over the wave's 16 channels.  Two steps at a time: the
             // lanes store their values channel-major, then lane l adds up the
             // 16 channels of entry l (step j + l/32, value l%32) in order.
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
 #pragma unroll
                 for (int cw = 0; cw < 16; ++cw)
                     acc += sT[wave][so][cw][kn];
-                sRed[wave][r + so][kn] = acc;
+                red[wave][j + so][kn] = acc;
                 __builtin_amdgcn_wave_barrier();
             }
             // keep the accumulators' chains in their steps (otherwise the
@@ -263,49 +264,70 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
         }
     };
 
-    // Checkpoints: the states at the starts of the chunk's quarters, from one
-    // forward pass over its first three quarters.  Then the quarters from the
-    // last to the first, each recomputed from its checkpoint; the adjoint
-    // carries on from one to the next.  A loop, not four copies, so that
-    // nothing of one quarter stays live into the next.
-    float ck1[4], ck2[4], ck3[4];
+    // Checkpoints: the states at the starts of the sub-chunks, from one
+    // forward pass over all but the last sub-chunk.  Then the sub-chunks from
+    // the last to the first, each recomputed from its checkpoint; the adjoint
+    // carries on from one to the next.  A loop, not eight copies, so that
+    // nothing of one sub-chunk stays live into the next.
     {
-        float h[4] = {hin[0], hin[1], hin[2], hin[3]}, ev[4], bv[4];
+        float h[4] = {ck[0][0], ck[0][1], ck[0][2], ck[0][3]}, ev[4], bv[4];
 #pragma unroll
-        for (int j = 0; j < 3 * kQuarter; ++j) {
+        for (int j = 0; j < kBT - kSub; ++j) {
             __builtin_amdgcn_sched_barrier(0);
             fwd(j, h, ev, bv);
-            if (j == kQuarter - 1 || j == 2 * kQuarter - 1 || j == 3 * kQuarter - 1) {
+            if ((j + 1) % kSub == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (j == kQuarter - 1)
-                        ck1[i] = h[i];
-                    else if (j == 2 * kQuarter - 1)
-                        ck2[i] = h[i];
-                    else
-                        ck3[i] = h[i];
-                }
+                for (int i = 0; i < 4; ++i)
+                    ck[(j + 1) / kSub][i] = h[i];
             }
         }
     }
 #pragma unroll 1
-    for (int qq = 3; qq >= 0; --qq) {
+    for (int k = kNSub - 1; k >= 0; --k) {
         float hst[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            hst[i] = qq == 3 ? ck3[i] : qq == 2 ? ck2[i] : qq == 1 ? ck1[i] : hin[i];
-        quarter(qq * kQuarter, hst);
+        for (int i = 0; i < 4; ++i) {
+            float v = ck[0][i];
+#pragma unroll
+            for (int m = 1; m < kNSub; ++m)
+                v = k == m ? ck[m][i] : v;
+            hst[i] = v;
+        }
+        const int buf = k & 1;
+        sub_chunk(k * kSub, hst, sRed[buf]);
+        // every wave has its sums of the sub-chunk's steps in sRed[buf]: add
+        // them in wave order and store the tile's partial dB, dC rows.  The
+        // buffer is written again two sub-chunks later, after the next
+        // barrier, which these threads reach only once they are done here.
+        __syncthreads();
+        if (tid < kSub * 2 * kMaxN) {
+            const int ss = tid / (2 * kMaxN), kn = tid % (2 * kMaxN);
+            const int r = k * kSub + ss;
+            if (r < nt) {
+                float v = sRed[buf][0][ss][kn];
+#pragma unroll
+                for (int wv = 1; wv < kBThreads / 64; ++wv)
+                    v += sRed[buf][wv][ss][kn];
+                const int64_t o = ((tile * p.B + b) * p.L + t0 + r) * kMaxN + (kn % kMaxN);
+                (kn < kMaxN ? p.dBp : p.dCp)[o] = v;
+            }
+        }
     }
-    __syncthreads();
 
     // ---- outputs ----------------------------------------------------------
+    // ddt = dΔ σ(dt + bias) (dΔ/d(dt) = σ), formed here once per element; it
+    // replaces dΔ in sDel for the ddt_bias sums below
     for (int e = tid; e < kCh * kBT; e += kBThreads) {
         const int cc = e / kBT, r = e % kBT;
         const int64_t dd = tile * kCh + cc;
         if (dd < p.D && r < nt) {
             const int64_t i = (b * p.D + dd) * p.L + t0 + r;
+            const float bias = p.dt_bias ? p.dt_bias[dd] : 0.f;
+            const float v = E::load(reinterpret_cast<const T *>(p.dt) + i) + bias;
+            const float ddt = sDel[cc][r] * hw_rcp(1.f + hw_exp2(-v * kLog2e));
+            sDel[cc][r] = ddt;
             E::store(reinterpret_cast<T *>(p.dx) + i, sX[cc][r]);
-            E::store(reinterpret_cast<T *>(p.ddt) + i, sSG[cc][r]);
+            E::store(reinterpret_cast<T *>(p.ddt) + i, ddt);
             if (p.dz) {
                 // dz = dout (y + D x) SiLU'(z), SiLU'(z) = σ(z)(1 + z(1 - σ(z)))
                 const float zv = E::load(reinterpret_cast<const T *>(p.z) + i);
@@ -316,28 +338,19 @@ __global__ void __launch_bounds__(kBThreads) scan_bwd_chunk_kernel(BwdArgs p)
             }
         }
     }
-    for (int e = tid; e < kBT * kMaxN; e += kBThreads) {
-        const int r = e / kMaxN, n = e % kMaxN;
-        if (r < nt) {
-            float sb = 0.f, sc = 0.f;
-#pragma unroll
-            for (int wv = 0; wv < kBThreads / 64; ++wv) {
-                sb += sRed[wv][r][n];
-                sc += sRed[wv][r][kMaxN + n];
-            }
-            const int64_t o = ((tile * p.B + b) * p.L + t0 + r) * kMaxN + n;
-            p.dBp[o] = sb;
-            p.dCp[o] = sc;
-        }
-    }
+    __syncthreads();
     if (active) {
         const int64_t bc = b * p.n_chunks + c;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             p.dAp[(bc * p.D + d) * kMaxN + 4 * q + i] = dAacc[i];
         if (q == 0) {
+            // the chunk's ddt_bias share: its ddt values in step order
+            float db = 0.f;
+            for (int r = 0; r < nt; ++r)
+                db += sDel[ch][r];
             p.dDp[bc * p.D + d] = dDacc;
-            p.dbp[bc * p.D + d] = dbacc;
+            p.dbp[bc * p.D + d] = db;
         }
     }
 }
