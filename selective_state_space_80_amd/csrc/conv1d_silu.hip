@@ -46,7 +46,7 @@ __device__ __forceinline__ void store8(void *base, int64_t off, const float (&v)
         uint32_t w4[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            w4[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+            w4[k] = cvt2(v[2 * k], v[2 * k + 1]);
         *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(base) + off) =
             make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }

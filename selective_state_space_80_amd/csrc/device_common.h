@@ -19,12 +19,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : r;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+// two floats -> a packed bf16 pair (a in the low half), round to nearest even
+// (one v_cvt_pk_bf16_f32); NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return cvt2(f, 0.f) & 0xffffu; }
 
 // Element load / store for the two I/O types.
 template <bool BF16> struct Elem;

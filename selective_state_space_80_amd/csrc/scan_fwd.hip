@@ -252,7 +252,7 @@ __device__ __forceinline__ void store_chunk(void *base, int64_t off, int klo, in
                         lo += __uint_as_float(old4[k] << 16);
                         hi += __uint_as_float(old4[k] & 0xffff0000u);
                     }
-                    w4[k] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+                    w4[k] = cvt2(lo, hi);
                 }
                 q[i] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
             }

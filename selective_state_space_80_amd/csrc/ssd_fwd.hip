@@ -50,17 +50,6 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
-
-// two floats -> a packed bf16 pair (a in the low half), round to nearest even
-// (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t cvt2(float a, float b)
-{
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
 // (a, b) ≈ hi + lo, each a packed bf16 pair: hi the rounded values, lo the
 // rounded remainders
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo)
