@@ -77,4 +77,20 @@ __device__ __forceinline__ float zoh_input_coef(float an, float delta, float en)
     return fabsf(v) < 0.125f ? delta * phi : (en - 1.f) * hw_rcp(an);
 }
 
+// The same coefficient taken from w = ΔA_n log2(e), the exponent already formed
+// for en = 2^w, with 1/A_n supplied:  for |ΔA_n| < 1/8 the series of φ1 through
+// v^4 written in w (coefficients ln2^k/(k+1)!; truncation below 5e-8
+// relative), otherwise (en - 1)/A_n.
+__device__ __forceinline__ float zoh_coef_w(float w, float delta, float en, float rcpa)
+{
+    constexpr float c1 = 0.693147180559945309f;  // ln 2
+    constexpr float c2 = c1 * c1, c3 = c2 * c1, c4 = c3 * c1;
+    float phi = c4 / 120.f;
+    phi = fmaf(phi, w, c3 / 24.f);
+    phi = fmaf(phi, w, c2 / 6.f);
+    phi = fmaf(phi, w, c1 / 2.f);
+    phi = fmaf(phi, w, 1.f);
+    return fabsf(w) < 0.125f * 1.44269504088896341f ? delta * phi : (en - 1.f) * rcpa;
+}
+
 }  // namespace mamba

@@ -54,24 +54,6 @@ __device__ __forceinline__ float dbeta_dA(float delta, float del2, float u, floa
     return fabsf(u) < 0.125f ? del2 * s : closed;
 }
 
-// Input coefficient of the exact ZOH step, β = (e^u - 1)/A = Δ φ1(u) with
-// φ1(u) = (e^u - 1)/u, u = ΔA, taken from w = u log2(e) (the exponent already
-// formed for e = 2^w):  for |u| < 1/8 the series of φ1 through u^4 written in
-// w (coefficients ln2^k/(k+1)!; truncation below 5e-8 relative), otherwise
-// (e - 1)/A, where |e - 1| > 0.117 keeps the subtraction's relative error near
-// 1e-6.
-__device__ __forceinline__ float zoh_coef_w(float w, float delta, float e, float rcpa)
-{
-    constexpr float c1 = 0.693147180559945309f;  // ln 2
-    constexpr float c2 = c1 * c1, c3 = c2 * c1, c4 = c3 * c1;
-    float phi = c4 / 120.f;
-    phi = fmaf(phi, w, c3 / 24.f);
-    phi = fmaf(phi, w, c2 / 6.f);
-    phi = fmaf(phi, w, c1 / 2.f);
-    phi = fmaf(phi, w, 1.f);
-    return fabsf(w) < 0.125f * 1.44269504088896341f ? delta * phi : (e - 1.f) * rcpa;
-}
-
 // Sum over the four lanes of a quad (one channel): two DPP quad permutes.
 __device__ __forceinline__ float quad_sum(float v)
 {

@@ -507,6 +507,7 @@ template <bool STRUCT, typename GetS>
 __device__ __forceinline__ void apply_map(float f, GetS get, const ARow &Ar, float (&h)[kMaxN])
 {
     float pw = f;
+    const float fc = fminf(f, __FLT_MAX__);  // finite: A_n = 0 gives 2^0 = 1
 #pragma unroll
     for (int n = 0; n < kMaxN; ++n) {
         float P;
@@ -514,7 +515,7 @@ __device__ __forceinline__ void apply_map(float f, GetS get, const ARow &Ar, flo
             P = pw;
             pw *= f;
         } else {
-            P = (Ar[n] == 0.f) ? 1.f : hw_exp2(Ar[n] * f);
+            P = hw_exp2(Ar[n] * fc);
         }
         h[n] = fmaf(P, h[n], get(n));
     }
@@ -570,7 +571,10 @@ __device__ __forceinline__ void scan_segment(
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
     // General path: the A rows of the tile's channels wait in LDS (s_A[n][lane]),
     // which keeps that path within the structured path's register budget.
+    // Their reciprocals (0 for A_n = 0) sit in s_part's first slot during the
+    // chunk scan: s_part is first written after the barrier that ends it.
     const ARow Ar{s_A, lane};
+    const ARow Ainv{s_part[0], lane};
     float a0 = -1.f, inva0 = -1.f;
     if constexpr (STRUCT) {
         a0 = p.A[dc * p.N];
@@ -579,7 +583,9 @@ __device__ __forceinline__ void scan_segment(
         for (int e = w * kWave + lane; e < kMaxN * kWave; e += kWave * kWavesPerSeg) {
             const int n = e / kWave, l = e % kWave;
             const int64_t dd = min(dtile * kWave + l, p.D - 1);
-            s_A[n][l] = (n < p.N) ? p.A[dd * p.N + n] : -1.f;
+            const float an = (n < p.N) ? p.A[dd * p.N + n] : -1.f;
+            s_A[n][l] = an;
+            s_part[0][n][l] = an != 0.f ? hw_rcp(an) : 0.f;
         }
     }
 
@@ -686,9 +692,9 @@ __device__ __forceinline__ void scan_segment(
                     cumL += l;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n) {
-                        const float an = Ar[n];
-                        const float en = hw_exp2(an * l);  // exp(Δ A_n); 1 when A_n = 0
-                        const float coef = zoh_input_coef(an, delta, en);
+                        const float wn = Ar[n] * l;
+                        const float en = hw_exp2(wn);  // exp(Δ A_n); 1 when A_n = 0
+                        const float coef = zoh_coef_w(wn, delta, en, Ainv[n]);
                         hs[n] = fmaf(en, hs[n], coef * (Bj[n] * xv));
                         acc = fmaf(Cj[n], hs[n], acc);
                     }
@@ -933,11 +939,12 @@ __device__ __forceinline__ void scan_segment(
             for (int j = 0; j < kChunkT; ++j) {
                 if (j < ntf) {
                     const float *cr = s_bc[1][w * kChunkT + j];  // C
-                    const float Lj = er[j];
+                    // cumulative Δ/ln2, kept finite so that A_n = 0 gives 2^0 = 1
+                    const float Lj = fminf(er[j], __FLT_MAX__);
                     float corr = 0.f;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n) {
-                        const float gdec = (Ar[n] == 0.f) ? 1.f : hw_exp2(Ar[n] * Lj);
+                        const float gdec = hw_exp2(Ar[n] * Lj);
                         corr = fmaf(cr[n] * gdec, hin[n], corr);
                     }
                     yl[j] += corr;
