@@ -30,6 +30,13 @@ struct ScanWsLayout {
 };
 ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L);
 
+// Classes of a 64-channel tile of A, written per call by the scan's prep kernel
+// into the workspace's tile table: structured when A[d,n] = (n+1) A[d,0] with
+// A[d,0] < 0 for every channel of the tile (the decays of a step are then
+// powers of one exponential), general otherwise.
+constexpr uint32_t kPathStructured = 0u;
+constexpr uint32_t kPathGeneral = 1u;
+
 // Fused causal conv1d front end of the scan: at most this many taps.
 constexpr int kFusedConvTaps = 4;
 

@@ -22,6 +22,8 @@
 //      decay and input coefficient, walk them backwards, and write dx, ddt,
 //      dz and per-tile / per-chunk partial sums of dB, dC, dA, dD, ddt_bias;
 //   4. a reduction of those partial sums in a fixed order (deterministic).
+#include <cstddef>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -70,27 +72,44 @@ struct BwdArgs {
     float *dBp, *dCp;             // [n_dtiles][B][L][16] partial sums over 64 channels
     float *dAp;                   // [B * n_chunks][D][16]
     float *dDp, *dbp;             // [B * n_chunks][D]
+    const uint32_t *tiles;        // [n_dtiles] class of each tile's A (the scan's table)
     int64_t B, D, L, n_dtiles, n_chunks, n_cslots;
     int N;
 };
 
-template <bool BF16>
-__global__ void __launch_bounds__(kBThreads, 3) scan_bwd_chunk_kernel(BwdArgs p)
-{
-    using E = Elem<BF16>;
-    using T = typename E::T;
-    // LDS stays under a third of the CU's 160 KB and the registers under 168,
-    // so that three workgroups (three waves per SIMD) share a CU.
-    __shared__ __align__(16) float sB[kBT][kMaxN];
-    __shared__ __align__(16) float sC[kBT][kMaxN];
+// LDS of the chunk kernel.  It stays under a third of the CU's 160 KB and the
+// registers under 168, so that three workgroups (three waves per SIMD) share a
+// CU.
+struct BwdSmem {
+    float sB[kBT][kMaxN];
+    float sC[kBT][kMaxN];
     // per channel and step: Δ, x, dy; once a step is done its slots hold dΔ
     // (sDel, summed over the channel's states), dx (sX) and y + D x (sDY)
-    __shared__ float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad];
+    float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad];
     // dB, dC of two steps per wave, channel-major, summed over the wave's 16
     // channels by reading them back transposed; the wave sums of a sub-chunk go
     // to sRed (two buffers: sub-chunks alternate)
-    __shared__ __align__(16) float sT[kBThreads / 64][2][16][kTStride];
-    __shared__ float sRed[2][kBThreads / 64][kSub][2 * kMaxN];
+    float sT[kBThreads / 64][2][16][kTStride];
+    float sRed[2][kBThreads / 64][kSub][2 * kMaxN];
+};
+static_assert(offsetof(BwdSmem, sC) % 16 == 0 && offsetof(BwdSmem, sT) % 16 == 0,
+              "rows read and written as float4");
+
+// The whole chunk computation for one class of A (STRUCT: the structured form,
+// whose recompute takes the decays of a step's states as powers of one
+// exponential).
+template <bool BF16, bool STRUCT>
+__device__ __forceinline__ void bwd_chunk(const BwdArgs &p, BwdSmem &sm)
+{
+    using E = Elem<BF16>;
+    using T = typename E::T;
+    auto &sB = sm.sB;
+    auto &sC = sm.sC;
+    auto &sDel = sm.sDel;
+    auto &sX = sm.sX;
+    auto &sDY = sm.sDY;
+    auto &sT = sm.sT;
+    auto &sRed = sm.sRed;
 
     const int64_t wg = blockIdx.x;
     const int64_t c = wg % p.n_chunks;         // chunk
@@ -138,6 +157,9 @@ __global__ void __launch_bounds__(kBThreads, 3) scan_bwd_chunk_kernel(BwdArgs p)
     // ---- per-lane constants: states n = 4q + i of channel dc --------------
     float a[4], rcpa[4], nu[4], dAacc[4];
     float ck[kNSub][4];  // state at the start of each sub-chunk
+    // structured: A_0 of the channel (its states' decays are powers of e^(ΔA_0))
+    const float a0 = STRUCT && active ? p.A[dc * p.N] : -1.f;
+    const float rcpa0 = hw_rcp(a0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = 4 * q + i;
@@ -153,18 +175,40 @@ __global__ void __launch_bounds__(kBThreads, 3) scan_bwd_chunk_kernel(BwdArgs p)
     float dDacc = 0.f;
 
     // one forward step of the lane's four states; e_n = exp(Δ A_n) and the
-    // input coefficient β_n = (e_n - 1)/A_n are returned for the caller
+    // input coefficient β_n = (e_n - 1)/A_n are returned for the caller.
+    // Structured A (A_n = (n+1) A_0): the lane's first state n = 4q as in the
+    // general form, then e_n - 1 = e (e_(n-1) - 1) + (e - 1) with e = e^(ΔA_0)
+    // for the next three, e - 1 from φ1's series near 0 (no cancellation), so
+    // each β_n = (e_n - 1)/A_n keeps full relative accuracy.
     auto fwd = [&](int r, float (&h)[4], float (&ev)[4], float (&bv)[4]) {
         const float del = sDel[ch][r], xv = sX[ch][r];
         const float l = del * kLog2e;
         const float4 B4 = *reinterpret_cast<const float4 *>(&sB[r][4 * q]);
         const float Bv[4] = {B4.x, B4.y, B4.z, B4.w};
+        if constexpr (STRUCT) {
+            const float w0 = a0 * l;
+            const float e1 = hw_exp2(w0);
+            const float em0 = zoh_coef_w(w0, del, e1, rcpa0) * a0;  // e - 1
+            const float wq = a[0] * l;
+            ev[0] = hw_exp2(wq);
+            bv[0] = zoh_coef_w(wq, del, ev[0], rcpa[0]);
+            float em = bv[0] * a[0];  // e_n - 1 of the lane's first state
+            h[0] = fmaf(ev[0], h[0], bv[0] * (Bv[0] * xv));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float w = a[i] * l;
-            ev[i] = hw_exp2(w);
-            bv[i] = zoh_coef_w(w, del, ev[i], rcpa[i]);
-            h[i] = fmaf(ev[i], h[i], bv[i] * (Bv[i] * xv));
+            for (int i = 1; i < 4; ++i) {
+                em = fmaf(e1, em, em0);
+                ev[i] = em + 1.f;
+                bv[i] = em * rcpa[i];
+                h[i] = fmaf(ev[i], h[i], bv[i] * (Bv[i] * xv));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float w = a[i] * l;
+                ev[i] = hw_exp2(w);
+                bv[i] = zoh_coef_w(w, del, ev[i], rcpa[i]);
+                h[i] = fmaf(ev[i], h[i], bv[i] * (Bv[i] * xv));
+            }
         }
     };
 
@@ -335,6 +379,18 @@ __global__ void __launch_bounds__(kBThreads, 3) scan_bwd_chunk_kernel(BwdArgs p)
             p.dbp[bc * p.D + d] = db;
         }
     }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kBThreads, 3) scan_bwd_chunk_kernel(BwdArgs p)
+{
+    __shared__ __align__(16) BwdSmem sm;
+    const int64_t tile = (blockIdx.x / p.n_chunks) % p.n_dtiles;
+    const uint32_t path = __builtin_amdgcn_readfirstlane(p.tiles[tile]);
+    if (path == kPathStructured)
+        bwd_chunk<BF16, true>(p, sm);
+    else
+        bwd_chunk<BF16, false>(p, sm);
 }
 
 // Fixed-order column sums of a [rows][cols] partial array:
@@ -522,6 +578,7 @@ hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s)
     k.dAp = reinterpret_cast<float *>(ws + w.off_dAp);
     k.dDp = reinterpret_cast<float *>(ws + w.off_dDp);
     k.dbp = reinterpret_cast<float *>(ws + w.off_dbp);
+    k.tiles = reinterpret_cast<const uint32_t *>(ws + w.scan.off_tiles);
     k.B = a.B;
     k.D = a.D;
     k.L = a.L;

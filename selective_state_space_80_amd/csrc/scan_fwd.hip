@@ -65,8 +65,6 @@ struct WsHeader {
 };
 
 constexpr uint32_t kFlagAgg = 1u;
-constexpr uint32_t kPathStructured = 0u;
-constexpr uint32_t kPathGeneral = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
 constexpr int kSpinLimit = 1 << 22;
 #ifndef SCAN_SUPERSEG
