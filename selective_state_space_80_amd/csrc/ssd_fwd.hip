@@ -58,6 +58,15 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
+// v + (v of the lane that DPP control CTRL selects, in the rows of ROW_MASK;
+// 0 where there is none)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __int_as_float(
+                   __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
 struct SsdKArgs {
     const uint16_t *x, *dt, *Bm, *Cm, *z;
     const float *dt_bias, *A, *Dskip, *h0;
@@ -93,6 +102,7 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
     constexpr int NB = N / 16;
     constexpr int kPer = (kQ * N / 8 + kT - 1) / kT;  // 16-byte B, C pieces per thread
     constexpr int kBtPer = kQ * N / kT;               // B^T values per thread
+    constexpr int kSW = 3;  // wave with the fewest causal tiles (tile k goes to wave k % 4)
     static_assert(kBtPer % 4 == 0 && kXPer % 8 == 0, "whole 8-byte / 16-byte pieces");
     __shared__ __align__(16) uint16_t sC[kQ * NP];         // C[t][n]
     __shared__ __align__(16) uint16_t sB[kQ * NP];         // B[s][n]
@@ -102,8 +112,10 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
     __shared__ __align__(16) uint16_t sXw[2][kP * kQP];    // (w x)^T[p][s], hi and lo
     __shared__ float sY[kQ * kYP];                         // output tile Y[t][p]
     __shared__ __align__(16) uint16_t sM[kTiles][2][64 * 4];  // M tiles, hi and lo, A layout
-    __shared__ float sLam[kQ], sBeta[kQ], sW[kQ], sEL[kQ];
-    __shared__ float sDecay;
+    // per step of a chunk: Λ, β, w = e^(Λ_end - Λ) β, e^Λ, and the chunk's
+    // e^Λ_end; two buffers, chunks alternate (see step 4)
+    __shared__ float sLam[2][kQ], sBeta[2][kQ], sW[2][kQ], sEL[2][kQ];
+    __shared__ float sDecay[2];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -134,7 +146,8 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
     // Global loads of chunk c+1 are issued while chunk c is computed: per
     // thread, B and C rows as 16-byte pieces e = tid + k kT, and x and z as the
     // two 16-byte pieces of step xr, channels xc .. xc+15 (the step and
-    // channels this thread gates and stores); wave 0 lane t: dt of step t.
+    // channels this thread gates and stores); wave kSW lane t: dt of step t,
+    // first, so that its wait does not include the others.
     // Steps past L load nothing and stage zeros.  Offsets within a chunk are
     // 32-bit (the entry point bounds H P kQ below 2^31).
     constexpr int kXP = kP + 8;  // row of the staged x[s][p]
@@ -148,6 +161,8 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
         const int ncur = (int)min((int64_t)kQ, p.L - tc);
         const uint16_t *Bb = p.Bm + ((b * p.L + tc) * p.G + grp) * N;
         const uint16_t *Cb = p.Cm + ((b * p.L + tc) * p.G + grp) * N;
+        if (w == kSW && lane < ncur)
+            pdt = p.dt[(b * p.L + tc + lane) * p.H + h];
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int e = tid + k * kT;
@@ -171,13 +186,44 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
                     pZ[k] = *reinterpret_cast<const uint4 *>(p.z + xo + off + 8 * k);
             }
         }
-        if (w == 0 && lane < ncur)
-            pdt = p.dt[(b * p.L + tc + lane) * p.H + h];
+    };
+
+    // Step values of a chunk (wave kSW, lane = step): Δ, ℓ = Δ a, β and the
+    // chunk-local inclusive prefix Λ of ℓ (DPP within rows of 16, then row
+    // broadcasts), into buffer buf.  Steps past L: no decay, no input.
+    auto step_values = [&](int buf, uint32_t dtb, int ncur) {
+        float ell = 0.f, beta = 0.f;
+        if (lane < ncur) {
+            const float v = bf16_bits_to_f32(dtb) + bias;
+            const float delta = softplus_log2(v * kLog2e) * kLn2;
+            ell = delta * a;
+            beta = zoh_input_coef(a, delta, hw_exp2(ell * kLog2e));
+        }
+        float cum = ell;
+        cum = dpp_add<0x111, 0xf>(cum);  // row_shr:1
+        cum = dpp_add<0x112, 0xf>(cum);  // row_shr:2
+        cum = dpp_add<0x114, 0xf>(cum);  // row_shr:4
+        cum = dpp_add<0x118, 0xf>(cum);  // row_shr:8
+        cum = dpp_add<0x142, 0xa>(cum);  // row_bcast:15 into rows 1 and 3
+        if constexpr (kQ > 32)
+            cum = dpp_add<0x143, 0xc>(cum);  // row_bcast:31 into rows 2 and 3
+        const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), kQ - 1));
+        if (lane < kQ) {
+            sLam[buf][lane] = cum;
+            sBeta[buf][lane] = beta;
+            sW[buf][lane] = hw_exp2((lend - cum) * kLog2e) * beta;
+            sEL[buf][lane] = hw_exp2(cum * kLog2e);
+        }
+        if (lane == 0)
+            sDecay[buf] = hw_exp2(lend * kLog2e);
     };
 
     const int64_t n_chunks = (p.L + kQ - 1) / kQ;
-    if (n_chunks > 0)
+    if (n_chunks > 0) {
         load_chunk(0);
+        if (w == kSW)
+            step_values(0, pdt, (int)min((int64_t)kQ, p.L));
+    }
     for (int64_t c = 0; c < n_chunks; ++c) {
         const int64_t t0 = c * kQ;
         const int nt = (int)min((int64_t)kQ, p.L - t0);
@@ -199,36 +245,10 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
             cX[k] = pX[k];
             cZ[k] = pZ[k];
         }
-        const uint32_t cdt = pdt;
         if (c + 1 < n_chunks)
             load_chunk(c + 1);
-
-        // ---- 2. per step (wave 0, lane = step): Δ, ℓ = Δ a, β, Λ ------------
-        if (w == 0) {
-            float ell = 0.f, beta = 0.f;  // steps past L: no decay, no input
-            if (lane < nt) {
-                const float v = bf16_bits_to_f32(cdt) + bias;
-                const float delta = softplus_log2(v * kLog2e) * kLn2;
-                ell = delta * a;
-                beta = zoh_input_coef(a, delta, hw_exp2(ell * kLog2e));
-            }
-            float cum = ell;  // inclusive prefix sum over the chunk
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(cum, off);
-                if (lane >= off)
-                    cum += o;
-            }
-            const float lend = __shfl(cum, kQ - 1);
-            if (lane < kQ) {
-                sLam[lane] = cum;
-                sBeta[lane] = beta;
-                sW[lane] = hw_exp2((lend - cum) * kLog2e) * beta;
-                sEL[lane] = hw_exp2(cum * kLog2e);
-            }
-            if (lane == 0)
-                sDecay = hw_exp2(lend * kLog2e);
-        }
+        const int buf = (int)(c & 1);
+        const float *cLam = sLam[buf], *cBeta = sBeta[buf], *cW = sW[buf], *cEL = sEL[buf];
         __syncthreads();
 
         // ---- 3. transposes: x^T, (w x)^T split into bf16 hi + lo, and B^T ----
@@ -242,7 +262,7 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
                 const int s0 = kS * w + j;
                 const uint32_t x0 = sX[s0 * kXP + lane], x1 = sX[(s0 + 1) * kXP + lane];
                 xs[j / 2] = x0 | (x1 << 16);
-                split2(__uint_as_float(x0 << 16) * sW[s0], __uint_as_float(x1 << 16) * sW[s0 + 1],
+                split2(__uint_as_float(x0 << 16) * cW[s0], __uint_as_float(x1 << 16) * cW[s0 + 1],
                        hs[j / 2], ls[j / 2]);
             }
             uint16_t *xt = sXt + lane * kQP + kS * w;
@@ -291,12 +311,12 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
             }
             // lane: G^T[s = 16 sb + 4 g4 + i][t = 16 tb + l16]
             const int t = 16 * tb + l16;
-            const float lt = sLam[t];
+            const float lt = cLam[t];
             float m[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * g4 + i;
-                m[i] = s <= t ? acc[i] * hw_exp2((lt - sLam[s]) * kLog2e) * sBeta[s] : 0.f;
+                m[i] = s <= t ? acc[i] * hw_exp2((lt - cLam[s]) * kLog2e) * cBeta[s] : 0.f;
             }
             uint32_t hi0, lo0, hi1, lo1;
             split2(m[0], m[1], hi0, lo0);
@@ -304,6 +324,12 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
             *reinterpret_cast<uint2 *>(&sM[k][0][lane * 4]) = make_uint2(hi0, hi1);
             *reinterpret_cast<uint2 *>(&sM[k][1][lane * 4]) = make_uint2(lo0, lo1);
         }
+        // The step values of the next chunk, by the wave with the fewest tiles
+        // (none for 32-step chunks), into the other buffer: its last readers
+        // finished before the barrier that ended the previous chunk's step 6,
+        // and the next chunk reads it after the barrier below.
+        if (w == kSW && c + 1 < n_chunks)
+            step_values(buf ^ 1, pdt, (int)min((int64_t)kQ, p.L - t0 - kQ));
         __syncthreads();
 
         // ---- 5. this wave's channels: Y = M x + e^Λ C H, S = B^T (w x) -----
@@ -381,10 +407,10 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + 4 * g4 + i;
-                sY[t * kYP + pcol] = fmaf(sEL[t], yo[tb][i], yd[tb][i]);
+                sY[t * kYP + pcol] = fmaf(cEL[t], yo[tb][i], yd[tb][i]);
             }
         }
-        const float decay = sDecay;
+        const float decay = sDecay[buf];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
