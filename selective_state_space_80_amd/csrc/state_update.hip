@@ -18,6 +18,9 @@ namespace mamba {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef STATE_UPDATE_QPT
+#define STATE_UPDATE_QPT 2
+#endif
 
 template <bool BF16>
 __device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4])
@@ -37,9 +40,12 @@ __device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4
     }
 }
 
-// N = 16, state and A rows 16-byte aligned, B/C rows aligned to 4 elements:
-// thread g handles states [4q, 4q+4) of channel g/4, q = g % 4.
-template <bool BF16>
+// N = 16, state and A rows 16-byte aligned, B/C rows aligned to 4 elements.
+// A wave handles QPT runs of 64 quads (16 channels each): lane l of wave w
+// takes quads w*64*QPT + k*64 + l, k < QPT, i.e. states [4q, 4q+4), q = l % 4,
+// of QPT channels, so each of its loads and stores still covers one contiguous
+// 1 KB run per wave while QPT of them are in flight per lane.
+template <bool BF16, int QPT>
 __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
@@ -48,43 +54,55 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
 {
     using E = Elem<BF16>;
     using T = typename E::T;
-    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    // whole channels per wave (64 lanes = 16 channels), so a lane past the
-    // end only ever shares its shuffles with lanes past the end too
-    const bool live = g < n_quads;
-    const int64_t gc = live ? g : n_quads - 1;
-    const int64_t c = gc >> 2;  // channel b*D + d
-    const int q = (int)(gc & 3);
-    const int64_t b = c / D, d = c - b * D;
-    float hs[4], a[4], Bv[4], Cv[4];
-    load4<false>(h, gc, hs);
-    load4<false>(A, d * 4 + q, a);
-    load4<BF16>(Bm_, b * 4 + q, Bv);
-    load4<BF16>(Cm_, b * 4 + q, Cv);
-    const float xv = E::load(reinterpret_cast<const T *>(x_) + c);
-    const float dtv = E::load(reinterpret_cast<const T *>(dt_) + c);
-    const float bias = dt_bias ? dt_bias[d] : 0.f;
-    const float l = softplus_log2(fmaf(dtv, kLog2e, bias * kLog2e));  // Δ / ln 2
-    const float delta = l * kLn2;
-    float acc = 0.f;
+    const int lane = (int)(threadIdx.x & 63);
+    const int q = lane & 3;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    float hs[QPT][4], a[QPT][4], Bv[QPT][4], Cv[QPT][4], xv[QPT], dtv[QPT], bias[QPT];
+    int64_t gq[QPT], cq[QPT], dq[QPT];
+    bool live[QPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float en = hw_exp2(a[i] * l);  // exp(Δ A_n); 1 when A_n = 0
-        const float coef = zoh_input_coef(a[i], delta, en);
-        hs[i] = fmaf(en, hs[i], coef * (Bv[i] * xv));
-        acc = fmaf(Cv[i], hs[i], acc);
+    for (int k = 0; k < QPT; ++k) {
+        const int64_t g = (wave * QPT + k) * 64 + lane;
+        // whole channels per run of 64 quads, so a lane past the end only ever
+        // shares its shuffles with lanes past the end too
+        live[k] = g < n_quads;
+        gq[k] = live[k] ? g : n_quads - 1;
+        cq[k] = gq[k] >> 2;  // channel b*D + d
+        const int64_t b = cq[k] / D;
+        dq[k] = cq[k] - b * D;
+        load4<false>(h, gq[k], hs[k]);
+        load4<false>(A, dq[k] * 4 + q, a[k]);
+        load4<BF16>(Bm_, b * 4 + q, Bv[k]);
+        load4<BF16>(Cm_, b * 4 + q, Cv[k]);
+        xv[k] = E::load(reinterpret_cast<const T *>(x_) + cq[k]);
+        dtv[k] = E::load(reinterpret_cast<const T *>(dt_) + cq[k]);
+        bias[k] = dt_bias ? dt_bias[dq[k]] : 0.f;
     }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    if (!live)
-        return;
-    if (q == 0) {
-        float yv = acc + (Dskip ? Dskip[d] : 0.f) * xv;
-        if (z_)
-            yv *= silu_hw(E::load(reinterpret_cast<const T *>(z_) + c));
-        E::store(reinterpret_cast<T *>(y_) + c, yv);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+        const float l = softplus_log2(fmaf(dtv[k], kLog2e, bias[k] * kLog2e));  // Δ / ln 2
+        const float delta = l * kLn2;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float en = hw_exp2(a[k][i] * l);  // exp(Δ A_n); 1 when A_n = 0
+            const float coef = zoh_input_coef(a[k][i], delta, en);
+            hs[k][i] = fmaf(en, hs[k][i], coef * (Bv[k][i] * xv[k]));
+            acc = fmaf(Cv[k][i], hs[k][i], acc);
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if (!live[k])
+            continue;
+        if (q == 0) {
+            float yv = acc + (Dskip ? Dskip[dq[k]] : 0.f) * xv[k];
+            if (z_)
+                yv *= silu_hw(E::load(reinterpret_cast<const T *>(z_) + cq[k]));
+            E::store(reinterpret_cast<T *>(y_) + cq[k], yv);
+        }
+        reinterpret_cast<float4 *>(h)[gq[k]] =
+            make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
     }
-    reinterpret_cast<float4 *>(h)[g] = make_float4(hs[0], hs[1], hs[2], hs[3]);
 }
 
 // Any N <= 16: one lane per channel.
@@ -134,16 +152,18 @@ hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
     const bool quad = a.N == kMaxN && ((uintptr_t)a.h % 16) == 0 && ((uintptr_t)a.A % 16) == 0 &&
                       ((uintptr_t)a.Bm % bc_align) == 0 && ((uintptr_t)a.Cm % bc_align) == 0;
     if (quad) {
+        constexpr int kQPT = STATE_UPDATE_QPT;
         const int64_t n_quads = n_ch * 4;
-        const dim3 grid((unsigned)((n_quads + kThreads - 1) / kThreads));
+        const int64_t per_block = (int64_t)kThreads * kQPT;
+        const dim3 grid((unsigned)((n_quads + per_block - 1) / per_block));
         if (a.bf16)
-            hipLaunchKernelGGL(state_update_quad_kernel<true>, grid, dim3(kThreads), 0, s, a.h,
-                               a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D,
-                               n_quads);
+            hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT>), grid, dim3(kThreads), 0, s,
+                               a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y,
+                               a.D, n_quads);
         else
-            hipLaunchKernelGGL(state_update_quad_kernel<false>, grid, dim3(kThreads), 0, s, a.h,
-                               a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D,
-                               n_quads);
+            hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT>), grid, dim3(kThreads), 0, s,
+                               a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y,
+                               a.D, n_quads);
     } else {
         const dim3 grid((unsigned)((n_ch + kThreads - 1) / kThreads));
         if (a.bf16)
