@@ -41,67 +41,84 @@ __device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4
 }
 
 // N = 16, state and A rows 16-byte aligned, B/C rows aligned to 4 elements.
-// A wave handles QPT runs of 64 quads (16 channels each): lane l of wave w
-// takes quads w*64*QPT + k*64 + l, k < QPT, i.e. states [4q, 4q+4), q = l % 4,
-// of QPT channels, so each of its loads and stores still covers one contiguous
-// 1 KB run per wave while QPT of them are in flight per lane.
+// Grid: x over one batch row's 4 D quads, y over batch rows from b0 (the host
+// launches once per 65535 rows).  A wave handles QPT runs of 64 quads (16 channels each): lane l
+// of wave w takes row quads w*64*QPT + k*64 + l, k < QPT, i.e. states
+// [4q, 4q+4), q = l % 4, of QPT channels, so each of its loads and stores
+// covers one contiguous 1 KB run per wave while QPT of them are in flight per
+// lane.  Every load of a lane is issued before the first use (no branch
+// between them: an absent dt_bias, Dskip or z is read through another valid
+// pointer and its value ignored).
 template <bool BF16, int QPT>
 __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
     const void *__restrict__ Cm_, const float *__restrict__ Dskip, const void *__restrict__ z_,
-    void *__restrict__ y_, int64_t D, int64_t n_quads)
+    void *__restrict__ y_, int64_t b0, int64_t D)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
+    const int64_t b = b0 + blockIdx.y;
     const int lane = (int)(threadIdx.x & 63);
     const int q = lane & 3;
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    float hs[QPT][4], a[QPT][4], Bv[QPT][4], Cv[QPT][4], xv[QPT], dtv[QPT], bias[QPT];
-    int64_t gq[QPT], cq[QPT], dq[QPT];
-    bool live[QPT];
+    const int64_t row_quads = 4 * D;
+    const float *bias_p = dt_bias ? dt_bias : A;  // A has at least D entries
+    const float bias_on = dt_bias ? 1.f : 0.f;
+    const float *skip_p = Dskip ? Dskip : A;
+    const float skip_on = Dskip ? 1.f : 0.f;
+    const T *z_p = reinterpret_cast<const T *>(z_ ? z_ : x_);  // same shape as x
+    {
+        float hs[QPT][4], a[QPT][4], Bv[4], Cv[4], xv[QPT], dtv[QPT], bias[QPT], zv[QPT], dsk[QPT];
+        int64_t gq[QPT], cq[QPT], dq[QPT];
+        bool live[QPT];
+        load4<BF16>(Bm_, b * 4 + q, Bv);
+        load4<BF16>(Cm_, b * 4 + q, Cv);
 #pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-        const int64_t g = (wave * QPT + k) * 64 + lane;
-        // whole channels per run of 64 quads, so a lane past the end only ever
-        // shares its shuffles with lanes past the end too
-        live[k] = g < n_quads;
-        gq[k] = live[k] ? g : n_quads - 1;
-        cq[k] = gq[k] >> 2;  // channel b*D + d
-        const int64_t b = cq[k] / D;
-        dq[k] = cq[k] - b * D;
-        load4<false>(h, gq[k], hs[k]);
-        load4<false>(A, dq[k] * 4 + q, a[k]);
-        load4<BF16>(Bm_, b * 4 + q, Bv[k]);
-        load4<BF16>(Cm_, b * 4 + q, Cv[k]);
-        xv[k] = E::load(reinterpret_cast<const T *>(x_) + cq[k]);
-        dtv[k] = E::load(reinterpret_cast<const T *>(dt_) + cq[k]);
-        bias[k] = dt_bias ? dt_bias[dq[k]] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-        const float l = softplus_log2(fmaf(dtv[k], kLog2e, bias[k] * kLog2e));  // Δ / ln 2
-        const float delta = l * kLn2;
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float en = hw_exp2(a[k][i] * l);  // exp(Δ A_n); 1 when A_n = 0
-            const float coef = zoh_input_coef(a[k][i], delta, en);
-            hs[k][i] = fmaf(en, hs[k][i], coef * (Bv[k][i] * xv[k]));
-            acc = fmaf(Cv[k][i], hs[k][i], acc);
+        for (int k = 0; k < QPT; ++k) {
+            const int64_t rq = (wave * QPT + k) * 64 + lane;  // quad within the row
+            // whole channels per run of 64 quads, so a lane past the end only
+            // ever shares its shuffles with lanes past the end too
+            live[k] = rq < row_quads;
+            const int64_t rqc = live[k] ? rq : row_quads - 1;
+            dq[k] = rqc >> 2;
+            cq[k] = b * D + dq[k];
+            gq[k] = b * row_quads + rqc;
+            load4<false>(h, gq[k], hs[k]);
+            load4<false>(A, dq[k] * 4 + q, a[k]);
+            xv[k] = E::load(reinterpret_cast<const T *>(x_) + cq[k]);
+            dtv[k] = E::load(reinterpret_cast<const T *>(dt_) + cq[k]);
+            bias[k] = bias_p[dq[k]];
+            zv[k] = E::load(z_p + cq[k]);
+            dsk[k] = skip_p[dq[k]];
         }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
-        if (!live[k])
-            continue;
-        if (q == 0) {
-            float yv = acc + (Dskip ? Dskip[dq[k]] : 0.f) * xv[k];
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) {
+            const float l =
+                softplus_log2(fmaf(dtv[k], kLog2e, bias_on * bias[k] * kLog2e));  // Δ / ln 2
+            const float delta = l * kLn2;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float en = hw_exp2(a[k][i] * l);  // exp(Δ A_n); 1 when A_n = 0
+                const float coef = zoh_input_coef(a[k][i], delta, en);
+                hs[k][i] = fmaf(en, hs[k][i], coef * (Bv[i] * xv[k]));
+                acc = fmaf(Cv[i], hs[k][i], acc);
+            }
+            acc += __shfl_xor(acc, 1);
+            acc += __shfl_xor(acc, 2);
+            // every lane forms the gated output (so no load sinks into the
+            // store's branch); lane q = 0 of the quad stores it
+            float yv = acc + skip_on * dsk[k] * xv[k];
             if (z_)
-                yv *= silu_hw(E::load(reinterpret_cast<const T *>(z_) + cq[k]));
-            E::store(reinterpret_cast<T *>(y_) + cq[k], yv);
+                yv *= silu_hw(zv[k]);
+            if (!live[k])
+                continue;
+            if (q == 0)
+                E::store(reinterpret_cast<T *>(y_) + cq[k], yv);
+            reinterpret_cast<float4 *>(h)[gq[k]] =
+                make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
         }
-        reinterpret_cast<float4 *>(h)[gq[k]] =
-            make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
     }
 }
 
@@ -153,17 +170,19 @@ hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
                       ((uintptr_t)a.Bm % bc_align) == 0 && ((uintptr_t)a.Cm % bc_align) == 0;
     if (quad) {
         constexpr int kQPT = STATE_UPDATE_QPT;
-        const int64_t n_quads = n_ch * 4;
         const int64_t per_block = (int64_t)kThreads * kQPT;
-        const dim3 grid((unsigned)((n_quads + per_block - 1) / per_block));
-        if (a.bf16)
-            hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT>), grid, dim3(kThreads), 0, s,
-                               a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y,
-                               a.D, n_quads);
-        else
-            hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT>), grid, dim3(kThreads), 0, s,
-                               a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y,
-                               a.D, n_quads);
+        for (int64_t b0 = 0; b0 < a.B; b0 += 65535) {
+            const dim3 grid((unsigned)((4 * a.D + per_block - 1) / per_block),
+                            (unsigned)min(a.B - b0, (int64_t)65535));
+            if (a.bf16)
+                hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT>), grid, dim3(kThreads), 0,
+                                   s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z,
+                                   a.y, b0, a.D);
+            else
+                hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT>), grid, dim3(kThreads),
+                                   0, s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z,
+                                   a.y, b0, a.D);
+        }
     } else {
         const dim3 grid((unsigned)((n_ch + kThreads - 1) / kThreads));
         if (a.bf16)
