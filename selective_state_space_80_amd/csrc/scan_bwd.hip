@@ -126,52 +126,91 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs &p, BwdSmem &sm)
     const T *Cb = reinterpret_cast<const T *>(p.Cm) + b * p.L * p.N;
 
     // ---- stage B, C rows and the per-channel step values ------------------
-    for (int e = tid; e < kBT * kMaxN; e += kBThreads) {
-        const int r = e / kMaxN, n = e % kMaxN;
-        const bool ok = r < nt && n < p.N;
-        sB[r][n] = ok ? E::load(Bb + (t0 + r) * p.N + n) : 0.f;
-        sC[r][n] = ok ? E::load(Cb + (t0 + r) * p.N + n) : 0.f;
-    }
-    for (int e = tid; e < kCh * kBT; e += kBThreads) {
-        const int cc = e / kBT, r = e % kBT;
-        const int64_t dd = tile * kCh + cc;
-        const int64_t i = (b * p.D + dd) * p.L + t0 + r;
-        // steps past L and channels past D are identity steps with zero
-        // input and zero output gradient: they add nothing to dB, dC
-        float del = 0.f, xv = 0.f, dy = 0.f;
-        if (r < nt && dd < p.D) {
-            const float bias = p.dt_bias ? p.dt_bias[dd] : 0.f;
-            const float v = E::load(reinterpret_cast<const T *>(p.dt) + i) + bias;
-            del = softplus_log2(v * kLog2e) * kLn2;
-            xv = E::load(reinterpret_cast<const T *>(p.x) + i);
-            dy = E::load(reinterpret_cast<const T *>(p.dout) + i);
-            if (p.z)
-                dy *= silu_hw(E::load(reinterpret_cast<const T *>(p.z) + i));
+    // Every load below is issued before any is used, with no branch around
+    // them: out-of-range elements read index 0 and are masked to 0 (a branch
+    // around a load makes the compiler wait for all earlier loads at the join).
+    // Steps past L and channels past D are identity steps with zero input and
+    // zero output gradient: they add nothing to dB, dC.
+    {
+        constexpr int kBC = kBT * kMaxN / kBThreads;  // B, C values per thread
+        constexpr int kPS = kCh * kBT / kBThreads;    // per-channel elements per thread
+        static_assert(kBThreads % kBT == 0, "one step per thread in the staging");
+        float bq[kBC], cq[kBC];
+        bool okbc[kBC];
+#pragma unroll
+        for (int k = 0; k < kBC; ++k) {
+            const int e = tid + k * kBThreads, r = e / kMaxN, n = e % kMaxN;
+            okbc[k] = r < nt && n < p.N;
+            const int64_t o = okbc[k] ? (t0 + r) * p.N + n : 0;
+            bq[k] = E::load(Bb + o);
+            cq[k] = E::load(Cb + o);
         }
-        sDel[cc][r] = del;
-        sX[cc][r] = xv;
-        sDY[cc][r] = dy;
+        const int r = tid % kBT;  // this thread's step; channels tid/kBT + k kBThreads/kBT
+        const T *dtp = reinterpret_cast<const T *>(p.dt), *xp = reinterpret_cast<const T *>(p.x);
+        const T *gp = reinterpret_cast<const T *>(p.dout);
+        const T *zp = reinterpret_cast<const T *>(p.z ? p.z : p.dout);
+        const float *biasp = p.dt_bias ? p.dt_bias : p.A;  // A has at least D entries
+        float dtv[kPS], xq[kPS], gq[kPS], zq[kPS], bq2[kPS];
+        bool ok[kPS];
+#pragma unroll
+        for (int k = 0; k < kPS; ++k) {
+            const int cc = tid / kBT + k * (kBThreads / kBT);
+            const int64_t dd = tile * kCh + cc;
+            ok[k] = r < nt && dd < p.D;
+            const int64_t i = ok[k] ? (b * p.D + dd) * p.L + t0 + r : 0;
+            dtv[k] = E::load(dtp + i);
+            xq[k] = E::load(xp + i);
+            gq[k] = E::load(gp + i);
+            zq[k] = E::load(zp + i);
+            bq2[k] = biasp[ok[k] ? dd : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < kBC; ++k) {
+            const int e = tid + k * kBThreads;
+            sB[e / kMaxN][e % kMaxN] = okbc[k] ? bq[k] : 0.f;
+            sC[e / kMaxN][e % kMaxN] = okbc[k] ? cq[k] : 0.f;
+        }
+        const float bias_on = p.dt_bias ? 1.f : 0.f;
+#pragma unroll
+        for (int k = 0; k < kPS; ++k) {
+            const int cc = tid / kBT + k * (kBThreads / kBT);
+            const float v = dtv[k] + bias_on * bq2[k];
+            const float gate = p.z ? silu_hw(zq[k]) : 1.f;
+            sDel[cc][r] = ok[k] ? softplus_log2(v * kLog2e) * kLn2 : 0.f;
+            sX[cc][r] = ok[k] ? xq[k] : 0.f;
+            sDY[cc][r] = ok[k] ? gq[k] * gate : 0.f;
+        }
     }
     __syncthreads();
 
     // ---- per-lane constants: states n = 4q + i of channel dc --------------
+    // (loads first and unconditional, as above; dc is always a valid channel)
     float a[4], rcpa[4], nu[4], dAacc[4];
     float ck[kNSub][4];  // state at the start of each sub-chunk
-    // structured: A_0 of the channel (its states' decays are powers of e^(ΔA_0))
-    const float a0 = STRUCT && active ? p.A[dc * p.N] : -1.f;
-    const float rcpa0 = hw_rcp(a0);
+    float araw[4], hraw[4], nraw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = 4 * q + i;
-        const bool live = active && n < p.N;  // other states stay exactly zero
-        a[i] = live ? p.A[dc * p.N + n] : 0.f;
-        rcpa[i] = a[i] != 0.f ? hw_rcp(a[i]) : 0.f;
         const int64_t cs = ((g * p.n_cslots + c) * kMaxN + n) * 64 + ch;
-        ck[0][i] = live ? p.hsave[cs] : 0.f;
-        nu[i] = live ? p.nusave[cs] : 0.f;
+        araw[i] = p.A[dc * p.N + min(n, p.N - 1)];
+        hraw[i] = p.hsave[cs];
+        nraw[i] = p.nusave[cs];
+    }
+    const float a0raw = p.A[dc * p.N];
+    const float Draw = (p.Dskip ? p.Dskip : p.A)[dc];
+    // structured: A_0 of the channel (its states' decays are powers of e^(ΔA_0))
+    const float a0 = STRUCT && active ? a0raw : -1.f;
+    const float rcpa0 = hw_rcp(a0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool live = active && 4 * q + i < p.N;  // other states stay exactly zero
+        a[i] = live ? araw[i] : 0.f;
+        rcpa[i] = a[i] != 0.f ? hw_rcp(a[i]) : 0.f;
+        ck[0][i] = live ? hraw[i] : 0.f;
+        nu[i] = live ? nraw[i] : 0.f;
         dAacc[i] = 0.f;
     }
-    const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
+    const float Dd = p.Dskip ? Draw : 0.f;
     float dDacc = 0.f;
 
     // one forward step of the lane's four states; e_n = exp(Δ A_n) and the
