@@ -564,9 +564,13 @@ __device__ __forceinline__ void scan_segment(
     auto slot = [](int j) { return REV ? kChunkT - 1 - j : j; };
     TRACE_POINT(0);
 
-    // per-channel constants
-    const float bias2 = (p.dt_bias ? p.dt_bias[dc] : 0.f) * kLog2e;
-    const float Dd = p.Dskip ? p.Dskip[dc] : 0.f;
+    // per-channel constants.  Loaded unconditionally (an absent dt_bias or D
+    // is read through A, which has at least D entries, and ignored), so the
+    // loads travel with the chunk's instead of each waiting at a branch.
+    const float bias_raw = (p.dt_bias ? p.dt_bias : p.A)[dc];
+    const float skip_raw = (p.Dskip ? p.Dskip : p.A)[dc];
+    const float bias2 = (p.dt_bias ? bias_raw : 0.f) * kLog2e;
+    const float Dd = p.Dskip ? skip_raw : 0.f;
     // General path: the A rows of the tile's channels wait in LDS (s_A[n][lane]),
     // which keeps that path within the structured path's register budget.
     // Their reciprocals (0 for A_n = 0) sit in s_part's first slot during the
@@ -578,12 +582,19 @@ __device__ __forceinline__ void scan_segment(
         a0 = p.A[dc * p.N];
         inva0 = 1.0f / a0;
     } else {
-        for (int e = w * kWave + lane; e < kMaxN * kWave; e += kWave * kWavesPerSeg) {
-            const int n = e / kWave, l = e % kWave;
-            const int64_t dd = min(dtile * kWave + l, p.D - 1);
-            const float an = (n < p.N) ? p.A[dd * p.N + n] : -1.f;
-            s_A[n][l] = an;
-            s_part[0][n][l] = an != 0.f ? hw_rcp(an) : 0.f;
+        // rows n = w + 4k of the tile's channels (this lane's channel), loads first
+        constexpr int kRows = kMaxN / kWavesPerSeg;
+        const int64_t dd = min(dtile * kWave + lane, p.D - 1);
+        float an[kRows];
+#pragma unroll
+        for (int k = 0; k < kRows; ++k)
+            an[k] = p.A[dd * p.N + min(w + kWavesPerSeg * k, p.N - 1)];
+#pragma unroll
+        for (int k = 0; k < kRows; ++k) {
+            const int n = w + kWavesPerSeg * k;
+            const float v = n < p.N ? an[k] : -1.f;
+            s_A[n][lane] = v;
+            s_part[0][n][lane] = v != 0.f ? hw_rcp(v) : 0.f;
         }
     }
 
