@@ -381,25 +381,50 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs &p, BwdSmem &sm)
 
     // ---- outputs ----------------------------------------------------------
     // ddt = dΔ σ(dt + bias) (dΔ/d(dt) = σ), formed here once per element; it
-    // replaces dΔ in sDel for the ddt_bias sums below
-    for (int e = tid; e < kCh * kBT; e += kBThreads) {
-        const int cc = e / kBT, r = e % kBT;
-        const int64_t dd = tile * kCh + cc;
-        if (dd < p.D && r < nt) {
-            const int64_t i = (b * p.D + dd) * p.L + t0 + r;
-            const float bias = p.dt_bias ? p.dt_bias[dd] : 0.f;
-            const float v = E::load(reinterpret_cast<const T *>(p.dt) + i) + bias;
-            const float ddt = sDel[cc][r] * hw_rcp(1.f + hw_exp2(-v * kLog2e));
-            sDel[cc][r] = ddt;
-            E::store(reinterpret_cast<T *>(p.dx) + i, sX[cc][r]);
-            E::store(reinterpret_cast<T *>(p.ddt) + i, ddt);
-            if (p.dz) {
+    // replaces dΔ in sDel for the ddt_bias sums below.  As in the staging, the
+    // loads of a group of elements are issued first and unconditionally (index
+    // 0 for elements out of range) and only the stores are conditional; two
+    // groups of four, so that the registers stay within budget.
+    {
+        constexpr int kPS = kCh * kBT / kBThreads;
+        constexpr int kGrp = kPS / 2;
+        const int r = tid % kBT;
+        const T *dtp = reinterpret_cast<const T *>(p.dt);
+        const T *zp = reinterpret_cast<const T *>(p.z ? p.z : p.dout);
+        const T *gp = reinterpret_cast<const T *>(p.dout);
+        const float *biasp = p.dt_bias ? p.dt_bias : p.A;
+        const float bias_on = p.dt_bias ? 1.f : 0.f;
+#pragma unroll 1
+        for (int k0 = 0; k0 < kPS; k0 += kGrp) {
+            float dtv[kGrp], zq[kGrp], gq[kGrp], bq[kGrp];
+#pragma unroll
+            for (int k = 0; k < kGrp; ++k) {
+                const int cc = tid / kBT + (k0 + k) * (kBThreads / kBT);
+                const int64_t dd = tile * kCh + cc;
+                const bool ok = dd < p.D && r < nt;
+                const int64_t i = ok ? (b * p.D + dd) * p.L + t0 + r : 0;
+                dtv[k] = E::load(dtp + i);
+                zq[k] = E::load(zp + i);
+                gq[k] = E::load(gp + i);
+                bq[k] = biasp[ok ? dd : 0];
+            }
+#pragma unroll
+            for (int k = 0; k < kGrp; ++k) {
+                const int cc = tid / kBT + (k0 + k) * (kBThreads / kBT);
+                const int64_t dd = tile * kCh + cc;
+                const float v = dtv[k] + bias_on * bq[k];
+                const float ddt = sDel[cc][r] * hw_rcp(1.f + hw_exp2(-v * kLog2e));
                 // dz = dout (y + D x) SiLU'(z), SiLU'(z) = σ(z)(1 + z(1 - σ(z)))
-                const float zv = E::load(reinterpret_cast<const T *>(p.z) + i);
-                const float go = E::load(reinterpret_cast<const T *>(p.dout) + i);
-                const float sz = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
-                E::store(reinterpret_cast<T *>(p.dz) + i,
-                         go * sDY[cc][r] * sz * fmaf(zv, 1.f - sz, 1.f));
+                const float sz = hw_rcp(1.f + hw_exp2(-zq[k] * kLog2e));
+                const float dzv = gq[k] * sDY[cc][r] * sz * fmaf(zq[k], 1.f - sz, 1.f);
+                if (dd < p.D && r < nt) {
+                    const int64_t i = (b * p.D + dd) * p.L + t0 + r;
+                    sDel[cc][r] = ddt;
+                    E::store(reinterpret_cast<T *>(p.dx) + i, sX[cc][r]);
+                    E::store(reinterpret_cast<T *>(p.ddt) + i, ddt);
+                    if (p.dz)
+                        E::store(reinterpret_cast<T *>(p.dz) + i, dzv);
+                }
             }
         }
     }
