@@ -85,6 +85,31 @@ def test_state_update_matches_oracle(N, io, A_kind):
         assert_within(host(h), h_or, STATE_TOL, f"decode h step {step}")
 
 
+@pytest.mark.parametrize("opt", ["all_inputs", "no_optional"])
+def test_state_update_many_rows(opt):
+    """More batch rows than one launch's grid holds (65535: the step is launched
+    again for the rest) and D = 20 (the second run of 64 quads of a row is
+    partly past its end); with and without the optional inputs."""
+    import selective_state_space_80_amd as mamba
+    say(f"decode step B=65537 D=20 {opt}")
+    B, D, N = 65537, 20, 16
+    wl = W.DecodeWorkload("t", B, D, N, "bf16", 1, 1, 78)
+    init = W.decode_initial(wl)
+    s = W.decode_step_inputs(wl, 0)
+    full = opt == "all_inputs"
+    h = dev(init["h0"])
+    y = mamba.selective_state_update(
+        h, dev(s["x"], "bf16"), dev(s["dt"], "bf16"), dev(init["A"]), dev(s["Bm"], "bf16"),
+        dev(s["Cm"], "bf16"), dt_bias=dev(init["dt_bias"]) if full else None,
+        Dskip=dev(init["Dskip"]) if full else None, z=dev(s["z"], "bf16") if full else None)
+    yo, ho = oracle.state_update(init["h0"], s["x"], s["dt"], init["A"], s["Bm"], s["Cm"],
+                                 dt_bias=init["dt_bias"] if full else None,
+                                 Dskip=init["Dskip"] if full else None,
+                                 z=s["z"] if full else None)
+    assert_within(host(y), yo, TOL["bf16"], "decode y, many rows")
+    assert_within(host(h), ho, STATE_TOL, "decode h, many rows")
+
+
 def test_decode_steps_equal_scan():
     """L decode steps from h0 give the scan's outputs and final state."""
     import torch
