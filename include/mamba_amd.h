@@ -82,7 +82,8 @@ int mamba_abi_version(void);
  * "Mamba架构与SSM模型：高效序列建模技术解析", §3.2):
  *   out[b,d,t] = SiLU( bias[d] + sum_{k<K} w[d,k] * x[b,d,t-(K-1)+k] ),  x[t<0] = 0.
  *   x, out : [B, D, L] of `dtype`;  w : [D, K] float;  bias : [D] float or NULL.
- * out must not overlap x.  K in 1..8.
+ * out must not overlap x.  K in 1..8.  MAMBA_ERR_SHAPE also when
+ * B * D * ceil(L / 4) >= 2^32 (one launch covers the whole problem).
  */
 mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias, void *out,
                                int64_t B, int64_t D, int64_t L, int64_t K, mamba_dtype dtype,

@@ -130,7 +130,7 @@ mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias,
     if (overlap(ro, rng(x, (size_t)n * es)) || overlap(ro, rng(w, (size_t)(D * K) * 4)) ||
         (bias && overlap(ro, rng(bias, (size_t)D * 4))))
         return MAMBA_ERR_ALIAS;
-    if (B * D * ((L + 7) / 8) >= (int64_t(1) << 32))
+    if (B * D * ((L + 3) / 4) >= (int64_t(1) << 32))  // launch grid: one thread per 4 steps
         return MAMBA_ERR_SHAPE;
     mamba_status st = device_ok();
     if (st != MAMBA_OK)

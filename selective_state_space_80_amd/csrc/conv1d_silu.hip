@@ -4,9 +4,11 @@
 // "Mamba架构与SSM模型：高效序列建模技术解析" §3.2).
 //   out[b,d,t] = SiLU(bias_d + sum_{k<K} w[d,k] x[b,d,t-(K-1)+k]),  x[t<0] = 0
 // Streaming and HBM-bound (one read, one write per element): each thread makes
-// 8 consecutive outputs of one row from one 128-bit (bf16) or two 128-bit
-// (fp32) loads plus the previous 8 inputs as the left halo, which the
-// neighbouring thread loads too, so the halo comes from cache, not HBM.
+// the outputs of one 16-byte piece of a row (8 bf16 or 4 fp32 values), so
+// consecutive lanes read and write consecutive pieces and every load or store
+// instruction of a wave covers one contiguous kilobyte.  The left halo (K - 1
+// inputs) is the previous one or two pieces, which the neighbouring threads
+// load too, so it comes from cache, not HBM.
 #include "device_common.h"
 #include "internal.h"
 
@@ -14,16 +16,15 @@ namespace mamba {
 
 namespace {
 
-constexpr int kVT = 8;  // outputs per thread
+// One 16-byte piece of a row: 8 bf16 or 4 fp32 values.
+template <bool BF16> constexpr int kPiece = BF16 ? 8 : 4;
 
 template <bool BF16>
-__device__ __forceinline__ void load8(const void *base, int64_t off, float (&v)[kVT])
+__device__ __forceinline__ void load_piece(const void *base, int64_t off, float (&v)[kPiece<BF16>])
 {
     if constexpr (!BF16) {
-        const float4 *q = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
-        const float4 a = q[0], c = q[1];
+        const float4 a = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + off);
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
     } else {
         const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
         const uint32_t w4[4] = {a.x, a.y, a.z, a.w};
@@ -36,12 +37,11 @@ __device__ __forceinline__ void load8(const void *base, int64_t off, float (&v)[
 }
 
 template <bool BF16>
-__device__ __forceinline__ void store8(void *base, int64_t off, const float (&v)[kVT])
+__device__ __forceinline__ void store_piece(void *base, int64_t off, const float (&v)[kPiece<BF16>])
 {
     if constexpr (!BF16) {
-        float4 *q = reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + off);
-        q[0] = make_float4(v[0], v[1], v[2], v[3]);
-        q[1] = make_float4(v[4], v[5], v[6], v[7]);
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + off) =
+            make_float4(v[0], v[1], v[2], v[3]);
     } else {
         uint32_t w4[4];
 #pragma unroll
@@ -52,9 +52,65 @@ __device__ __forceinline__ void store8(void *base, int64_t off, const float (&v)
     }
 }
 
-// VEC: L % 8 == 0 and 16-byte aligned rows, so every thread's 8 outputs lie in
-// one row and the 8-element loads are aligned.
-template <bool BF16, bool VEC, int K>
+// Rows of whole 16-byte pieces (L a multiple of the piece, 16-byte aligned).
+// Grid (D, pieces / 256, B): the workgroup's channel and batch row come from
+// its indices (no division; the weights are the same for the whole
+// workgroup), thread t makes the outputs of piece 256 blockIdx.y + t.  Its
+// halo pieces are loaded unconditionally (a piece at the start of a row reads
+// itself) and zeroed where they would lie before the row.
+template <bool BF16, int K>
+__global__ void __launch_bounds__(256) conv1d_silu_piece_kernel(
+    const void *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    void *__restrict__ out, int64_t D, int64_t L)
+{
+    constexpr int V = kPiece<BF16>;
+    constexpr int HP = (K - 1 + V - 1) / V;  // halo pieces
+    const int64_t t0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * V;
+    if (t0 >= L)
+        return;
+    const int64_t d = blockIdx.x;
+    const int64_t base = ((int64_t)blockIdx.z * D + d) * L;
+    const float bias_raw = (bias ? bias : w)[d];
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        wk[k] = w[d * K + k];
+    float win[(HP + 1) * V];  // x[t0 - HP V .. t0 + V - 1]
+    {
+        float v[V];
+        load_piece<BF16>(x, base + t0, v);
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            win[HP * V + k] = v[k];
+    }
+#pragma unroll
+    for (int h = 1; h <= HP; ++h) {
+        float v[V];
+        const bool in_row = t0 >= h * V;
+        load_piece<BF16>(x, base + (in_row ? t0 - h * V : t0), v);
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            win[(HP - h) * V + k] = in_row ? v[k] : 0.f;
+    }
+    const float bv = bias ? bias_raw : 0.f;
+    float res[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        // tap k multiplies x[t0 + j - (K-1) + k]
+        float acc = bv;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            acc = fmaf(wk[k], win[HP * V + j - (K - 1) + k], acc);
+        res[j] = silu_hw(acc);
+    }
+    store_piece<BF16>(out, base + t0, res);
+}
+
+// Other rows (L not a multiple of the piece, or unaligned): kVT outputs per
+// thread, element loads with bounds checks.
+constexpr int kVT = 8;
+
+template <bool BF16, int K>
 __global__ void __launch_bounds__(256) conv1d_silu_kernel(
     const void *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     void *__restrict__ out, int64_t D, int64_t L, int64_t vec_per_row, int64_t n_threads)
@@ -70,28 +126,11 @@ __global__ void __launch_bounds__(256) conv1d_silu_kernel(
     const int64_t base = row * L;
 
     float win[2 * kVT];  // x[t0-8 .. t0+7]
-    if constexpr (VEC) {
-        float cur[kVT], prev[kVT];
-        load8<BF16>(x, base + t0, cur);
-        if (t0 > 0) {
-            load8<BF16>(x, base + t0 - kVT, prev);
-        } else {
+    const T *xr = reinterpret_cast<const T *>(x) + base;
 #pragma unroll
-            for (int k = 0; k < kVT; ++k)
-                prev[k] = 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < kVT; ++k) {
-            win[k] = prev[k];
-            win[kVT + k] = cur[k];
-        }
-    } else {
-        const T *xr = reinterpret_cast<const T *>(x) + base;
-#pragma unroll
-        for (int k = 0; k < 2 * kVT; ++k) {
-            const int64_t t = t0 - kVT + k;
-            win[k] = (t >= 0 && t < L) ? E::load(xr + t) : 0.f;
-        }
+    for (int k = 0; k < 2 * kVT; ++k) {
+        const int64_t t = t0 - kVT + k;
+        win[k] = (t >= 0 && t < L) ? E::load(xr + t) : 0.f;
     }
 
     const float bv = bias ? bias[d] : 0.f;
@@ -99,7 +138,7 @@ __global__ void __launch_bounds__(256) conv1d_silu_kernel(
 #pragma unroll
     for (int k = 0; k < K; ++k)
         wk[k] = w[d * K + k];
-    float res[kVT];
+    T *orow = reinterpret_cast<T *>(out) + base;
 #pragma unroll
     for (int j = 0; j < kVT; ++j) {
         // tap k multiplies x[t - (K-1) + k], i.e. window index kVT + j - (K-1) + k
@@ -107,33 +146,27 @@ __global__ void __launch_bounds__(256) conv1d_silu_kernel(
 #pragma unroll
         for (int k = 0; k < K; ++k)
             acc = fmaf(wk[k], win[kVT + j - (K - 1) + k], acc);
-        res[j] = silu_hw(acc);
-    }
-
-    if constexpr (VEC) {
-        store8<BF16>(out, base + t0, res);
-    } else {
-        T *orow = reinterpret_cast<T *>(out) + base;
-#pragma unroll
-        for (int j = 0; j < kVT; ++j)
-            if (t0 + j < L)
-                E::store(orow + t0 + j, res[j]);
+        if (t0 + j < L)
+            E::store(orow + t0 + j, silu_hw(acc));
     }
 }
 
 template <bool BF16, int K>
 hipError_t launch_typed(const ConvArgs &a, hipStream_t s)
 {
+    constexpr int V = kPiece<BF16>;
+    const int64_t piece_blocks = (a.L / V + 255) / 256;
+    if (a.L % V == 0 && (((uintptr_t)a.x | (uintptr_t)a.out) % 16 == 0) && a.B <= 65535 &&
+        piece_blocks <= 65535 && a.D < (int64_t(1) << 31)) {
+        hipLaunchKernelGGL((conv1d_silu_piece_kernel<BF16, K>),
+                           dim3((unsigned)a.D, (unsigned)piece_blocks, (unsigned)a.B), dim3(256), 0,
+                           s, a.x, a.w, a.bias, a.out, a.D, a.L);
+        return hipGetLastError();
+    }
     const int64_t vpr = (a.L + kVT - 1) / kVT;
     const int64_t n = a.B * a.D * vpr;
-    const unsigned blocks = (unsigned)((n + 255) / 256);
-    const bool vec = (a.L % kVT == 0) && (((uintptr_t)a.x | (uintptr_t)a.out) % 16 == 0);
-    if (vec)
-        hipLaunchKernelGGL((conv1d_silu_kernel<BF16, true, K>), dim3(blocks), dim3(256), 0, s,
-                           a.x, a.w, a.bias, a.out, a.D, a.L, vpr, n);
-    else
-        hipLaunchKernelGGL((conv1d_silu_kernel<BF16, false, K>), dim3(blocks), dim3(256), 0, s,
-                           a.x, a.w, a.bias, a.out, a.D, a.L, vpr, n);
+    hipLaunchKernelGGL((conv1d_silu_kernel<BF16, K>), dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, a.x, a.w, a.bias, a.out, a.D, a.L, vpr, n);
     return hipGetLastError();
 }
 

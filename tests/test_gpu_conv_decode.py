@@ -30,6 +30,38 @@ def test_conv_matches_oracle(K, io, L):
     assert_within(host(out), want, CONV_TOL[io], "conv")
 
 
+@pytest.mark.parametrize("case", ["many_rows", "unaligned"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_fallback_layouts(case, io):
+    """Rows of whole 16-byte pieces that still take the bounds-checked kernel:
+    65537 batch rows (beyond one launch dimension), or input and output that
+    start one element past a 16-byte boundary."""
+    import torch
+    import selective_state_space_80_amd as mamba
+    say(f"conv fallback {case} io={io}")
+    rng = np.random.default_rng(77)
+    B, D, L, K = (65537, 1, 16, 4) if case == "many_rows" else (3, 5, 64, 4)
+    x = rng.standard_normal((B, D, L)).astype(np.float32)
+    if io == "bf16":
+        x = W.round_bf16(x)
+    w = (0.5 * rng.standard_normal((D, K))).astype(np.float32)
+    bias = rng.standard_normal(D).astype(np.float32)
+    xd = dev(x, io)
+    if case == "unaligned":
+        n = x.size
+        buf = torch.zeros(n + 1, dtype=xd.dtype, device="cuda")
+        buf[1:].copy_(xd.reshape(-1))
+        xd = buf[1:].view(B, D, L)
+        obuf = torch.empty(n + 1, dtype=xd.dtype, device="cuda")
+        out = obuf[1:].view(B, D, L)
+        assert xd.data_ptr() % 16 != 0 and out.data_ptr() % 16 != 0
+        mamba.conv1d_silu(xd, dev(w), dev(bias), out=out)
+    else:
+        out = mamba.conv1d_silu(xd, dev(w), dev(bias))
+    want = oracle.conv1d_silu(x, w, bias)
+    assert_within(host(out), want, CONV_TOL[io], "conv")
+
+
 def test_block_workload_sampled():
     """The d_model=768 block: conv1d(k=4)+SiLU feeding the scan, full size,
     checked on sampled channels (oracle conv then oracle scan in fp64)."""
