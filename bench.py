@@ -540,10 +540,19 @@ def run_decode(args, torch, mamba, W):
         st = W.decode_step_inputs(wl, s)
         toks.append({k: T(v, torch.bfloat16) for k, v in st.items()})
     y = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
+    K = 4
+    if args.with_conv:
+        ci = W.decode_conv_initial(wl, K)
+        cw, cstate = T(ci["conv_w"]), T(ci["conv_state"], torch.bfloat16)
+        xc = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
 
     def step(i):
         t = toks[i % len(toks)]
-        mamba.selective_state_update(h, t["x"], t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"],
+        x = t["x"]
+        if args.with_conv:  # the token's raw input through the conv front end first
+            mamba.conv1d_update(cstate, x, cw, None, out=xc)
+            x = xc
+        mamba.selective_state_update(h, x, t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"],
                                      out=y)
 
     for i in range(args.warmup):
@@ -557,12 +566,19 @@ def run_decode(args, torch, mamba, W):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     nbytes = wl.B * wl.D * (2 * wl.N * 4 + 4 * 2) + wl.B * 2 * wl.N * 2 + wl.D * (wl.N + 2) * 4
+    if args.with_conv:  # window read and written, raw input read, conv output written
+        # (the state update above counts reading it back)
+        nbytes += wl.B * wl.D * (2 * (K - 1) + 2) * 2 + wl.D * K * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"metric": "decode state update GB/s", "value": round(gbs, 1), "unit": "GB/s",
+    metric = ("decode step (conv update + state update) GB/s" if args.with_conv else
+              "decode state update GB/s")
+    return {"metric": metric, "value": round(gbs, 1), "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16-io/f32", "data": "synthetic",
-            "config": {"workload": wl.name, "batch": wl.B, "d_inner": wl.D, "d_state": wl.N},
+            "config": {"workload": wl.name, "batch": wl.B, "d_inner": wl.D, "d_state": wl.N,
+                       **({"d_conv": K, "step": "conv1d_update, then selective_state_update"}
+                          if args.with_conv else {})},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "note": "state (84 MB) stays resident in the 256 MB MALL between steps"}}
@@ -583,6 +599,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
                          "instead of the fused entry point")
+    ap.add_argument("--with-conv", action="store_true",
+                    help="decode workload: each step runs the conv front end's decode step "
+                         "(conv1d_update, K = 4) on the token's raw input before the state update")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one elementwise kernel that reads and writes "
                          "this many MiB (known traffic for scaling rocprofv3 byte counters)")

@@ -9,6 +9,8 @@
 // instruction of a wave covers one contiguous kilobyte.  The left halo (K - 1
 // inputs) is the previous one or two pieces, which the neighbouring threads
 // load too, so it comes from cache, not HBM.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -190,51 +192,152 @@ hipError_t launch_k(const ConvArgs &a, hipStream_t s)
 // raw inputs carried in `state` ([B, D, K-1], oldest first).
 //   out[b,d] = SiLU(bias_d + sum_{k<K-1} w[d,k] state[b,d,k] + w[d,K-1] x[b,d])
 //   state[b,d,:] <- (state[b,d,1:], x[b,d])
-// One thread per channel; the state moves by one slot in place.
-template <bool BF16>
+// One thread per channel on a (channel block, batch row) grid, so no thread
+// divides; the window is read whole before the state moves by one slot in
+// place.
+template <bool BF16, int K>
 __global__ void __launch_bounds__(256) conv1d_update_kernel(void *__restrict__ state_,
                                                             const void *__restrict__ x_,
                                                             const float *__restrict__ w,
                                                             const float *__restrict__ bias,
                                                             void *__restrict__ out_, int64_t D,
-                                                            int64_t n, int K)
+                                                            int64_t b0)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n)
+    const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (d >= D)
         return;
-    const int64_t d = i % D;
+    const int64_t i = (b0 + blockIdx.y) * D + d;
     T *state = reinterpret_cast<T *>(state_) + i * (K - 1);
-    const T xraw = reinterpret_cast<const T *>(x_)[i];
-    float acc = bias ? bias[d] : 0.f;
-    for (int k = 0; k < K - 1; ++k) {
-        const T v = state[k];
-        acc = fmaf(w[d * K + k], E::load(&v), acc);
-        if (k > 0)
-            state[k - 1] = v;
-    }
-    acc = fmaf(w[d * K + K - 1], E::load(&xraw), acc);
-    if (K > 1)
-        state[K - 2] = xraw;
+    T win[K];  // the K inputs of this step, oldest first
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+        win[k] = state[k];
+    win[K - 1] = reinterpret_cast<const T *>(x_)[i];
+    const float bias_raw = (bias ? bias : w)[d];
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        wk[k] = w[d * K + k];
+    float acc = bias ? bias_raw : 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        acc = fmaf(wk[k], E::load(&win[k]), acc);
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+        state[k] = win[k + 1];
     E::store(reinterpret_cast<T *>(out_) + i, silu_hw(acc));
+}
+
+// The same step for rows of whole pieces: thread t owns the C channels of one
+// 16-byte piece of x (C = 8 bf16 or 4 fp32).  Their windows are C (K-1)
+// consecutive state values, i.e. K-1 whole pieces, and their weights C K
+// consecutive floats, so every access is a 16-byte one and each wave's loads
+// and stores cover contiguous runs.  Needs D a multiple of C and 16-byte
+// aligned state, x, out, w (and bias).
+template <bool BF16, int K>
+__global__ void __launch_bounds__(256) conv1d_update_piece_kernel(void *__restrict__ state_,
+                                                                  const void *__restrict__ x_,
+                                                                  const float *__restrict__ w,
+                                                                  const float *__restrict__ bias,
+                                                                  void *__restrict__ out_,
+                                                                  int64_t D, int64_t b0)
+{
+    constexpr int C = kPiece<BF16>;
+    const int64_t d0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * C;
+    if (d0 >= D)
+        return;
+    const int64_t i0 = (b0 + blockIdx.y) * D + d0;  // flat index of the first channel
+    float st[(K - 1) * C + 1];  // channel c's window at c (K-1) .. c (K-1) + K-2
+#pragma unroll
+    for (int q = 0; q < K - 1; ++q) {
+        float v[C];
+        load_piece<BF16>(state_, i0 * (K - 1) + q * C, v);
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+            st[q * C + k] = v[k];
+    }
+    float xv[C];
+    load_piece<BF16>(x_, i0, xv);
+    float wv[C * K];
+#pragma unroll
+    for (int q = 0; q < C * K / 4; ++q) {
+        const float4 a = reinterpret_cast<const float4 *>(w + d0 * K)[q];
+        wv[4 * q] = a.x; wv[4 * q + 1] = a.y; wv[4 * q + 2] = a.z; wv[4 * q + 3] = a.w;
+    }
+    float bv[C];
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) {
+        const float4 a = reinterpret_cast<const float4 *>((bias ? bias : w) + d0)[q];
+        bv[4 * q] = a.x; bv[4 * q + 1] = a.y; bv[4 * q + 2] = a.z; bv[4 * q + 3] = a.w;
+    }
+    float res[C], ns[(K - 1) * C + 1];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        float acc = bias ? bv[c] : 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            acc = fmaf(wv[c * K + k], k < K - 1 ? st[c * (K - 1) + k] : xv[c], acc);
+        res[c] = silu_hw(acc);
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j)
+            ns[c * (K - 1) + j] = j < K - 2 ? st[c * (K - 1) + j + 1] : xv[c];
+    }
+#pragma unroll
+    for (int q = 0; q < K - 1; ++q) {
+        float v[C];
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+            v[k] = ns[q * C + k];
+        store_piece<BF16>(state_, i0 * (K - 1) + q * C, v);
+    }
+    store_piece<BF16>(out_, i0, res);
+}
+
+template <bool BF16, int K>
+hipError_t launch_update_typed(const ConvUpdateArgs &a, hipStream_t s)
+{
+    constexpr int C = kPiece<BF16>;
+    const bool pieces = a.D % C == 0 &&
+                        (((uintptr_t)a.state | (uintptr_t)a.x | (uintptr_t)a.out |
+                          (uintptr_t)a.w | (uintptr_t)a.bias) % 16) == 0;
+    const unsigned gx = (unsigned)((pieces ? a.D / C + 255 : a.D + 255) / 256);
+    for (int64_t b0 = 0; b0 < a.B; b0 += 65535) {
+        const unsigned gy = (unsigned)std::min<int64_t>(a.B - b0, 65535);
+        if (pieces)
+            hipLaunchKernelGGL((conv1d_update_piece_kernel<BF16, K>), dim3(gx, gy), dim3(256), 0,
+                               s, a.state, a.x, a.w, a.bias, a.out, a.D, b0);
+        else
+            hipLaunchKernelGGL((conv1d_update_kernel<BF16, K>), dim3(gx, gy), dim3(256), 0, s,
+                               a.state, a.x, a.w, a.bias, a.out, a.D, b0);
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_update_k(const ConvUpdateArgs &a, hipStream_t s)
+{
+    switch (a.K) {
+    case 1: return launch_update_typed<BF16, 1>(a, s);
+    case 2: return launch_update_typed<BF16, 2>(a, s);
+    case 3: return launch_update_typed<BF16, 3>(a, s);
+    case 4: return launch_update_typed<BF16, 4>(a, s);
+    case 5: return launch_update_typed<BF16, 5>(a, s);
+    case 6: return launch_update_typed<BF16, 6>(a, s);
+    case 7: return launch_update_typed<BF16, 7>(a, s);
+    case 8: return launch_update_typed<BF16, 8>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s)
 {
-    const int64_t n = a.B * a.D;
-    if (n == 0)
+    if (a.B * a.D == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((n + 255) / 256));
-    if (a.bf16)
-        hipLaunchKernelGGL(conv1d_update_kernel<true>, grid, dim3(256), 0, s, a.state, a.x, a.w,
-                           a.bias, a.out, a.D, n, a.K);
-    else
-        hipLaunchKernelGGL(conv1d_update_kernel<false>, grid, dim3(256), 0, s, a.state, a.x, a.w,
-                           a.bias, a.out, a.D, n, a.K);
-    return hipGetLastError();
+    return a.bf16 ? launch_update_k<true>(a, s) : launch_update_k<false>(a, s);
 }
 
 hipError_t launch_conv1d_silu(const ConvArgs &a, hipStream_t s)

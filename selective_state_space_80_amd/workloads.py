@@ -170,6 +170,18 @@ def decode_step_inputs(wl: DecodeWorkload, step: int, seed: int | None = None):
     return out
 
 
+def decode_conv_initial(wl: DecodeWorkload, K: int = 4, seed: int | None = None):
+    """The conv front end of a decode run: weights [D,K] ~ N(0, 0.5) (as in the
+    block workload) and the carried window of K-1 raw inputs [B,D,K-1] ~ N(0,1)
+    (bf16-exact for bf16 I/O).  Each step's raw input is that step's x."""
+    rng = np.random.default_rng([wl.seed if seed is None else seed, 0, K])
+    w = _normal(rng, (wl.D, K), 0.5)
+    state = _normal(rng, (wl.B, wl.D, K - 1))
+    if wl.io == "bf16":
+        state = round_bf16(state)
+    return {"conv_w": w, "conv_state": state}
+
+
 def make_ssd_inputs(B: int, L: int, H: int, P: int, G: int, N: int, seed: int = 0):
     """Draw one Mamba-2-form problem (bf16 I/O).  Returns float32 numpy arrays
     holding bf16-exact values: x, z [B,L,H,P]; dt [B,L,H]; Bm, Cm [B,L,G,N];

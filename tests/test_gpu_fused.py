@@ -160,13 +160,15 @@ def test_fused_conv_state_in_place(L):
     assert np.array_equal(host(st), want) and np.array_equal(host(cs_sep), want)
 
 
-@pytest.mark.parametrize("K", [1, 2, 4, 8])
+# D = 320 takes the 16-byte piece kernel, D = 333 the per-channel one
+@pytest.mark.parametrize("D", [320, 333])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_conv_update_matches_oracle(K, io):
+def test_conv_update_matches_oracle(K, io, D):
     import selective_state_space_80_amd as mamba
-    say(f"conv update K={K} io={io}")
+    say(f"conv update K={K} io={io} D={D}")
     rng = np.random.default_rng(40 + K)
-    B, D, T = 3, 333, 6
+    B, T = 3, 6
     w = (0.5 * rng.standard_normal((D, K))).astype(np.float32)
     bias = rng.standard_normal(D).astype(np.float32) if K != 2 else None
     st0 = rng.standard_normal((B, D, K - 1)).astype(np.float32)
@@ -182,6 +184,32 @@ def test_conv_update_matches_oracle(K, io):
         assert_within(host(out), want, CONV_TOL[io], f"conv update t={t}")
         if K > 1:
             assert np.array_equal(host(st), st_or), "conv window"
+
+
+@pytest.mark.parametrize("D", [8, 3])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_update_many_rows(io, D):
+    """65537 batch rows: more than one launch covers (the rows go in slices of
+    65535), two steps, every output and window checked; D = 8 takes the
+    16-byte piece kernel, D = 3 the per-channel one."""
+    import selective_state_space_80_amd as mamba
+    say(f"conv update many rows io={io} D={D}")
+    rng = np.random.default_rng(48)
+    B, K = 65537, 4
+    w = (0.5 * rng.standard_normal((D, K))).astype(np.float32)
+    bias = rng.standard_normal(D).astype(np.float32)
+    st0 = rng.standard_normal((B, D, K - 1)).astype(np.float32)
+    xs = rng.standard_normal((B, D, 2)).astype(np.float32)
+    if io == "bf16":
+        st0, xs = W.round_bf16(st0), W.round_bf16(xs)
+    st = dev(st0, io)
+    st_or = st0.astype(np.float64)
+    for t in range(2):
+        out = mamba.conv1d_update(st, dev(np.ascontiguousarray(xs[:, :, t]), io), dev(w),
+                                  dev(bias))
+        want, st_or = oracle.conv1d_update(st_or, xs[:, :, t], w, bias)
+        assert_within(host(out), want, CONV_TOL[io], f"conv update t={t}")
+        assert np.array_equal(host(st), st_or), "conv window"
 
 
 def test_block_workload_fused_sampled():

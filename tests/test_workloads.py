@@ -63,3 +63,7 @@ def test_decode_recipe():
     assert h["h0"].shape == (3, 5, 16) and s0["x"].shape == (3, 5)
     assert s0["Bm"].shape == (3, 16) and not np.array_equal(s0["x"], s1["x"])
     assert np.array_equal(W.decode_step_inputs(wl, 1)["x"], s1["x"])
+    c = W.decode_conv_initial(wl)
+    assert c["conv_w"].shape == (5, 4) and c["conv_state"].shape == (3, 5, 3)
+    assert np.array_equal(W.round_bf16(c["conv_state"]), c["conv_state"])
+    assert np.array_equal(W.decode_conv_initial(wl)["conv_w"], c["conv_w"])
