@@ -549,6 +549,10 @@ def run_decode(args, torch, mamba, W):
     def step(i):
         t = toks[i % len(toks)]
         x = t["x"]
+        if args.with_conv and not args.unfused:  # conv front end and state update in one kernel
+            mamba.conv1d_selective_state_update(h, cstate, x, cw, t["dt"], A, t["Bm"], t["Cm"],
+                                                dt_bias=bias, Dskip=Dk, z=t["z"], out=y)
+            return
         if args.with_conv:  # the token's raw input through the conv front end first
             mamba.conv1d_update(cstate, x, cw, None, out=xc)
             x = xc
@@ -566,9 +570,9 @@ def run_decode(args, torch, mamba, W):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     nbytes = wl.B * wl.D * (2 * wl.N * 4 + 4 * 2) + wl.B * 2 * wl.N * 2 + wl.D * (wl.N + 2) * 4
-    if args.with_conv:  # window read and written, raw input read, conv output written
-        # (the state update above counts reading it back)
-        nbytes += wl.B * wl.D * (2 * (K - 1) + 2) * 2 + wl.D * K * 4
+    if args.with_conv:  # window read and written (the state update above counts the raw
+        # input's read; the conv output never reaches memory when fused)
+        nbytes += wl.B * wl.D * 2 * (K - 1) * 2 + wl.D * K * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     metric = ("decode step (conv update + state update) GB/s" if args.with_conv else
               "decode state update GB/s")
@@ -577,7 +581,9 @@ def run_decode(args, torch, mamba, W):
             "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16-io/f32", "data": "synthetic",
             "config": {"workload": wl.name, "batch": wl.B, "d_inner": wl.D, "d_state": wl.N,
-                       **({"d_conv": K, "step": "conv1d_update, then selective_state_update"}
+                       **({"d_conv": K,
+                           "step": ("conv1d_update, then selective_state_update" if args.unfused
+                                    else "conv1d_selective_state_update (one kernel)")}
                           if args.with_conv else {})},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
@@ -598,10 +604,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--unfused", action="store_true",
                     help="block workload: run conv1d_silu and selective_scan_fwd as two calls "
-                         "instead of the fused entry point")
+                         "instead of the fused entry point; decode --with-conv: conv1d_update "
+                         "and selective_state_update as two calls")
     ap.add_argument("--with-conv", action="store_true",
                     help="decode workload: each step runs the conv front end's decode step "
-                         "(conv1d_update, K = 4) on the token's raw input before the state update")
+                         "(K = 4) on the token's raw input, then the state update, fused into "
+                         "one kernel (conv1d_selective_state_update)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one elementwise kernel that reads and writes "
                          "this many MiB (known traffic for scaling rocprofv3 byte counters)")

@@ -6,9 +6,10 @@
  *   mamba_selective_scan_fwd     fused selective-scan forward (prefill)
  *   mamba_selective_state_update single-token recurrent step (decode)
  * the scan with direction / accumulate flags (mamba_selective_scan_fwd_ex),
- * and two that join the front end to the scan:
- *   mamba_conv1d_selective_scan_fwd  conv1d + SiLU fused into the scan
- *   mamba_conv1d_update              single-token conv step with its state
+ * and three that join the front end to the scan:
+ *   mamba_conv1d_selective_scan_fwd      conv1d + SiLU fused into the scan
+ *   mamba_conv1d_update                  single-token conv step with its state
+ *   mamba_conv1d_selective_state_update  that conv step and the decode step fused
  * the scan's backward pass (mamba_selective_scan_bwd), the Mamba-2 form of
  * the scan on the matrix cores (mamba_ssd_scan_fwd),
  * plus workspace sizing and status helpers.
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 5
+#define MAMBA_AMD_ABI_VERSION 6
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
@@ -210,6 +211,30 @@ mamba_status mamba_conv1d_selective_scan_fwd(
 mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, const float *bias,
                                  void *out, int64_t B, int64_t D, int64_t K, mamba_dtype dtype,
                                  void *stream);
+
+/*
+ * The block's whole decode step in one pass: the front end's decode step
+ * (mamba_conv1d_update) on the raw input x_raw, whose output feeds the state
+ * update (mamba_selective_state_update) as its x (the D skip included), in
+ * one kernel ("Mamba架构深度剖析：如何以线性时间重塑序列建模", §3: recurrent
+ * inference, each token advancing a fixed-size state; "Mamba状态空间模型深度
+ * 解析：挑战Transformer的下一代序列建模范式", §3.1: conv1d + SiLU in front of
+ * the SSM).  Same result as mamba_conv1d_update followed by
+ * mamba_selective_state_update, except that the conv output is not rounded to
+ * `io` in between.
+ *   conv_state : [B, D, K-1] of `io`, read and overwritten with the last K-1
+ *                raw inputs (may be NULL when K = 1)
+ *   x_raw      : [B, D] of `io`;  conv_w : [D, K] float, K in 1..4
+ *                (MAMBA_MAX_FUSED_CONV_TAPS);  conv_bias : [D] float or NULL
+ * Every other argument is as for mamba_selective_state_update.  y must not
+ * overlap h, conv_state or any input; conv_state must not overlap h or any
+ * input.
+ */
+mamba_status mamba_conv1d_selective_state_update(
+    float *h, void *conv_state, const void *x_raw, const float *conv_w, const float *conv_bias,
+    int64_t K, const void *dt, const float *dt_bias, const float *A, const void *Bm,
+    const void *Cm, const float *Dskip, const void *z, void *y, int64_t B, int64_t D, int64_t N,
+    mamba_dtype io, void *stream);
 
 /*
  * Backward pass of the selective scan ("Mamba状态空间模型深度解析：挑战

@@ -45,7 +45,7 @@ EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_conv1d_selective_scan_fwd",
             "mamba_conv1d_update", "mamba_set_scan_timing_events",
             "mamba_selective_scan_bwd_workspace_size", "mamba_selective_scan_bwd",
-            "mamba_ssd_scan_fwd"]
+            "mamba_ssd_scan_fwd", "mamba_conv1d_selective_state_update"]
 
 _lib = None
 
@@ -86,6 +86,9 @@ def load_library(path: str = LIBRARY):
                                                     [SZ, I64, I64, I64, I64, I32, P])
     lib.mamba_conv1d_update.restype = I32
     lib.mamba_conv1d_update.argtypes = [P] * 5 + [I64, I64, I64, I32, P]
+    lib.mamba_conv1d_selective_state_update.restype = I32
+    lib.mamba_conv1d_selective_state_update.argtypes = [P] * 5 + [I64] + [P] * 8 + [I64, I64, I64,
+                                                                                  I32, P]
     lib.mamba_selective_scan_bwd_workspace_size.restype = SZ
     lib.mamba_selective_scan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I32]
     lib.mamba_selective_scan_bwd.restype = I32
@@ -322,6 +325,41 @@ def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None
         _ptr(h), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
         _ptr(z), _ptr(out), B, D, N, _io_dtype(x), _stream(dev))
     _raise(st, "mamba_selective_state_update")
+    return out
+
+
+def conv1d_selective_state_update(h, conv_state, x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None,
+                                  dt_bias=None, Dskip=None, z=None, out=None):
+    """The block's decode step in one kernel: the conv front end's step on the
+    raw input x_raw [B,D] (conv_state [B,D,K-1] of x_raw's dtype, updated in
+    place; conv_w [D,K] f32 with K <= 4, conv_bias [D] f32), feeding the state
+    update of h [B,D,N] f32 (in place).  Other arguments as for
+    selective_state_update.  Returns y [B,D] of x_raw's dtype."""
+    torch = _torch()
+    lib = load_library()
+    B, D, N = h.shape
+    K = conv_w.shape[1]
+    dev, io_t = h.device, x_raw.dtype
+    _check(h, "h", (B, D, N), torch.float32, dev)
+    _check(conv_state, "conv_state", (B, D, K - 1), io_t, dev, optional=K == 1)
+    _check(x_raw, "x_raw", (B, D), io_t, dev)
+    _check(conv_w, "conv_w", (D, K), torch.float32, dev)
+    _check(conv_bias, "conv_bias", (D,), torch.float32, dev, optional=True)
+    _check(dt, "dt", (B, D), io_t, dev)
+    _check(z, "z", (B, D), io_t, dev, optional=True)
+    _check(Bm, "Bm", (B, N), io_t, dev)
+    _check(Cm, "Cm", (B, N), io_t, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (D,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty_like(x_raw)
+    _check(out, "out", (B, D), io_t, dev)
+    st = lib.mamba_conv1d_selective_state_update(
+        _ptr(h), _ptr(conv_state), _ptr(x_raw), _ptr(conv_w), _ptr(conv_bias), K, _ptr(dt),
+        _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(out), B, D, N,
+        _io_dtype(x_raw), _stream(dev))
+    _raise(st, "mamba_conv1d_selective_state_update")
     return out
 
 

@@ -278,6 +278,62 @@ mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
     return launched(mamba::launch_selective_scan(a, (hipStream_t)stream));
 }
 
+// Shared body of the two decode entry points.  conv_K = 0: x is the scan
+// input; conv_K in 1..4: x is the raw input of the fused conv front end, whose
+// window conv_state is updated in place.
+mamba_status step_entry(float *h, void *conv_state, const void *x, int64_t conv_K,
+                        const float *conv_w, const float *conv_b, const void *dt,
+                        const float *dt_bias, const float *A, const void *Bm, const void *Cm,
+                        const float *Dskip, const void *z, void *y, int64_t B, int64_t D,
+                        int64_t N, mamba_dtype io, void *stream)
+{
+    if (!valid_dtype(io))
+        return MAMBA_ERR_DTYPE;
+    if (!sizes_ok(B, D, 1) || N < 0 || conv_K < 0)
+        return MAMBA_ERR_SHAPE;
+    if (N < 1 || N > kMaxN || conv_K > mamba::kFusedConvTaps)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (B * D == 0)
+        return MAMBA_OK;
+    const bool conv = conv_K != 0;
+    if (!h || !x || !dt || !A || !Bm || !Cm || !y || (conv && !conv_w) ||
+        (conv_K > 1 && !conv_state))
+        return MAMBA_ERR_NULL;
+    const size_t es = esize(io);
+    if (!aligned(h, 4) || !aligned(x, es) || !aligned(dt, es) || !aligned(z, es) ||
+        !aligned(y, es) || !aligned(Bm, es) || !aligned(Cm, es) || !aligned(A, 4) ||
+        !aligned(dt_bias, 4) || !aligned(Dskip, 4) || !aligned(conv_state, es) ||
+        !aligned(conv_w, 4) || !aligned(conv_b, 4))
+        return MAMBA_ERR_ALIGN;
+    const int64_t n = B * D;
+    const Range ry = rng(y, (size_t)n * es);
+    const Range rh = rng(h, (size_t)(n * N) * 4);
+    const Range rc = rng(conv_state, conv_K > 1 ? (size_t)(n * (conv_K - 1)) * es : 0);
+    const Range ins[] = {rng(x, (size_t)n * es), rng(dt, (size_t)n * es),
+                         rng(z, z ? (size_t)n * es : 0), rng(Bm, (size_t)(B * N) * es),
+                         rng(Cm, (size_t)(B * N) * es), rng(A, (size_t)(D * N) * 4),
+                         rng(dt_bias, dt_bias ? (size_t)D * 4 : 0),
+                         rng(Dskip, Dskip ? (size_t)D * 4 : 0),
+                         rng(conv_w, conv ? (size_t)(D * conv_K) * 4 : 0),
+                         rng(conv_b, conv && conv_b ? (size_t)D * 4 : 0)};
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rh, r) || overlap(rc, r))
+            return MAMBA_ERR_ALIAS;
+    if (overlap(ry, rh) || overlap(ry, rc) || overlap(rh, rc))
+        return MAMBA_ERR_ALIAS;
+    if ((n * 4 + 255) / 256 >= (int64_t(1) << 31))  // launch grid (four lanes per channel)
+        return MAMBA_ERR_SHAPE;
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    mamba::StepArgs a{h, x, dt, Bm, Cm, z, dt_bias, A, Dskip, y, B, D, (int)N, io == MAMBA_BF16};
+    a.conv_K = (int)conv_K;
+    a.conv_state = conv_state;
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    return launched(mamba::launch_state_update(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -364,43 +420,23 @@ mamba_status mamba_selective_state_update(float *h, const void *x, const void *d
                                           const void *z, void *y, int64_t B, int64_t D,
                                           int64_t N, mamba_dtype io, void *stream)
 {
-    if (!valid_dtype(io))
-        return MAMBA_ERR_DTYPE;
-    if (!sizes_ok(B, D, 1) || N < 0)
-        return MAMBA_ERR_SHAPE;
-    if (N < 1 || N > kMaxN)
-        return MAMBA_ERR_UNSUPPORTED;
-    if (B * D == 0)
-        return MAMBA_OK;
-    if (!h || !x || !dt || !A || !Bm || !Cm || !y)
-        return MAMBA_ERR_NULL;
-    const size_t es = esize(io);
-    if (!aligned(h, 4) || !aligned(x, es) || !aligned(dt, es) || !aligned(z, es) ||
-        !aligned(y, es) || !aligned(Bm, es) || !aligned(Cm, es) || !aligned(A, 4) ||
-        !aligned(dt_bias, 4) || !aligned(Dskip, 4))
-        return MAMBA_ERR_ALIGN;
-    const int64_t n = B * D;
-    const Range ry = rng(y, (size_t)n * es);
-    const Range rh = rng(h, (size_t)(n * N) * 4);
-    const Range ins[] = {rng(x, (size_t)n * es), rng(dt, (size_t)n * es),
-                         rng(z, z ? (size_t)n * es : 0), rng(Bm, (size_t)(B * N) * es),
-                         rng(Cm, (size_t)(B * N) * es), rng(A, (size_t)(D * N) * 4),
-                         rng(dt_bias, dt_bias ? (size_t)D * 4 : 0),
-                         rng(Dskip, Dskip ? (size_t)D * 4 : 0)};
-    for (const Range &r : ins)
-        if (overlap(ry, r) || overlap(rh, r))
-            return MAMBA_ERR_ALIAS;
-    if (overlap(ry, rh))
-        return MAMBA_ERR_ALIAS;
-    if ((n * 4 + 255) / 256 >= (int64_t(1) << 31))  // launch grid (four lanes per channel)
-        return MAMBA_ERR_SHAPE;
-    mamba_status st = device_ok();
-    if (st != MAMBA_OK)
-        return st;
-    mamba::StepArgs a{h, x, dt, Bm, Cm, z, dt_bias, A, Dskip, y, B, D, (int)N, io == MAMBA_BF16};
-    return launched(mamba::launch_state_update(a, (hipStream_t)stream));
+    return step_entry(h, nullptr, x, 0, nullptr, nullptr, dt, dt_bias, A, Bm, Cm, Dskip, z, y, B,
+                      D, N, io, stream);
 }
 
+mamba_status mamba_conv1d_selective_state_update(
+    float *h, void *conv_state, const void *x_raw, const float *conv_w, const float *conv_bias,
+    int64_t K, const void *dt, const float *dt_bias, const float *A, const void *Bm,
+    const void *Cm, const float *Dskip, const void *z, void *y, int64_t B, int64_t D, int64_t N,
+    mamba_dtype io, void *stream)
+{
+    if (K < 0)
+        return valid_dtype(io) ? MAMBA_ERR_SHAPE : MAMBA_ERR_DTYPE;
+    if (K == 0)
+        return valid_dtype(io) ? MAMBA_ERR_UNSUPPORTED : MAMBA_ERR_DTYPE;
+    return step_entry(h, conv_state, x_raw, K, conv_w, conv_bias, dt, dt_bias, A, Bm, Cm, Dskip,
+                      z, y, B, D, N, io, stream);
+}
 
 size_t mamba_selective_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,
                                                mamba_dtype io)

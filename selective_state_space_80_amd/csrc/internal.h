@@ -132,6 +132,11 @@ struct StepArgs {
     int64_t B, D;
     int N;
     bool bf16;
+    // conv front end in front (conv_K in 1..kFusedConvTaps; 0 = none): x is
+    // the raw input and conv_state [B, D, K-1] its window, updated in place
+    int conv_K = 0;
+    void *conv_state = nullptr;
+    const float *conv_w = nullptr, *conv_b = nullptr;
 };
 hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
 

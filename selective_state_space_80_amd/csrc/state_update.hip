@@ -10,6 +10,10 @@
 // channel, one 16-byte quarter of its state each, so every load and store of
 // a wave covers one contiguous 1 KB run; the readout is summed over the four
 // lanes with two cross-lane adds.  Other N: one lane per channel.
+// With the conv front end fused in front (KC taps), x is the raw input: the
+// step's scan input is SiLU(conv_b + sum_k conv_w[d,k] u_k) over the KC - 1
+// carried raw inputs and the new one, and the window moves by one slot
+// ("Mamba状态空间模型深度解析：挑战Transformer的下一代序列建模范式" §3.1).
 #include "device_common.h"
 #include "internal.h"
 
@@ -40,6 +44,41 @@ __device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4
     }
 }
 
+// The conv front end of one channel (flat index c, channel d), KC >= 1 taps:
+// its inputs (the KC - 1 carried raw inputs, then x_raw), weights and bias.
+template <bool BF16, int KC>
+struct ConvStep {
+    float u[KC], w[KC], b;
+    __device__ __forceinline__ void load(const void *state, float x_raw, const float *conv_w,
+                                         const float *bias_p, int64_t c, int64_t d)
+    {
+        using E = Elem<BF16>;
+        const typename E::T *st = reinterpret_cast<const typename E::T *>(state) + c * (KC - 1);
+#pragma unroll
+        for (int k = 0; k < KC - 1; ++k)
+            u[k] = E::load(st + k);
+        u[KC - 1] = x_raw;
+#pragma unroll
+        for (int k = 0; k < KC; ++k)
+            w[k] = conv_w[d * KC + k];
+        b = bias_p[d];
+    }
+    __device__ __forceinline__ float out(float bias_on) const
+    {
+        float acc = bias_on * b;
+#pragma unroll
+        for (int k = 0; k < KC; ++k)
+            acc = fmaf(w[k], u[k], acc);
+        return silu_hw(acc);
+    }
+    // slot j (< KC - 1, a constant after unrolling) of the window after this step
+    __device__ __forceinline__ void store_slot(void *state, int64_t c, int j) const
+    {
+        using E = Elem<BF16>;
+        E::store(reinterpret_cast<typename E::T *>(state) + c * (KC - 1) + j, u[j + 1]);
+    }
+};
+
 // N = 16, state and A rows 16-byte aligned, B/C rows aligned to 4 elements.
 // Grid: x over one batch row's 4 D quads, y over batch rows from b0 (the host
 // launches once per 65535 rows).  A wave handles QPT runs of 64 quads (16 channels each): lane l
@@ -49,12 +88,17 @@ __device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4
 // lane.  Every load of a lane is issued before the first use (no branch
 // between them: an absent dt_bias, Dskip or z is read through another valid
 // pointer and its value ignored).
-template <bool BF16, int QPT>
+// KC > 0: the conv front end first.  Lane q of a quad holds tap q (window
+// slot q, or the raw input for the last tap; lanes past the taps weigh 0):
+// one 2-byte and one 4-byte load per lane, the weighted taps summed over the
+// quad like the readout, and lane q in 1..KC-1 writes its tap to slot q - 1.
+template <bool BF16, int QPT, int KC>
 __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
     const void *__restrict__ Cm_, const float *__restrict__ Dskip, const void *__restrict__ z_,
-    void *__restrict__ y_, int64_t b0, int64_t D)
+    void *__restrict__ y_, int64_t b0, int64_t D, void *__restrict__ conv_state,
+    const float *__restrict__ conv_w, const float *__restrict__ conv_b)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
@@ -68,8 +112,13 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
     const float *skip_p = Dskip ? Dskip : A;
     const float skip_on = Dskip ? 1.f : 0.f;
     const T *z_p = reinterpret_cast<const T *>(z_ ? z_ : x_);  // same shape as x
+    const float *cb_p = conv_b ? conv_b : conv_w;  // conv_w has at least D entries
+    const float cb_on = conv_b ? 1.f : 0.f;
     {
         float hs[QPT][4], a[QPT][4], Bv[4], Cv[4], xv[QPT], dtv[QPT], bias[QPT], zv[QPT], dsk[QPT];
+        float tu[QPT], tw[QPT], tb[QPT];  // this lane's conv tap: input, weight; conv bias
+        const int tap = KC > 0 ? (q < KC ? q : KC - 1) : 0;
+        const float tap_on = q < KC ? 1.f : 0.f;
         int64_t gq[QPT], cq[QPT], dq[QPT];
         bool live[QPT];
         load4<BF16>(Bm_, b * 4 + q, Bv);
@@ -91,9 +140,25 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
             bias[k] = bias_p[dq[k]];
             zv[k] = E::load(z_p + cq[k]);
             dsk[k] = skip_p[dq[k]];
+            if constexpr (KC > 0) {
+                tu[k] = xv[k];
+                if constexpr (KC > 1) {
+                    const T *win = reinterpret_cast<const T *>(conv_state) + cq[k] * (KC - 1);
+                    const float u = E::load(win + (tap < KC - 1 ? tap : KC - 2));
+                    tu[k] = tap < KC - 1 ? u : xv[k];
+                }
+                tw[k] = conv_w[dq[k] * KC + tap];
+                tb[k] = cb_p[dq[k]];
+            }
         }
 #pragma unroll
         for (int k = 0; k < QPT; ++k) {
+            if constexpr (KC > 0) {  // the scan input of this step
+                float part = tap_on * tw[k] * tu[k];
+                part += __shfl_xor(part, 1);
+                part += __shfl_xor(part, 2);
+                xv[k] = silu_hw(part + cb_on * tb[k]);
+            }
             const float l =
                 softplus_log2(fmaf(dtv[k], kLog2e, bias_on * bias[k] * kLog2e));  // Δ / ln 2
             const float delta = l * kLn2;
@@ -116,6 +181,10 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
                 continue;
             if (q == 0)
                 E::store(reinterpret_cast<T *>(y_) + cq[k], yv);
+            if constexpr (KC > 1) {
+                if (q >= 1 && q < KC)
+                    E::store(reinterpret_cast<T *>(conv_state) + cq[k] * (KC - 1) + (q - 1), tu[k]);
+            }
             reinterpret_cast<float4 *>(h)[gq[k]] =
                 make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
         }
@@ -123,12 +192,13 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
 }
 
 // Any N <= 16: one lane per channel.
-template <bool BF16>
+template <bool BF16, int KC>
 __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
     const void *__restrict__ Cm_, const float *__restrict__ Dskip, const void *__restrict__ z_,
-    void *__restrict__ y_, int64_t D, int N, int64_t n_ch)
+    void *__restrict__ y_, int64_t D, int N, int64_t n_ch, void *__restrict__ conv_state,
+    const float *__restrict__ conv_w, const float *__restrict__ conv_b)
 {
     using E = Elem<BF16>;
     using T = typename E::T;
@@ -138,7 +208,15 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     const int64_t b = c / D, d = c - b * D;
     const T *Bm = reinterpret_cast<const T *>(Bm_) + b * N;
     const T *Cm = reinterpret_cast<const T *>(Cm_) + b * N;
-    const float xv = E::load(reinterpret_cast<const T *>(x_) + c);
+    float xv = E::load(reinterpret_cast<const T *>(x_) + c);
+    if constexpr (KC > 0) {
+        ConvStep<BF16, KC> cv;
+        cv.load(conv_state, xv, conv_w, conv_b ? conv_b : conv_w, c, d);
+        xv = cv.out(conv_b ? 1.f : 0.f);
+#pragma unroll
+        for (int j = 0; j < KC - 1; ++j)
+            cv.store_slot(conv_state, c, j);
+    }
     const float dtv = E::load(reinterpret_cast<const T *>(dt_) + c);
     const float bias = dt_bias ? dt_bias[d] : 0.f;
     const float l = softplus_log2(fmaf(dtv, kLog2e, bias * kLog2e));  // Δ / ln 2
@@ -158,13 +236,10 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     E::store(reinterpret_cast<T *>(y_) + c, yv);
 }
 
-}  // namespace
-
-hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
+template <int KC>
+hipError_t launch_state_update_k(const StepArgs &a, hipStream_t s)
 {
     const int64_t n_ch = a.B * a.D;
-    if (n_ch == 0)
-        return hipSuccess;
     const size_t bc_align = a.bf16 ? 8 : 16;
     const bool quad = a.N == kMaxN && ((uintptr_t)a.h % 16) == 0 && ((uintptr_t)a.A % 16) == 0 &&
                       ((uintptr_t)a.Bm % bc_align) == 0 && ((uintptr_t)a.Cm % bc_align) == 0;
@@ -175,26 +250,43 @@ hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
             const dim3 grid((unsigned)((4 * a.D + per_block - 1) / per_block),
                             (unsigned)min(a.B - b0, (int64_t)65535));
             if (a.bf16)
-                hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT>), grid, dim3(kThreads), 0,
-                                   s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z,
-                                   a.y, b0, a.D);
-            else
-                hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT>), grid, dim3(kThreads),
+                hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT, KC>), grid, dim3(kThreads),
                                    0, s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z,
-                                   a.y, b0, a.D);
+                                   a.y, b0, a.D, a.conv_state, a.conv_w, a.conv_b);
+            else
+                hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT, KC>), grid,
+                                   dim3(kThreads), 0, s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm,
+                                   a.Cm, a.Dskip, a.z, a.y, b0, a.D, a.conv_state, a.conv_w,
+                                   a.conv_b);
         }
     } else {
         const dim3 grid((unsigned)((n_ch + kThreads - 1) / kThreads));
         if (a.bf16)
-            hipLaunchKernelGGL(state_update_kernel<true>, grid, dim3(kThreads), 0, s, a.h, a.x,
-                               a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
-                               n_ch);
+            hipLaunchKernelGGL((state_update_kernel<true, KC>), grid, dim3(kThreads), 0, s, a.h,
+                               a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
+                               n_ch, a.conv_state, a.conv_w, a.conv_b);
         else
-            hipLaunchKernelGGL(state_update_kernel<false>, grid, dim3(kThreads), 0, s, a.h, a.x,
-                               a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
-                               n_ch);
+            hipLaunchKernelGGL((state_update_kernel<false, KC>), grid, dim3(kThreads), 0, s, a.h,
+                               a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
+                               n_ch, a.conv_state, a.conv_w, a.conv_b);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
+{
+    if (a.B * a.D == 0)
+        return hipSuccess;
+    switch (a.conv_K) {
+    case 0: return launch_state_update_k<0>(a, s);
+    case 1: return launch_state_update_k<1>(a, s);
+    case 2: return launch_state_update_k<2>(a, s);
+    case 3: return launch_state_update_k<3>(a, s);
+    case 4: return launch_state_update_k<4>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace mamba

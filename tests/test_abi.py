@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 5
+    assert lib.mamba_abi_version() == 6
     for st in range(10):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -171,6 +171,33 @@ def test_fused_scan_empty_is_ok(lib):
     assert fused(lib, D=0, x=None, w=None) == OK
 
 
+def fused_step(lib, **kw):
+    a = dict(h=P(1), cs=P(11), x=P(2), w=P(12), cb=P(13), K=4, dt=P(3), dt_bias=P(4), A=P(5),
+             Bm=P(6), Cm=P(7), Dskip=P(8), z=P(9), y=P(10), B=4, D=64, N=16, io=F32)
+    a.update(kw)
+    return lib.mamba_conv1d_selective_state_update(
+        a["h"], a["cs"], a["x"], a["w"], a["cb"], a["K"], a["dt"], a["dt_bias"], a["A"], a["Bm"],
+        a["Cm"], a["Dskip"], a["z"], a["y"], a["B"], a["D"], a["N"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(io=7), EDTYPE), (dict(K=0), EUNSUP), (dict(K=5), EUNSUP), (dict(K=-1), ESHAPE),
+    (dict(N=17), EUNSUP), (dict(B=-1), ESHAPE), (dict(w=None), ENULL), (dict(cs=None), ENULL),
+    (dict(h=None), ENULL), (dict(x=None), ENULL),
+    (dict(w=ctypes.c_void_p(0xC0000000002)), EALIGN),
+    (dict(io=BF16, cs=ctypes.c_void_p(0xB0000000001)), EALIGN),
+    (dict(cs=P(2)), EALIAS), (dict(cs=P(1)), EALIAS), (dict(cs=P(10)), EALIAS),
+    (dict(cs=P(12)), EALIAS), (dict(y=P(13)), EALIAS), (dict(h=P(12)), EALIAS),
+])
+def test_fused_step_rejects(lib, kw, want):
+    assert fused_step(lib, **kw) == want
+
+
+def test_fused_step_empty_is_ok(lib):
+    assert fused_step(lib, B=0) == OK
+    assert fused_step(lib, D=0, h=None, cs=None) == OK
+
+
 def test_conv_update_rejects(lib):
     f = lib.mamba_conv1d_update
     assert f(P(1), P(2), P(3), None, P(4), 2, 8, 9, F32, None) == EUNSUP
@@ -279,6 +306,8 @@ def test_valid_arguments_without_gpu_report_device(lib):
     assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
                                             P(9), P(10), 4, 64, 16, F32, None) == EDEV
     assert bwd(lib) == EDEV
+    assert fused_step(lib) == EDEV
+    assert fused_step(lib, K=1, cs=None) == EDEV  # one tap: no window to carry
     assert ssd(lib) == EDEV
     assert ssd(lib, L=0, x=None, y=None, dt=None, Bm=None, Cm=None) == EDEV  # h_last = h0
 

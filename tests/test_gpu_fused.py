@@ -235,3 +235,83 @@ def test_block_workload_fused_sampled():
     e = assert_within(pick(y), yo, TOL["f32"], "fused block y")
     assert_within(pick(hl), ho, STATE_TOL, "fused block h_last")
     say(f"  max rel err {e:.2e}")
+
+
+@pytest.mark.parametrize("N", [16, 5])  # 16: four lanes per channel; 5: one lane per channel
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_fused_decode_step_matches_oracle(N, K, io):
+    """mamba_conv1d_selective_state_update over several tokens against the
+    oracle's conv step followed by its state update (conv output in fp64, not
+    rounded), with the window checked bit for bit after every token."""
+    import selective_state_space_80_amd as mamba
+    say(f"fused decode step N={N} K={K} io={io}")
+    B, D, T = 3, 300, 4
+    wl = W.DecodeWorkload("t", B, D, N, io, T, 1, 90 + K)
+    init = W.decode_initial(wl)
+    ci = W.decode_conv_initial(wl, K)
+    rng = np.random.default_rng(K)
+    cb = rng.standard_normal(D).astype(np.float32) if K != 2 else None
+    with_opt = K != 3  # K = 3: no dt_bias, Dskip, z
+    h = dev(init["h0"])
+    cs = dev(ci["conv_state"], io) if K > 1 else None
+    h_or, cs_or = init["h0"].astype(np.float64), ci["conv_state"].astype(np.float64)
+    for t in range(T):
+        s = W.decode_step_inputs(wl, t)
+        y = mamba.conv1d_selective_state_update(
+            h, cs, dev(s["x"], io), dev(ci["conv_w"]), dev(s["dt"], io), dev(init["A"]),
+            dev(s["Bm"], io), dev(s["Cm"], io), conv_bias=dev(cb),
+            dt_bias=dev(init["dt_bias"]) if with_opt else None,
+            Dskip=dev(init["Dskip"]) if with_opt else None,
+            z=dev(s["z"], io) if with_opt else None)
+        xc, cs_or = oracle.conv1d_update(cs_or, s["x"], ci["conv_w"], cb)
+        yo, h_or = oracle.state_update(h_or, xc, s["dt"], init["A"], s["Bm"], s["Cm"],
+                                       dt_bias=init["dt_bias"] if with_opt else None,
+                                       Dskip=init["Dskip"] if with_opt else None,
+                                       z=s["z"] if with_opt else None)
+        assert_within(host(y), yo, TOL[io], f"fused decode y t={t}")
+        assert_within(host(h), h_or, STATE_TOL, f"fused decode h t={t}")
+        if K > 1:
+            assert np.array_equal(host(cs), cs_or), f"conv window t={t}"
+
+
+def test_fused_decode_step_equals_separate_calls():
+    """fp32: the fused step gives what conv1d_update then selective_state_update
+    give (the conv output is exact in fp32 either way)."""
+    import selective_state_space_80_amd as mamba
+    B, D, N, K = 4, 640, 16, 4
+    wl = W.DecodeWorkload("t", B, D, N, "f32", 3, 1, 97)
+    init, ci = W.decode_initial(wl), W.decode_conv_initial(wl, K)
+    h1, h2 = dev(init["h0"]), dev(init["h0"])
+    c1, c2 = dev(ci["conv_state"]), dev(ci["conv_state"])
+    w, A, bias, Dk = dev(ci["conv_w"]), dev(init["A"]), dev(init["dt_bias"]), dev(init["Dskip"])
+    for t in range(3):
+        s = W.decode_step_inputs(wl, t)
+        x, dt, Bm, Cm, z = (dev(s[k]) for k in ("x", "dt", "Bm", "Cm", "z"))
+        y1 = mamba.conv1d_selective_state_update(h1, c1, x, w, dt, A, Bm, Cm, dt_bias=bias,
+                                                 Dskip=Dk, z=z)
+        xc = mamba.conv1d_update(c2, x, w)
+        y2 = mamba.selective_state_update(h2, xc, dt, A, Bm, Cm, dt_bias=bias, Dskip=Dk, z=z)
+        assert_within(host(y1), host(y2), 1e-6, f"fused vs separate y t={t}")
+        assert_within(host(h1), host(h2), 1e-6, f"fused vs separate h t={t}")
+        assert np.array_equal(host(c1), host(c2)), f"fused vs separate window t={t}"
+
+
+def test_fused_decode_step_many_rows():
+    """65537 batch rows (two launches) through the fused step, bf16."""
+    import selective_state_space_80_amd as mamba
+    B, D, N, K = 65537, 4, 16, 4
+    wl = W.DecodeWorkload("t", B, D, N, "bf16", 1, 1, 98)
+    init, ci = W.decode_initial(wl), W.decode_conv_initial(wl, K)
+    s = W.decode_step_inputs(wl, 0)
+    h, cs = dev(init["h0"]), dev(ci["conv_state"], "bf16")
+    y = mamba.conv1d_selective_state_update(
+        h, cs, dev(s["x"], "bf16"), dev(ci["conv_w"]), dev(s["dt"], "bf16"), dev(init["A"]),
+        dev(s["Bm"], "bf16"), dev(s["Cm"], "bf16"), dt_bias=dev(init["dt_bias"]),
+        Dskip=dev(init["Dskip"]), z=dev(s["z"], "bf16"))
+    xc, cs_or = oracle.conv1d_update(ci["conv_state"].astype(np.float64), s["x"], ci["conv_w"])
+    yo, ho = oracle.state_update(init["h0"].astype(np.float64), xc, s["dt"], init["A"], s["Bm"],
+                                 s["Cm"], dt_bias=init["dt_bias"], Dskip=init["Dskip"], z=s["z"])
+    assert_within(host(y), yo, TOL["bf16"], "fused decode y")
+    assert_within(host(h), ho, STATE_TOL, "fused decode h")
+    assert np.array_equal(host(cs), cs_or), "conv window"
