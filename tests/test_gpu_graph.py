@@ -124,3 +124,36 @@ def test_graph_ssd():
         x.copy_(dev(rng.standard_normal((B, L, H, 64)).astype(np.float32), "bf16"))
 
     _replays(lambda: call(y, hl), lambda: call(None, None), refill)
+
+
+def test_graph_fused_decode():
+    """The fused decode step (conv window and state advance in place) captured
+    and replayed: k replays equal k eager steps from the same start."""
+    import torch
+    import selective_state_space_80_amd as mamba
+    wl = W.DecodeWorkload("t", 4, 320, 16, "bf16", 1, 1, 27)
+    say("graph fused decode")
+    init, ci = W.decode_initial(wl), W.decode_conv_initial(wl, 4)
+    s = W.decode_step_inputs(wl, 0)
+    x, dt, z = dev(s["x"], "bf16"), dev(s["dt"], "bf16"), dev(s["z"], "bf16")
+    Bm, Cm = dev(s["Bm"], "bf16"), dev(s["Cm"], "bf16")
+    A, bias, Dk, w = dev(init["A"]), dev(init["dt_bias"]), dev(init["Dskip"]), dev(ci["conv_w"])
+    h_g, c_g = dev(init["h0"]), dev(ci["conv_state"], "bf16")
+    h_e, c_e = h_g.clone(), c_g.clone()
+    y = torch.empty_like(x)
+    rng = np.random.default_rng(28)
+
+    def call(h, c, out=None):
+        return mamba.conv1d_selective_state_update(h, c, x, w, dt, A, Bm, Cm, dt_bias=bias,
+                                                   Dskip=Dk, z=z, out=out)
+
+    # the warm-up call of _replays advances h_g and c_g once: advance h_e, c_e to match
+    call(h_e, c_e)
+
+    def refill(k):
+        x.copy_(dev(rng.standard_normal((wl.B, wl.D)).astype(np.float32), "bf16"))
+
+    def eager():
+        return call(h_e, c_e), h_e, c_e
+
+    _replays(lambda: (call(h_g, c_g, out=y), h_g, c_g), eager, refill, n=4)
