@@ -25,6 +25,12 @@
  *     nothing.  A failure to launch returns MAMBA_ERR_LAUNCH.  Faults inside a
  *     kernel surface at the caller's next synchronisation, as usual for HIP.
  *   - Outputs must not overlap inputs (only the decode state is in/out).
+ *   - Sizes: each of B, D, L (or H, P) and the product of the non-zero ones
+ *     is at most 2^40, and each call's launch grids must fit one launch:
+ *     about 2^31 channels for the decode calls (B*D), 2^31 threads for the
+ *     standalone conv (B*D*ceil(L/4)), 2^23 64-channel x 128-step segments for
+ *     the scans (2^21 for the backward, with B*L < 2^25), B*H < 2^24 for the
+ *     Mamba-2 form.  Beyond them a call returns MAMBA_ERR_SHAPE.
  *   - Element types: MAMBA_F32 = float, MAMBA_BF16 = bfloat16 (stored as
  *     uint16, round-to-nearest-even on output).  Parameters (A, dt_bias, D,
  *     conv weights, states) are always float.
@@ -84,7 +90,7 @@ int mamba_abi_version(void);
  *   out[b,d,t] = SiLU( bias[d] + sum_{k<K} w[d,k] * x[b,d,t-(K-1)+k] ),  x[t<0] = 0.
  *   x, out : [B, D, L] of `dtype`;  w : [D, K] float;  bias : [D] float or NULL.
  * out must not overlap x.  K in 1..8.  MAMBA_ERR_SHAPE also when
- * B * D * ceil(L / 4) >= 2^32 (one launch covers the whole problem).
+ * B * D * ceil(L / 4) >= 2^31 (one launch covers the whole problem).
  */
 mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias, void *out,
                                int64_t B, int64_t D, int64_t L, int64_t K, mamba_dtype dtype,

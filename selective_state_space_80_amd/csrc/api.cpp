@@ -6,6 +6,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "internal.h"
@@ -15,6 +16,9 @@ namespace {
 using mamba::kMaxN;
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // B*D*L bound (keeps every index in int64)
+// Every launch keeps blocks x threads per grid dimension below 2^32 work-items;
+// the MAMBA_ERR_SHAPE checks below bound each entry point's grids for that.
+constexpr int64_t kMaxGrid = int64_t(1) << 31;
 
 thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
@@ -35,18 +39,21 @@ bool overlap(Range a, Range b)
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Non-negative sizes whose product stays below kMaxElems.
+// Non-negative sizes; each, and the product of the non-zero ones, at most
+// kMaxElems (so an empty dimension leaves the others bounded too).
 bool sizes_ok(int64_t a, int64_t b, int64_t c)
 {
     if (a < 0 || b < 0 || c < 0)
         return false;
-    if (a == 0 || b == 0 || c == 0)
-        return true;
-    if (a > kMaxElems || b > kMaxElems || c > kMaxElems)
-        return false;
-    if (a > kMaxElems / b)
-        return false;
-    return a * b <= kMaxElems / c;
+    int64_t p = 1;
+    for (const int64_t v : {a, b, c}) {
+        if (v == 0)
+            continue;
+        if (v > kMaxElems || p > kMaxElems / v)
+            return false;
+        p *= v;
+    }
+    return true;
 }
 
 // The kernels are built for gfx950 only.
@@ -118,6 +125,8 @@ mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias,
         return MAMBA_ERR_SHAPE;
     if (K < 1 || K > MAMBA_MAX_CONV_TAPS)
         return MAMBA_ERR_UNSUPPORTED;
+    if (B * D * ((L + 3) / 4) >= kMaxGrid)  // launch grid: one thread per 4 or 8 steps
+        return MAMBA_ERR_SHAPE;
     const int64_t n = B * D * L;
     if (n == 0)
         return MAMBA_OK;
@@ -130,8 +139,6 @@ mamba_status mamba_conv1d_silu(const void *x, const float *w, const float *bias,
     if (overlap(ro, rng(x, (size_t)n * es)) || overlap(ro, rng(w, (size_t)(D * K) * 4)) ||
         (bias && overlap(ro, rng(bias, (size_t)D * 4))))
         return MAMBA_ERR_ALIAS;
-    if (B * D * ((L + 3) / 4) >= (int64_t(1) << 32))  // launch grid: one thread per 4 steps
-        return MAMBA_ERR_SHAPE;
     mamba_status st = device_ok();
     if (st != MAMBA_OK)
         return st;
@@ -176,6 +183,8 @@ mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
         return MAMBA_ERR_UNSUPPORTED;
     if (conv && conv_K > mamba::kFusedConvTaps)
         return MAMBA_ERR_UNSUPPORTED;
+    if (L == 0 && (h_last || conv_state_out) && B * D * N >= kMaxGrid)
+        return MAMBA_ERR_SHAPE;  // launch grid of the state copy
     if (B * D == 0)
         return MAMBA_OK;
     const int64_t n = B * D * L;
@@ -293,6 +302,8 @@ mamba_status step_entry(float *h, void *conv_state, const void *x, int64_t conv_
         return MAMBA_ERR_SHAPE;
     if (N < 1 || N > kMaxN || conv_K > mamba::kFusedConvTaps)
         return MAMBA_ERR_UNSUPPORTED;
+    if (B * D >= kMaxGrid)  // launch grid: up to two lanes per channel in a row's dimension
+        return MAMBA_ERR_SHAPE;
     if (B * D == 0)
         return MAMBA_OK;
     const bool conv = conv_K != 0;
@@ -321,8 +332,6 @@ mamba_status step_entry(float *h, void *conv_state, const void *x, int64_t conv_
             return MAMBA_ERR_ALIAS;
     if (overlap(ry, rh) || overlap(ry, rc) || overlap(rh, rc))
         return MAMBA_ERR_ALIAS;
-    if ((n * 4 + 255) / 256 >= (int64_t(1) << 31))  // launch grid (four lanes per channel)
-        return MAMBA_ERR_SHAPE;
     mamba_status st = device_ok();
     if (st != MAMBA_OK)
         return st;
@@ -387,6 +396,8 @@ mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, con
         return MAMBA_ERR_SHAPE;
     if (K < 1 || K > MAMBA_MAX_CONV_TAPS)
         return MAMBA_ERR_UNSUPPORTED;
+    if (B * D >= kMaxGrid)  // launch grid: up to one thread per channel
+        return MAMBA_ERR_SHAPE;
     const int64_t n = B * D;
     if (n == 0)
         return MAMBA_OK;
@@ -405,8 +416,6 @@ mamba_status mamba_conv1d_update(void *state, const void *x, const float *w, con
             return MAMBA_ERR_ALIAS;
     if (overlap(ro, rs))
         return MAMBA_ERR_ALIAS;
-    if ((n + 255) / 256 >= (int64_t(1) << 31))
-        return MAMBA_ERR_SHAPE;
     mamba_status st = device_ok();
     if (st != MAMBA_OK)
         return st;
@@ -479,12 +488,16 @@ mamba_status mamba_selective_scan_bwd(
         !aligned(h0, 4) || !aligned(dh_last, 4) || !aligned(dA, 4) || !aligned(dB, 4) ||
         !aligned(dC, 4) || !aligned(dD, 4) || !aligned(ddt_bias, 4) || !aligned(dh0, 4))
         return MAMBA_ERR_ALIGN;
+    if (empty && (B * D * N >= kMaxGrid || D * N >= kMaxGrid))  // grid of the empty-problem kernel
+        return MAMBA_ERR_SHAPE;
     size_t ws_need = 0;
     if (!empty) {
         if (B * L * kMaxN >= (int64_t(1) << 31))
             return MAMBA_ERR_SHAPE;
         const mamba::BwdWsLayout lay = mamba::scan_bwd_ws_layout(B, D, L);
-        if (lay.scan.n_items >= (int64_t(1) << 23))
+        // chunk kernel: four 32-step chunks per segment, 256 threads each;
+        // column sums: up to 16 threads per (b, t, n) column
+        if (lay.scan.n_items >= (int64_t(1) << 21) || B * L >= (int64_t(1) << 25))
             return MAMBA_ERR_SHAPE;
         ws_need = lay.total;
         if (!workspace || workspace_bytes < ws_need || !aligned(workspace, 256))
@@ -569,7 +582,7 @@ mamba_status mamba_ssd_scan_fwd(const void *x, const void *dt, const float *dt_b
         return MAMBA_ERR_SHAPE;
     if (io != MAMBA_BF16 || P != mamba::kSsdHeadDim || !(N == 16 || N == 32 || N == 64 || N == 128))
         return MAMBA_ERR_UNSUPPORTED;
-    if (G < 1 || H % G != 0 || B * H >= (int64_t(1) << 31))
+    if (G < 1 || H % G != 0 || B * H >= (int64_t(1) << 24))  // one 256-thread workgroup each
         return MAMBA_ERR_SHAPE;
     if (H * P * 64 >= (int64_t(1) << 31) || G * N * 64 >= (int64_t(1) << 31))
         return MAMBA_ERR_SHAPE;  // 32-bit offsets within a 64-step chunk

@@ -159,7 +159,7 @@ hipError_t launch_typed(const ConvArgs &a, hipStream_t s)
     constexpr int V = kPiece<BF16>;
     const int64_t piece_blocks = (a.L / V + 255) / 256;
     if (a.L % V == 0 && (((uintptr_t)a.x | (uintptr_t)a.out) % 16 == 0) && a.B <= 65535 &&
-        piece_blocks <= 65535 && a.D < (int64_t(1) << 31)) {
+        piece_blocks <= 65535 && a.D < (int64_t(1) << 24)) {  // D x 256 work-items < 2^32
         hipLaunchKernelGGL((conv1d_silu_piece_kernel<BF16, K>),
                            dim3((unsigned)a.D, (unsigned)piece_blocks, (unsigned)a.B), dim3(256), 0,
                            s, a.x, a.w, a.bias, a.out, a.D, a.L);

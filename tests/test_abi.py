@@ -295,6 +295,28 @@ def test_ssd_empty_is_ok(lib):
     assert ssd(lib, L=0, h_last=None, x=None, y=None) == OK
 
 
+def test_launch_grid_limits(lib):
+    """Sizes whose launch grids would reach 2^32 work-items in one dimension are
+    shape errors, reported before any pointer is looked at."""
+    big = dict(B=1 << 16, D=1 << 15)  # 2^31 channels
+    assert lib.mamba_conv1d_silu(P(1), P(2), None, P(3), 1, 1 << 20, 1 << 13, 4, F32,
+                                 None) == ESHAPE
+    assert lib.mamba_selective_state_update(*[P(k) for k in range(1, 11)], big["B"], big["D"],
+                                            16, F32, None) == ESHAPE
+    assert fused_step(lib, **big) == ESHAPE
+    assert lib.mamba_conv1d_update(P(1), P(2), P(3), None, P(4), big["B"], big["D"], 4, F32,
+                                   None) == ESHAPE
+    # an empty sequence still copies h0 into h_last over B*D*N values
+    assert scan(lib, B=1 << 12, D=1 << 15, L=0) == ESHAPE
+    assert scan(lib, B=1 << 12, D=1 << 15, L=0, h_last=None) == OK  # nothing to launch
+    # an empty dimension leaves the others bounded
+    assert scan(lib, B=1 << 30, D=1 << 30, L=0, h_last=None) == ESHAPE
+    assert bwd(lib, B=1, D=64, L=1 << 25) == ESHAPE  # column sums over B*L*16 columns
+    assert bwd(lib, B=1, D=1 << 16, L=1 << 18) == ESHAPE  # 2^21 segments
+    assert bwd(lib, B=1 << 12, D=1 << 15, L=0) == ESHAPE  # empty problem over B*D*N
+    assert ssd(lib, B=1 << 12, H=1 << 12, G=1) == ESHAPE
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="valid fake pointers must never reach a GPU")
 def test_valid_arguments_without_gpu_report_device(lib):
     assert fused(lib) == EDEV
