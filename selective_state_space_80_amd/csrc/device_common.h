@@ -93,4 +93,13 @@ __device__ __forceinline__ float zoh_coef_w(float w, float delta, float en, floa
     return fabsf(w) < 0.125f * 1.44269504088896341f ? delta * phi : (en - 1.f) * rcpa;
 }
 
+// Sum over the four lanes of a quad, the result in all four: two DPP quad
+// permutes (lane ^ 1, then lane ^ 2), no LDS traffic.
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
 }  // namespace mamba

@@ -56,14 +56,6 @@ __device__ __forceinline__ float dbeta_dA(float delta, float del2, float u, floa
     return fabsf(u) < 0.125f ? del2 * s : closed;
 }
 
-// Sum over the four lanes of a quad (one channel): two DPP quad permutes.
-__device__ __forceinline__ float quad_sum(float v)
-{
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // lane ^ 1
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // lane ^ 2
-    return v;
-}
-
 struct BwdArgs {
     const void *x, *dt, *z, *dout, *Bm, *Cm;
     const float *dt_bias, *A, *Dskip;

@@ -9,7 +9,7 @@
 // dominates the traffic.  With N = 16 and aligned rows, four lanes share a
 // channel, one 16-byte quarter of its state each, so every load and store of
 // a wave covers one contiguous 1 KB run; the readout is summed over the four
-// lanes with two cross-lane adds.  Other N: one lane per channel.
+// lanes with two DPP quad permutes.  Other N: one lane per channel.
 // With the conv front end fused in front (KC taps), x is the raw input: the
 // step's scan input is SiLU(conv_b + sum_k conv_w[d,k] u_k) over the KC - 1
 // carried raw inputs and the new one, and the window moves by one slot
@@ -155,9 +155,7 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
         for (int k = 0; k < QPT; ++k) {
             if constexpr (KC > 0) {  // the scan input of this step
                 float part = tap_on * tw[k] * tu[k];
-                part += __shfl_xor(part, 1);
-                part += __shfl_xor(part, 2);
-                xv[k] = silu_hw(part + cb_on * tb[k]);
+                xv[k] = silu_hw(quad_sum(part) + cb_on * tb[k]);
             }
             const float l =
                 softplus_log2(fmaf(dtv[k], kLog2e, bias_on * bias[k] * kLog2e));  // Δ / ln 2
@@ -170,8 +168,7 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
                 hs[k][i] = fmaf(en, hs[k][i], coef * (Bv[i] * xv[k]));
                 acc = fmaf(Cv[i], hs[k][i], acc);
             }
-            acc += __shfl_xor(acc, 1);
-            acc += __shfl_xor(acc, 2);
+            acc = quad_sum(acc);
             // every lane forms the gated output (so no load sinks into the
             // store's branch); lane q = 0 of the quad stores it
             float yv = acc + skip_on * dsk[k] * xv[k];
