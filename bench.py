@@ -210,6 +210,37 @@ def cpu_baseline_ssd(p, wl, target_s=15.0):
             "single_thread_value": round(wl.L * wl.P / t1 / 1e9, 6), "cpu_model": cpu_model()}
 
 
+def cpu_baseline_decode(wl, init, steps, nbytes, conv=None, target_s=10.0):
+    """The fp64 oracle's decode step (with `conv`: its conv step first) over the
+    whole B x D problem, batch rows split across a pool of host threads, for
+    about target_s seconds of steps; reported in GB/s of the same algorithmic
+    bytes per step as the GPU line."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    parts = [r for r in np.array_split(np.arange(wl.B), threads) if len(r)]
+
+    def job(r, s):
+        b0, b1 = int(r[0]), int(r[-1]) + 1
+
+        def run():
+            x = s["x"][b0:b1]
+            if conv is not None:
+                x, _ = oracle.conv1d_update(conv["conv_state"][b0:b1], x, conv["conv_w"])
+            oracle.state_update(init["h0"][b0:b1], x, s["dt"][b0:b1], init["A"], s["Bm"][b0:b1],
+                                s["Cm"][b0:b1], init["dt_bias"], init["Dskip"], s["z"][b0:b1])
+        return run
+
+    t_one = _pool_time([job(r, steps[0]) for r in parts], threads)
+    n = int(max(1, min(256, target_s / max(t_one, 1e-6))))
+    dt = _pool_time([job(r, steps[i % len(steps)]) for i in range(n) for r in parts], threads)
+    what = "conv step, then state update" if conv is not None else "state update"
+    return {"value": round(nbytes * n / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{n} whole decode steps ({wl.B} x {wl.D} channels, {what}) in fp64, "
+                      f"batch rows split over {threads} host threads",
+            "cpu_model": cpu_model()}
+
+
 def quantiles(ms):
     a = np.asarray(ms, dtype=np.float64)
     return {"mean": round(float(a.mean()), 4), "p10": round(float(np.percentile(a, 10)), 4),
@@ -535,9 +566,10 @@ def run_decode(args, torch, mamba, W):
     T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
     h = T(init["h0"])
     A, bias, Dk = T(init["A"]), T(init["dt_bias"]), T(init["Dskip"])
-    toks = []
+    toks, toks_np = [], []
     for s in range(8):
         st = W.decode_step_inputs(wl, s)
+        toks_np.append(st)
         toks.append({k: T(v, torch.bfloat16) for k, v in st.items()})
     y = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
     K = 4
@@ -587,7 +619,10 @@ def run_decode(args, torch, mamba, W):
                           if args.with_conv else {})},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "note": "state (84 MB) stays resident in the 256 MB MALL between steps"}}
+                         "note": "state (84 MB) stays resident in the 256 MB MALL between steps"},
+            **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_decode(
+                wl, init, toks_np, nbytes, W.decode_conv_initial(wl, K) if args.with_conv
+                else None)})}
 
 
 def main():
