@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
         for (int k = 0; k < QPT; ++k) {
             const int64_t rq = (wave * QPT + k) * 64 + lane;  // quad within the row
             // whole channels per run of 64 quads, so a lane past the end only
-            // ever shares its shuffles with lanes past the end too
+            // ever shares its quad sums with lanes past the end too
             live[k] = rq < row_quads;
             const int64_t rqc = live[k] ? rq : row_quads - 1;
             dq[k] = rqc >> 2;
