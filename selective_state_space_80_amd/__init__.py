@@ -28,6 +28,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmamba_amd.so")
+ABI_VERSION = 6  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
 
 MAMBA_F32 = 0
 MAMBA_BF16 = 1
@@ -70,6 +71,10 @@ def load_library(path: str = LIBRARY):
     lib.mamba_status_string.argtypes = [I32]
     lib.mamba_abi_version.restype = I32
     lib.mamba_abi_version.argtypes = []
+    if lib.mamba_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.mamba_abi_version()}, this binding "
+                           f"follows {ABI_VERSION}: rebuild it (`python -m "
+                           "selective_state_space_80_amd.build`)")
     lib.mamba_conv1d_silu.restype = I32
     lib.mamba_conv1d_silu.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, P]
     lib.mamba_selective_scan_fwd_workspace_size.restype = SZ

@@ -31,6 +31,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", text)))
 
 
+def test_binding_follows_the_header_abi_version():
+    m = re.search(r"#define MAMBA_AMD_ABI_VERSION (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == mamba.ABI_VERSION
+
+
 def test_header_lists_what_binding_expects():
     assert declared_functions() == sorted(mamba.EXPORTED)
 
