@@ -32,8 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
-SCAN_SRC = os.path.join(ROOT, "selective_state_space_80_amd", "csrc", "scan_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 class HipEvents:
@@ -74,18 +73,26 @@ def conv_bytes(B, D, L, K, esz):
     return 2 * B * D * L * esz + D * K * 4
 
 
-def traffic_record(variant):
-    """HBM traffic and VALU instruction count of the main scan kernel measured
-    by rocprofv3 counters on the block workload (`variant` = fused or
-    unfused), if taken on the current kernel source (else None)."""
+def traffic_record(key):
+    """HBM traffic (and VALU instruction count) of a workload's dominant kernel
+    measured by rocprofv3 counters, if they were taken on the current source of
+    that kernel (else None: counters of an older kernel say nothing)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE)).get(variant)
+        rec = json.load(open(TRAFFIC_FILE)).get(key)
     except (OSError, ValueError, AttributeError):
         return None
-    if not rec:
+    if not rec or "source" not in rec:
         return None
-    sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
-    return rec if rec.get("scan_fwd_sha256") == sha else None
+    try:
+        sha = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return rec if rec.get("source_sha256") == sha else None
+
+
+def traffic_bytes(tr):
+    """FETCH_SIZE + WRITE_SIZE per launch, each scaled by a copy kernel of known size."""
+    return None if tr is None else int(round(tr["fetch_bytes"] + tr["write_bytes"]))
 
 
 def cpu_model():
@@ -263,6 +270,201 @@ def valu_record(tr, elems, kernel_ms):
             "issue_peak_per_s": peak, "frac": round(per_s / peak, 4)}
 
 
+
+def settle_clocks(step, torch, seconds):
+    """Run the step back to back for `seconds` of wall time before the warm-up
+    steps: the GPU only reaches its steady clocks after tens of milliseconds of
+    sustained work, which a few warm-up steps of a sub-millisecond kernel do
+    not give.  Untimed; reported beside the result."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return {"seconds": round(time.perf_counter() - t0, 3), "steps": n}
+
+
+def time_with_scan_events(step, torch, mamba, steps):
+    """Time `steps` calls of step(): wall clock per step, and the main scan
+    kernel's duration per launch from HIP events recorded around it on its own
+    stream (the library's timing hook)."""
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        mamba.set_scan_timing_events_raw(pairs[i][0], pairs[i][1])
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mamba.set_scan_timing_events_raw(None, None)
+    k_all = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    return elapsed / steps * 1e3, k_all
+
+
+def cpu_baseline_scan(p, wl, target_s, y_gpu_rows=None, tol=2e-2):
+    """The fp64 oracle's scan on a bounded sample of a workload: whole
+    sequences of the first channels of batch row 0 on the host threads, sized
+    for about target_s seconds; with the benchmarked output of those channels
+    (y_gpu_rows, [1, ch, L]) also its largest error against the oracle."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    L = wl.L
+
+    def run(ch, nthreads):
+        return oracle.selective_scan(p["x"][0:1, :ch], p["dt"][0:1, :ch], p["A"][:ch],
+                                     p["Bm"][0:1], p["Cm"][0:1], p["dt_bias"][:ch],
+                                     p["Dskip"][:ch], p["z"][0:1, :ch], nthreads=nthreads)[0]
+
+    t0 = time.perf_counter()
+    run(threads, threads)
+    per_ch = (time.perf_counter() - t0) / threads
+    ch = int(min(wl.D, max(threads, target_s / max(per_ch, 1e-9))) // threads * threads)
+    t0 = time.perf_counter()
+    y_or = run(ch, threads)
+    dt = time.perf_counter() - t0
+    out = {"value": round(ch * L / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
+           "kind": "oracle", "seconds": round(dt, 3),
+           "sample": f"batch row 0, channels 0..{ch - 1} of {wl.D}, all {L} steps, fp64 on "
+                     f"{threads} host threads ({ch * L} elements)",
+           "cpu_model": cpu_model()}
+    if y_gpu_rows is not None:
+        k = min(ch, y_gpu_rows.shape[1])
+        err = np.abs(y_gpu_rows[:, :k] - y_or[:, :k]) / (1.0 + np.abs(y_or[:, :k]))
+        out["check"] = {"max_rel_err": float(err.max()), "tolerance": tol,
+                        "sample": f"batch row 0, channels 0..{k - 1}, all {L} steps of "
+                                  "the benchmarked output",
+                        "within": bool(err.max() <= tol)}
+    return out
+
+
+def measure_scan(torch, mamba, W, idx, steps, warmup, settle_s, cpu_s, no_cpu=False):
+    """One scan workload in the benchmark's launch: kernel and step time, the
+    HBM roofline of the main kernel, its counter traffic and VALU issue when
+    profiled on the current source, and the oracle on a bounded sample."""
+    wl = W.WORKLOADS[idx]
+    B, D, L, N = wl.B, wl.D, wl.L, wl.N
+    p = W.scan_inputs(wl)
+    dev = torch.device("cuda:0")
+    bf = wl.io == "bf16"
+    io_t = torch.bfloat16 if bf else torch.float32
+    T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    x, dt, z = T(p["x"], io_t), T(p["dt"], io_t), T(p["z"], io_t)
+    Bm, Cm = T(p["Bm"], io_t), T(p["Cm"], io_t)
+    A, bias, Dk = T(p["A"]), T(p["dt_bias"]), T(p["Dskip"])
+    y = torch.empty_like(x)
+    ws = torch.empty(max(1, mamba.selective_scan_fwd_workspace_size(B, D, L, N)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        mamba.selective_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
+
+    settle = settle_clocks(step, torch, settle_s)
+    for _ in range(warmup):
+        step()
+    ms_step, k_all = time_with_scan_events(step, torch, mamba, steps)
+    k_ms = float(np.mean(k_all))
+    elems = B * D * L
+    sb = scan_bytes(B, D, L, N, 2 if bf else 4)
+    achieved = sb / (k_ms * 1e-3) / 1e9
+    tr = traffic_record(wl.name)
+    out = {"config": {"batch": B, "d_inner": D, "seq_len": L, "d_state": N, "io": wl.io,
+                      "state": "f32"},
+           "step_gelem_s": round(elems / (ms_step * 1e-3) / 1e9, 3),
+           "ms_per_step": round(ms_step, 4), "steps": steps, "warmup": warmup,
+           "clock_settle": settle,
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": traffic_bytes(tr), "kernel": f"main scan kernel ({wl.io})",
+                        "kernel_ms": round(k_ms, 4), "algorithmic_bytes": sb},
+           "valu": valu_record(tr, elems, k_ms),
+           "kernels": {"scan_ms": quantiles(k_all),
+                       "scan_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
+    if idx == 0:
+        out["roofline"]["note"] = ("0.3 MB problem: cache-resident and launch-latency bound, "
+                                   "reported for completeness")
+    if not no_cpu:
+        ch = min(D, 64)
+        y_rows = y[0:1, :ch].float().cpu().numpy().astype(np.float64)
+        out["cpu_baseline"] = cpu_baseline_scan(p, wl, cpu_s, y_rows,
+                                                tol=2e-2 if bf else 1e-4)
+    del x, dt, z, Bm, Cm, y, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_decode(torch, mamba, W, steps, warmup, settle_s, n_sets, with_conv=False,
+                   unfused=False):
+    """Decode steps of the [256, 5120, 16] workload, warm and cold.  Warm: one
+    state buffer (84 MB, resident in the 256 MB MALL between steps).  Cold:
+    n_sets state buffers (and conv windows) used in turn, more bytes than the
+    MALL holds, so every step reads its state from HBM."""
+    wl = W.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    init = W.decode_initial(wl)
+    T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
+    hs = [T(init["h0"]) for _ in range(n_sets)]
+    A, bias, Dk = T(init["A"]), T(init["dt_bias"]), T(init["Dskip"])
+    toks, toks_np = [], []
+    for s_ in range(8):
+        st = W.decode_step_inputs(wl, s_)
+        toks_np.append(st)
+        toks.append({k: T(v, torch.bfloat16) for k, v in st.items()})
+    y = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
+    K = 4
+    if with_conv:
+        ci = W.decode_conv_initial(wl, K)
+        cw = T(ci["conv_w"])
+        cstates = [T(ci["conv_state"], torch.bfloat16) for _ in range(n_sets)]
+        xc = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
+
+    def step(i, k):
+        t = toks[i % len(toks)]
+        x, h = t["x"], hs[k]
+        if with_conv and not unfused:  # conv front end and state update in one kernel
+            mamba.conv1d_selective_state_update(h, cstates[k], x, cw, t["dt"], A, t["Bm"],
+                                                t["Cm"], dt_bias=bias, Dskip=Dk, z=t["z"],
+                                                out=y)
+            return
+        if with_conv:
+            mamba.conv1d_update(cstates[k], x, cw, None, out=xc)
+            x = xc
+        mamba.selective_state_update(h, x, t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"], out=y)
+
+    nbytes = wl.B * wl.D * (2 * wl.N * 4 + 4 * 2) + wl.B * 2 * wl.N * 2 + wl.D * (wl.N + 2) * 4
+    if with_conv:  # window read and written (the state update above counts the raw input's
+        # read; the conv output never reaches memory when fused)
+        nbytes += wl.B * wl.D * 2 * (K - 1) * 2 + wl.D * K * 4
+    settle = settle_clocks(lambda: step(0, 0), torch, settle_s)
+    res = {}
+    for mode, sets in (("warm", 1), ("cold", n_sets)):
+        for i in range(warmup):
+            step(i, i % sets)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step(i, i % sets)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[mode] = {"ms_per_step": round(ms, 5), "GBps": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "state_sets": sets, "state_set_bytes": hs[0].numel() * 4}
+    res["clock_settle"] = settle
+    res["algorithmic_bytes_per_step"] = nbytes
+    res["toks_np"], res["init"] = toks_np, init
+    del hs, toks, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_block(args, torch, mamba, W):
     wl = W.WORKLOADS[1]
     B, D, L, N = wl.B, wl.D, wl.L, wl.N
@@ -288,10 +490,14 @@ def run_block(args, torch, mamba, W):
             mamba.conv1d_selective_scan_fwd(x_raw, cw, dt, A, Bm, Cm, dt_bias=bias, Dskip=Dk,
                                             z=z, out=y, workspace=ws)
 
-    for _ in range(args.warmup):
+    def block_step():
         if args.unfused:
             conv()
         scan()
+
+    settle = settle_clocks(block_step, torch, args.settle_seconds)
+    for _ in range(args.warmup):
+        block_step()
     torch.cuda.synchronize()
 
     ev = HipEvents()
@@ -323,12 +529,10 @@ def run_block(args, torch, mamba, W):
     sb = scan_bytes(B, D, L, N, 4) + (0 if args.unfused else D * K * 4)
     cb = conv_bytes(B, D, L, K, 4)
     achieved = sb / (scan_ms * 1e-3) / 1e9
-    tr = traffic_record("unfused" if args.unfused else "fused")
-    traffic = None
-    if tr is not None:
-        # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
-        # a copy kernel of known size; null once the kernel source has changed
-        traffic = int(round(tr["fetch_bytes"] + tr["write_bytes"]))
+    tr = traffic_record("block_unfused" if args.unfused else "block_fused")
+    # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+    # copy kernel of known size; null once the kernel source has changed
+    traffic = traffic_bytes(tr)
     kname = "scan_main_kernel<fp32>" if args.unfused else "scan_main_kernel<fp32, conv>"
     kernels = {"scan_ms": quantiles(scan_all),
                "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}
@@ -360,20 +564,64 @@ def run_block(args, torch, mamba, W):
                      "algorithmic_bytes": sb},
         "valu": valu_record(tr, elems, scan_ms),
         "kernels": kernels,
+        "clock_settle": settle,
     }
     if not args.no_cpu:
         y0 = y[0:1, :4].double().cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(p, B, D, L, y_gpu=y0)
+    if not args.headline_only:
+        del x_raw, cw, dt, A, Bm, Cm, bias, Dk, z, y, xc, ws
+        torch.cuda.empty_cache()
+        out["other_workloads"] = other_workloads(args, torch, mamba, W)
     return out
 
 
+def other_workloads(args, torch, mamba, W):
+    """The other configurations of the hot path, measured in the same run
+    beside the headline: the 2.8B-scale layer and the long sequence (bf16 scans
+    whose inputs far exceed the MALL), the small fp32 case, and the decode
+    workload warm and cold, each with its roofline and an oracle baseline."""
+    res = {}
+    for idx in (2, 3, 0):
+        wl = W.WORKLOADS[idx]
+        res[wl.name] = measure_scan(torch, mamba, W, idx, steps=20, warmup=10,
+                                    settle_s=min(args.settle_seconds, 0.5), cpu_s=4.0,
+                                    no_cpu=args.no_cpu)
+    wl = W.WORKLOADS[4]
+    d = measure_decode(torch, mamba, W, steps=200, warmup=20,
+                       settle_s=min(args.settle_seconds, 0.5), n_sets=args.decode_sets)
+    toks_np, init = d.pop("toks_np"), d.pop("init")
+    d["roofline"] = {"bound": "hbm", "achieved": d["cold"]["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d["cold"]["frac"],
+                     "traffic": traffic_bytes(traffic_record(wl.name)),
+                     "kernel": "state update (cold: state read from HBM every step)"}
+    if not args.no_cpu:
+        d["cpu_baseline"] = cpu_baseline_decode(wl, init, toks_np,
+                                                d["algorithmic_bytes_per_step"], target_s=4.0)
+    res[wl.name] = d
+    return res
+
+
 def run_scan(args, torch, mamba, W, idx, bidir=False, general=False):
-    """One workload's scan; bidir: the forward scan, then the reverse scan of
-    a second parameter set added into the same y (a bidirectional layer);
-    general: A[d, n] ~ -U(0.05, 5) with no structure across n (as after
-    training), which takes the general path."""
+    """One workload's scan as the JSON line.  bidir: the forward scan, then the
+    reverse scan of a second parameter set added into the same y (a
+    bidirectional layer); general: A[d, n] ~ -U(0.05, 5) with no structure
+    across n (as after training), which takes the general path."""
     wl = W.WORKLOADS[idx]
     B, D, L, N = wl.B, wl.D, wl.L, wl.N
+    line = {"metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
+            "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16-io/f32" if wl.io == "bf16" else "f32", "data": "synthetic"}
+    if not bidir and not general:
+        m = measure_scan(torch, mamba, W, idx, args.steps, args.warmup, args.settle_seconds,
+                         cpu_s=15.0, no_cpu=args.no_cpu)
+        line.update(value=m.pop("step_gelem_s"), ms_per_step=m.pop("ms_per_step"))
+        m.pop("steps"), m.pop("warmup")
+        cfg = m.pop("config")
+        line["config"] = {"workload": wl.name, **cfg, "step": "forward scan"}
+        line.update(m)
+        return line
     p = W.scan_inputs(wl)
     if general:
         p["A"] = (-np.random.default_rng(wl.seed + 77).uniform(0.05, 5.0, size=(D, N))).astype(
@@ -393,49 +641,45 @@ def run_scan(args, torch, mamba, W, idx, bidir=False, general=False):
         dt2, Bm2, Cm2 = T(q["dt"], io_t), T(q["Bm"], io_t), T(q["Cm"], io_t)
         A2, bias2, Dk2 = T(q["A"]), T(q["dt_bias"]), T(q["Dskip"])
 
-    def step(i=None, pair=None):
-        if pair is not None:
-            mamba.set_scan_timing_events_raw(pair[0], pair[1])
+    def step():
         mamba.selective_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y, workspace=ws)
         if bidir:
             mamba.set_scan_timing_events_raw(None, None)
             mamba.selective_scan_fwd(x, dt2, A2, Bm2, Cm2, bias2, Dk2, z, out=y, workspace=ws,
                                      reverse=True, accumulate=True)
 
+    settle = settle_clocks(step, torch, args.settle_seconds)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, pairs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    mamba.set_scan_timing_events_raw(None, None)
-    scan_all = [ev.elapsed_ms(a, b) for a, b in pairs]
+    ms_step, scan_all = time_with_scan_events(step, torch, mamba, args.steps)
     scan_ms = float(np.mean(scan_all))
-    ms_step = elapsed / args.steps * 1e3
     elems = B * D * L
     sb = scan_bytes(B, D, L, N, 2 if bf else 4)
     achieved = sb / (scan_ms * 1e-3) / 1e9
-    return {"metric": "selective-scan Gelem/s (B*L*D_inner) and HBM GB/s as % of MI355X peak",
-            "value": round(elems * (2 if bidir else 1) / (ms_step * 1e-3) / 1e9, 3),
-            "unit": "Gelem/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "bf16-io/f32", "data": "synthetic",
-            "config": {"workload": wl.name + ("_bidirectional" if bidir else "")
-                       + ("_general_A" if general else ""), "batch": B,
-                       "d_inner": D, "seq_len": L, "d_state": N, "io": wl.io,
-                       "step": ("forward scan, then reverse scan added into y" if bidir else
-                                "forward scan"),
-                       "elements_per_step": elems * (2 if bidir else 1)},
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel_ms": round(scan_ms, 4)},
-            "kernels": {"scan_ms": quantiles(scan_all),
-                        "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)}}
+    key = wl.name + ("_bidirectional" if bidir else "") + ("_general_A" if general else "")
+    tr = traffic_record(key)
+    line.update({
+        "value": round(elems * (2 if bidir else 1) / (ms_step * 1e-3) / 1e9, 3),
+        "ms_per_step": round(ms_step, 4),
+        "config": {"workload": key, "batch": B, "d_inner": D, "seq_len": L, "d_state": N,
+                   "io": wl.io,
+                   "step": ("forward scan, then reverse scan added into y" if bidir else
+                            "forward scan"),
+                   "elements_per_step": elems * (2 if bidir else 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_bytes(tr), "kernel_ms": round(scan_ms, 4),
+                     "algorithmic_bytes": sb,
+                     "kernel": "main scan kernel of the forward call"},
+        "valu": valu_record(tr, elems, scan_ms),
+        "kernels": {"scan_ms": quantiles(scan_all),
+                    "scan_gelem_s": round(elems / (scan_ms * 1e-3) / 1e9, 2)},
+        "clock_settle": settle})
+    if general and not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_scan(
+            p, wl, 15.0, y[0:1, :64].float().cpu().numpy().astype(np.float64),
+            tol=2e-2 if bf else 1e-4)
+    return line
 
 
 def run_bwd(args, torch, mamba, W):
@@ -458,6 +702,7 @@ def run_bwd(args, torch, mamba, W):
             mamba.set_scan_timing_events_raw(pair[0], pair[1])
         mamba.selective_scan_bwd(x, dt, A, Bm, Cm, dout, bias, Dk, z, workspace=ws)
 
+    settle = settle_clocks(step, torch, args.settle_seconds)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -475,7 +720,7 @@ def run_bwd(args, torch, mamba, W):
     elems = B * D * L
     return {"metric": "selective-scan backward Gelem/s (B*L*D_inner)",
             "value": round(elems / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "steps": args.steps, "warmup": args.warmup, "clock_settle": settle, "ms_per_step": round(ms_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic",
             "config": {"workload": f"scan_bwd_b{B}_d{D}_l{L}_n{N}_f32", "batch": B,
@@ -513,6 +758,7 @@ def run_ssd(args, torch, mamba, W):
             mamba.set_scan_timing_events_raw(pair[0], pair[1])
         mamba.ssd_scan_fwd(x, dt, A, Bm, Cm, bias, Dk, z, out=y)
 
+    settle = settle_clocks(step, torch, args.settle_seconds)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -541,7 +787,7 @@ def run_ssd(args, torch, mamba, W):
     flops = chunks * (2 * (Q * (Q + 1) // 2) * (wl.N + wl.P) + 2 * 2 * Q * wl.N * wl.P)
     return {"metric": "Mamba-2 form scan Gelem/s (B*L*H*P) and HBM GB/s as % of MI355X peak",
             "value": round(elems / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "steps": args.steps, "warmup": args.warmup, "clock_settle": settle, "ms_per_step": round(ms_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16-io/f32", "data": "synthetic",
             "config": {"workload": wl.name, "batch": wl.B, "seq_len": wl.L, "heads": wl.H,
@@ -561,65 +807,33 @@ def run_ssd(args, torch, mamba, W):
 
 def run_decode(args, torch, mamba, W):
     wl = W.WORKLOADS[4]
-    dev = torch.device("cuda:0")
-    init = W.decode_initial(wl)
-    T = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(t)
-    h = T(init["h0"])
-    A, bias, Dk = T(init["A"]), T(init["dt_bias"]), T(init["Dskip"])
-    toks, toks_np = [], []
-    for s in range(8):
-        st = W.decode_step_inputs(wl, s)
-        toks_np.append(st)
-        toks.append({k: T(v, torch.bfloat16) for k, v in st.items()})
-    y = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
     K = 4
-    if args.with_conv:
-        ci = W.decode_conv_initial(wl, K)
-        cw, cstate = T(ci["conv_w"]), T(ci["conv_state"], torch.bfloat16)
-        xc = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
-
-    def step(i):
-        t = toks[i % len(toks)]
-        x = t["x"]
-        if args.with_conv and not args.unfused:  # conv front end and state update in one kernel
-            mamba.conv1d_selective_state_update(h, cstate, x, cw, t["dt"], A, t["Bm"], t["Cm"],
-                                                dt_bias=bias, Dskip=Dk, z=t["z"], out=y)
-            return
-        if args.with_conv:  # the token's raw input through the conv front end first
-            mamba.conv1d_update(cstate, x, cw, None, out=xc)
-            x = xc
-        mamba.selective_state_update(h, x, t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"],
-                                     out=y)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    nbytes = wl.B * wl.D * (2 * wl.N * 4 + 4 * 2) + wl.B * 2 * wl.N * 2 + wl.D * (wl.N + 2) * 4
-    if args.with_conv:  # window read and written (the state update above counts the raw
-        # input's read; the conv output never reaches memory when fused)
-        nbytes += wl.B * wl.D * 2 * (K - 1) * 2 + wl.D * K * 4
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    d = measure_decode(torch, mamba, W, args.steps, args.warmup, args.settle_seconds,
+                       args.decode_sets, with_conv=args.with_conv, unfused=args.unfused)
+    toks_np, init = d.pop("toks_np"), d.pop("init")
+    nbytes = d["algorithmic_bytes_per_step"]
+    cold = d["cold"]
     metric = ("decode step (conv update + state update) GB/s" if args.with_conv else
               "decode state update GB/s")
-    return {"metric": metric, "value": round(gbs, 1), "unit": "GB/s",
+    key = wl.name + ("_conv" if args.with_conv else "")
+    return {"metric": metric, "value": cold["GBps"], "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "ms_per_step": cold["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16-io/f32", "data": "synthetic",
             "config": {"workload": wl.name, "batch": wl.B, "d_inner": wl.D, "d_state": wl.N,
+                       "state_sets": args.decode_sets,
                        **({"d_conv": K,
                            "step": ("conv1d_update, then selective_state_update" if args.unfused
                                     else "conv1d_selective_state_update (one kernel)")}
                           if args.with_conv else {})},
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "note": "state (84 MB) stays resident in the 256 MB MALL between steps"},
+            "roofline": {"bound": "hbm", "achieved": cold["GBps"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": cold["frac"],
+                         "traffic": traffic_bytes(traffic_record(key)),
+                         "note": (f"cold: {args.decode_sets} state sets of "
+                                  f"{cold['state_set_bytes'] / 1e6:.0f} MB used in turn, more "
+                                  "than the 256 MB MALL holds")},
+            "warm": d["warm"], "cold": cold, "clock_settle": d["clock_settle"],
+            "algorithmic_bytes_per_step": nbytes,
             **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_decode(
                 wl, init, toks_np, nbytes, W.decode_conv_initial(wl, K) if args.with_conv
                 else None)})}
@@ -645,6 +859,12 @@ def main():
                     help="decode workload: each step runs the conv front end's decode step "
                          "(K = 4) on the token's raw input, then the state update, fused into "
                          "one kernel (conv1d_selective_state_update)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="block workload: skip the other configurations")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed back-to-back steps before the warm-up, for steady clocks")
+    ap.add_argument("--decode-sets", type=int, default=8,
+                    help="decode: state buffers used in turn for the cold figure (8 x 84 MB)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one elementwise kernel that reads and writes "
                          "this many MiB (known traffic for scaling rocprofv3 byte counters)")

@@ -49,10 +49,6 @@
 #include "device_common.h"
 #include "internal.h"
 
-#ifndef SCAN_WAVES_PER_SIMD
-#define SCAN_WAVES_PER_SIMD 3
-#endif
-
 namespace mamba {
 
 namespace {
@@ -67,34 +63,34 @@ struct WsHeader {
 constexpr uint32_t kFlagAgg = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
 constexpr int kSpinLimit = 1 << 22;
-#ifndef SCAN_SUPERSEG
-#define SCAN_SUPERSEG 8
-#endif
-constexpr int64_t kSuperSeg = SCAN_SUPERSEG;  // segments per superblock of the carry
-#ifdef SCAN_TRACE
-#define TRACE_POINT(k)                                                                        \
-    do {                                                                                      \
-        if (lane == 0)                                                                        \
-            reinterpret_cast<uint64_t *>(p.ws + lay.total - (size_t)lay.n_items * 256)[(item * 4 + w) * 8 + (k)] = \
-                __builtin_amdgcn_s_memrealtime();                                             \
-    } while (0)
-#else
-#define TRACE_POINT(k) \
-    do {               \
-    } while (0)
-#endif
+// segments per superblock of the carry (16 or 32 measured 1-8% slower on the
+// three forward workloads, 4 or 6 within 1%)
+constexpr int64_t kSuperSeg = 8;
+// waves per SIMD the register budget is held to (158-167 VGPRs)
+constexpr int kScanWavesPerSimd = 3;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
 // Prep kernel: clears the ticket, the error word and the per-segment flags,
-// and decides per 64-channel tile whether A has the structured form.
+// zeroes the tags of every inclusive record the main kernel will poll, and
+// decides per 64-channel tile whether A has the structured form.
 __global__ void __launch_bounds__(256) scan_prep_kernel(const float *__restrict__ A,
                                                         unsigned char *__restrict__ ws,
                                                         ScanWsLayout lay, int64_t D, int N,
-                                                        int64_t n_flags, int64_t classify_base)
+                                                        int64_t n_flags, int64_t classify_base,
+                                                        int64_t clear_base, int64_t n_clear16)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= clear_base) {
+        // Polled inclusive records start this call with tag 0, which no call
+        // uses, so a word carries this call's epoch only once this call has
+        // written it, whatever the workspace's memory held before.
+        const int64_t k = i - clear_base;
+        if (k < n_clear16)
+            reinterpret_cast<uint4 *>(ws + lay.off_incl)[k] = make_uint4(0u, 0u, 0u, 0u);
+        return;
+    }
     if (i < n_flags) {
         if (i == 0) {
             WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + lay.off_header);
@@ -291,9 +287,9 @@ __device__ __forceinline__ void store_rec(float *p, float v)
 // 64-bit word, beside the value: a reader accepts a word once its tag is this
 // call's, so the record needs no flag, its writer no wait for its stores, and
 // its reader one round trip.  Each 64-bit word is written and read
-// atomically.  Stale words of earlier calls carry older epochs (the epoch
-// skips 0 and would only repeat after 2^32 calls on one workspace); a fresh
-// workspace would need all 16 of a lane's words to hold this epoch by chance.
+// atomically.  The prep kernel of the same call has set the tag of every
+// polled word to 0 and the epoch is never 0, so only a word this call wrote
+// can match, whatever the workspace's memory held before the call.
 __device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t epoch)
 {
     const uint64_t w = ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
@@ -562,7 +558,6 @@ __device__ __forceinline__ void scan_segment(
     const int64_t row_off = (b * p.D + dc) * p.L + p0;
     const int64_t chunk_slot = REV ? Ls / kChunkT - 1 - t0 / kChunkT : t0 / kChunkT;
     auto slot = [](int j) { return REV ? kChunkT - 1 - j : j; };
-    TRACE_POINT(0);
 
     // per-channel constants.  Loaded unconditionally (an absent dt_bias or D
     // is read through A, which has at least D entries, and ignored), so the
@@ -724,7 +719,6 @@ __device__ __forceinline__ void scan_segment(
             summ = cumL;
         }
     }
-    TRACE_POINT(1);
 
     // z is only needed by the final gating.  bf16 z (16 VGPRs) is requested
     // now, so it arrives while the workgroup resolves its start state; wave 0
@@ -741,8 +735,6 @@ __device__ __forceinline__ void scan_segment(
     for (int n = 0; n < kMaxN; ++n)
         s_agg[w][1 + n][lane] = hs[n];
     __syncthreads();
-
-    TRACE_POINT(2);
     // ---- 3. segment map and the records this segment folds ------------------
     // Fixed association order, independent of scheduling: a segment folds the
     // aggregates of the earlier segments of its superblock, in order, onto the
@@ -793,8 +785,6 @@ __device__ __forceinline__ void scan_segment(
         }
     }
     __syncthreads();
-
-    TRACE_POINT(3);
     // ---- 4. fold the predecessors' aggregates, four waves in parallel --------
     {
         const int64_t per = (depth + kWavesPerSeg - 1) / kWavesPerSeg;
@@ -829,8 +819,6 @@ __device__ __forceinline__ void scan_segment(
                 slot[1 + n][lane] = ps[n];
         }
         __syncthreads();
-
-        TRACE_POINT(4);
         // ---- 5. segment start state and inclusive record ---------------------
         if (w == 0) {
             float hin[kMaxN];
@@ -893,7 +881,6 @@ __device__ __forceinline__ void scan_segment(
         }
     }
     __syncthreads();
-    TRACE_POINT(5);
 
     if (nt <= 0)
         return;
@@ -970,11 +957,10 @@ __device__ __forceinline__ void scan_segment(
     if (active)
         store_chunk<BF16>(p.y, row_off, klo, khi, vec, p.accumulate != 0,
                           [&](int k) { return yl[slot(k)]; });
-    TRACE_POINT(6);
 }
 
 template <bool BF16, bool CONV, bool REV, bool ADJ>
-__global__ void __launch_bounds__(kWave *kWavesPerSeg, SCAN_WAVES_PER_SIMD) scan_main_kernel(
+__global__ void __launch_bounds__(kWave *kWavesPerSeg, kScanWavesPerSimd) scan_main_kernel(
     ScanKArgs p, const uint32_t *__restrict__ tiles)
 {
     __shared__ float s_agg[kWavesPerSeg][kAggFields][kWave];
@@ -1063,9 +1049,6 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L)
     off = round_up(off + (size_t)(((l.n_seg + kSuperSeg - 1) / kSuperSeg) * l.groups) *
                              kInclFields * kWave * 8,
                    256);
-#ifdef SCAN_TRACE
-    off = round_up(off + (size_t)l.n_items * 256, 256);
-#endif
     l.total = off;
     return l;
 }
@@ -1101,12 +1084,17 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     }
     if (lay.n_items == 0)
         return hipSuccess;
-    // prep: flags and header, then tile classification from a wave boundary
+    // prep: flags and header, then tile classification, then the tags of the
+    // inclusive records (every superblock but the last is polled), each part
+    // from a wave boundary
     const int64_t n_flags = lay.n_items;
     const int64_t classify_base = (n_flags + kWave - 1) / kWave * kWave;
-    const int64_t total = classify_base + lay.n_dtiles * kWave;
+    const int64_t clear_base = classify_base + lay.n_dtiles * kWave;
+    const int64_t n_sb = (lay.n_seg + kSuperSeg - 1) / kSuperSeg;
+    const int64_t n_clear16 = (n_sb - 1) * lay.groups * kInclFields * kWave * 8 / 16;
+    const int64_t total = clear_base + n_clear16;
     hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       a.A, a.ws, lay, a.D, a.N, n_flags, classify_base);
+                       a.A, a.ws, lay, a.D, a.N, n_flags, classify_base, clear_base, n_clear16);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

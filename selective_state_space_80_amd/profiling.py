@@ -3,8 +3,8 @@
     python -m selective_state_space_80_amd.profiling trace  RESULTS.db
     python -m selective_state_space_80_amd.profiling counters RESULTS.db [RESULTS.db ...]
     python -m selective_state_space_80_amd.profiling traffic --fetch F.db --write W.db \
-        --copy-bytes N --kernel scan_main_kernel [--sq SQ.db] [--variant fused|unfused] \
-        --out profiles/scan_traffic.json
+        --copy-bytes N --kernel KERNEL --source SRC [--sq SQ.db] [--variant WORKLOAD] \
+        --out profiles/traffic.json
 
 ``trace`` prints per-kernel call counts and average durations in microseconds (from
 ``rocprofv3 --kernel-trace --stats``); ``counters`` prints per-kernel averages of
@@ -85,7 +85,9 @@ def traffic(fetch_db, write_db, copy_bytes, kernel, source=None, sq_db=None):
         out["valu_insts"] = sq["SQ_INSTS_VALU"]
         out["waves"] = sq["SQ_WAVES"]
     if source:
-        out["scan_fwd_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
+        out["source"] = os.path.relpath(source, os.path.dirname(os.path.dirname(
+            os.path.abspath(__file__))))
+        out["source_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
     return out
 
 
@@ -104,8 +106,8 @@ def main(argv=None):
     tr.add_argument("--kernel", default="scan_main_kernel")
     tr.add_argument("--source", default=None, help="kernel source to fingerprint")
     tr.add_argument("--sq", default=None, help="run with SQ_INSTS_VALU and SQ_WAVES")
-    tr.add_argument("--variant", default="fused",
-                    help="key of the record in --out (fused / unfused block step)")
+    tr.add_argument("--variant", default="block_fused",
+                    help="key of the record in --out: the workload it was taken on")
     tr.add_argument("--out", default=None)
     a = ap.parse_args(argv)
     if a.cmd == "trace":

@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 
 import oracle
-from scan_check import STATE_TOL, TOL, assert_within, dev, host, sample_channels, say
+from scan_check import (STATE_TOL, TOL, assert_within, check_scan_full, dev, host,
+                        oracle_conv_full, oracle_state_update_threaded, say)
 from selective_state_space_80_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -62,10 +63,10 @@ def test_conv_fallback_layouts(case, io):
     assert_within(host(out), want, CONV_TOL[io], "conv")
 
 
-def test_block_workload_sampled():
-    """The d_model=768 block: conv1d(k=4)+SiLU feeding the scan, full size,
-    checked on sampled channels (oracle conv then oracle scan in fp64)."""
-    import torch
+def test_block_workload_every_element():
+    """The d_model=768 block (B=2 D=1536 L=8192, fp32): conv1d(k=4)+SiLU, then
+    the scan, as two calls at full size; the conv output, every scan output
+    and every final state against the oracle (conv, then scan, in fp64)."""
     import selective_state_space_80_amd as mamba
     wl = W.WORKLOADS[1]
     say(f"block {wl.name}: drawing inputs")
@@ -75,18 +76,11 @@ def test_block_workload_sampled():
     y, hl = mamba.selective_scan_fwd(xc, dev(p["dt"]), dev(p["A"]), dev(p["Bm"]), dev(p["Cm"]),
                                      dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]),
                                      z=dev(p["z"]), return_last_state=True)
-    bs, ds = sample_channels(wl.B, wl.D, seed=1)
-    bi, di = torch.tensor(bs, device="cuda"), torch.tensor(ds, device="cuda")
-    pick = lambda t: host(t.index_select(0, bi).index_select(1, di))
-    x_or = oracle.conv1d_silu(p["x_raw"][np.ix_(bs, ds)], p["conv_w"][ds])
-    assert_within(pick(xc), x_or, CONV_TOL["f32"], "block conv")
-    sub = lambda a: a[np.ix_(bs, ds)]
-    yo, ho = oracle.selective_scan(x_or, sub(p["dt"]), p["A"][ds], p["Bm"][bs], p["Cm"][bs],
-                                   dt_bias=p["dt_bias"][ds], Dskip=p["Dskip"][ds],
-                                   z=sub(p["z"]), nthreads=8)
-    e = assert_within(pick(y), yo, TOL["f32"], "block y")
-    assert_within(pick(hl), ho, STATE_TOL, "block h_last")
-    say(f"  max rel err {e:.2e}")
+    say("  oracle conv over every channel")
+    x_or = oracle_conv_full(p["x_raw"], p["conv_w"])
+    e = assert_within(host(xc), x_or, CONV_TOL["f32"], "block conv")
+    say(f"  conv: every element compared, max rel err {e:.3e}")
+    check_scan_full(y, hl, p, "f32", x=x_or, label="block scan")
 
 
 @pytest.mark.parametrize("N", [16, 5])
@@ -167,29 +161,37 @@ def test_decode_steps_equal_scan():
 
 
 def test_decode_workload_1024_steps():
-    """Decode workload: 1024 steps on [256, 5120, 16] fp32 state with fresh bf16
-    tokens, checked against the oracle every 128 steps on sampled channels."""
-    import torch
+    """Decode workload: 1024 steps on the [256, 5120, 16] fp32 state with fresh
+    bf16 tokens; every 128 steps, every output and every state element is
+    compared with the oracle (which runs every step over every channel)."""
+    from concurrent.futures import ThreadPoolExecutor
     import selective_state_space_80_amd as mamba
     wl = W.WORKLOADS[4]
     say(f"decode {wl.name}")
     init = W.decode_initial(wl)
     h = dev(init["h0"])
     A, bias, Dk = dev(init["A"]), dev(init["dt_bias"]), dev(init["Dskip"])
-    bs, ds = sample_channels(wl.B, wl.D, seed=4)
-    h_or = init["h0"][np.ix_(bs, ds)].astype(np.float64)
-    bi, di = torch.tensor(bs, device="cuda"), torch.tensor(ds, device="cuda")
-    for step in range(wl.steps):
-        s = W.decode_step_inputs(wl, step)
-        y = mamba.selective_state_update(h, dev(s["x"], "bf16"), dev(s["dt"], "bf16"), A,
-                                         dev(s["Bm"], "bf16"), dev(s["Cm"], "bf16"), bias, Dk,
-                                         dev(s["z"], "bf16"))
-        sub = lambda a: a[np.ix_(bs, ds)]
-        yo, h_or = oracle.state_update(h_or, sub(s["x"]), sub(s["dt"]), init["A"][ds],
-                                       s["Bm"][bs], s["Cm"][bs], dt_bias=init["dt_bias"][ds],
-                                       Dskip=init["Dskip"][ds], z=sub(s["z"]))
-        if (step + 1) % wl.check_every == 0:
-            pick = lambda t: host(t.index_select(0, bi).index_select(1, di))
-            e1 = assert_within(pick(y), yo, TOL["bf16"], f"decode y step {step + 1}")
-            e2 = assert_within(pick(h), h_or, STATE_TOL, f"decode h step {step + 1}")
-            say(f"  step {step + 1}: max rel err y {e1:.2e} h {e2:.2e}")
+    h_or = init["h0"].astype(np.float64)
+    worst_y = worst_h = 0.0
+    # the seeded per-step inputs are drawn a few steps ahead on host threads
+    with ThreadPoolExecutor(4) as ex:
+        ahead = [ex.submit(W.decode_step_inputs, wl, s) for s in range(min(8, wl.steps))]
+        for step in range(wl.steps):
+            s = ahead[step].result()
+            if step + 8 < wl.steps:
+                ahead.append(ex.submit(W.decode_step_inputs, wl, step + 8))
+            ahead[step] = None
+            y = mamba.selective_state_update(h, dev(s["x"], "bf16"), dev(s["dt"], "bf16"), A,
+                                             dev(s["Bm"], "bf16"), dev(s["Cm"], "bf16"), bias,
+                                             Dk, dev(s["z"], "bf16"))
+            yo, h_or = oracle_state_update_threaded(h_or, s["x"], s["dt"], init["A"], s["Bm"],
+                                                    s["Cm"], dt_bias=init["dt_bias"],
+                                                    Dskip=init["Dskip"], z=s["z"])
+            if (step + 1) % wl.check_every == 0:
+                e1 = assert_within(host(y), yo, TOL["bf16"], f"decode y step {step + 1}")
+                e2 = assert_within(host(h), h_or, STATE_TOL, f"decode h step {step + 1}")
+                worst_y, worst_h = max(worst_y, e1), max(worst_h, e2)
+                say(f"  step {step + 1}: every element compared ({y.numel()} outputs, "
+                    f"{h.numel()} states); max rel err y {e1:.2e} h {e2:.2e}")
+    say(f"  decode: max rel err y {worst_y:.3e} (tol {TOL['bf16']}) h {worst_h:.3e} "
+        f"(tol {STATE_TOL})")
