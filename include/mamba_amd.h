@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 6
+#define MAMBA_AMD_ABI_VERSION 7
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
@@ -73,7 +73,8 @@ typedef enum {
     MAMBA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
     MAMBA_ERR_WORKSPACE = 7,   /* workspace missing, misaligned or too small  */
     MAMBA_ERR_LAUNCH = 8,      /* HIP reported an error when launching        */
-    MAMBA_ERR_DEVICE = 9       /* no HIP device, or not a gfx950 device       */
+    MAMBA_ERR_DEVICE = 9,      /* no HIP device, or not a gfx950 device       */
+    MAMBA_ERR_TIMEOUT = 10     /* a scan's carry wait gave up (see below)     */
 } mamba_status;
 
 /* Static, human-readable name of a status value (never NULL). */
@@ -320,6 +321,32 @@ mamba_status mamba_ssd_scan_fwd(const void *x, const void *dt, const float *dt_b
  * kernel of mamba_ssd_scan_fwd, on the call's stream.  Pass NULL, NULL to turn it off.
  */
 void mamba_set_scan_timing_events(void *start, void *stop);
+
+/*
+ * Health of the cross-chunk carry of the calls that last used `workspace`
+ * (of mamba_selective_scan_fwd and its variants, or of
+ * mamba_selective_scan_bwd, whose two scans both report here).  Blocks until
+ * `stream` has finished its work, then reads the workspace's error word:
+ * MAMBA_OK, or MAMBA_ERR_TIMEOUT when a wait of a segment for its
+ * predecessors' carry records gave up.  Such a wait is bounded (only a
+ * device fault can make it time out); the segments whose start state it
+ * would have given, and everything computed from them, are then NaN instead
+ * of a silently wrong number.  The word is cleared by the next scan call on
+ * the workspace.  MAMBA_ERR_WORKSPACE for a NULL, misaligned or too small
+ * (< 256 bytes) workspace; MAMBA_ERR_LAUNCH when the stream reports an error
+ * or is being captured into a graph (then nothing is waited for or read).
+ */
+mamba_status mamba_selective_scan_check(const void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
+/*
+ * Diagnostic hook for tests of the failure path: polls before a carry wait of
+ * later scan calls (from any host thread) gives up; polls < 0 restores the
+ * default (2^22, far beyond any real wait).  With 0, any wait not satisfied at
+ * its first poll gives up, so a test can make the NaN poisoning and
+ * MAMBA_ERR_TIMEOUT happen while every kernel still ends normally.
+ */
+void mamba_set_scan_spin_limit(int polls);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,9 @@ Entry points (same names as the C ABI, without the ``mamba_`` prefix):
   selective_scan_bwd_workspace_size(B, D, L, N, dtype)
   ssd_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
                return_last_state=False, out=None, h_last=None)
+  selective_scan_check(workspace)        the carry's error word (after a sync)
+  set_scan_spin_limit(polls)             diagnostic bound of the carry waits
+Test helper: set_carry_checks(True) checks the carry after every scan call.
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmamba_amd.so")
-ABI_VERSION = 6  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
+ABI_VERSION = 7  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
 
 MAMBA_F32 = 0
 MAMBA_BF16 = 1
@@ -37,7 +40,8 @@ MAMBA_SCAN_ACCUMULATE = 2
 
 STATUS_NAMES = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ERR_DTYPE",
                 4: "MAMBA_ERR_UNSUPPORTED", 5: "MAMBA_ERR_ALIGN", 6: "MAMBA_ERR_ALIAS",
-                7: "MAMBA_ERR_WORKSPACE", 8: "MAMBA_ERR_LAUNCH", 9: "MAMBA_ERR_DEVICE"}
+                7: "MAMBA_ERR_WORKSPACE", 8: "MAMBA_ERR_LAUNCH", 9: "MAMBA_ERR_DEVICE",
+                10: "MAMBA_ERR_TIMEOUT"}
 
 # every symbol include/mamba_amd.h declares
 EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
@@ -46,7 +50,8 @@ EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_conv1d_selective_scan_fwd",
             "mamba_conv1d_update", "mamba_set_scan_timing_events",
             "mamba_selective_scan_bwd_workspace_size", "mamba_selective_scan_bwd",
-            "mamba_ssd_scan_fwd", "mamba_conv1d_selective_state_update"]
+            "mamba_ssd_scan_fwd", "mamba_conv1d_selective_state_update",
+            "mamba_selective_scan_check", "mamba_set_scan_spin_limit"]
 
 _lib = None
 
@@ -102,6 +107,10 @@ def load_library(path: str = LIBRARY):
     lib.mamba_ssd_scan_fwd.argtypes = [P] * 11 + [I64] * 6 + [I32, P]
     lib.mamba_set_scan_timing_events.restype = None
     lib.mamba_set_scan_timing_events.argtypes = [P, P]
+    lib.mamba_selective_scan_check.restype = I32
+    lib.mamba_selective_scan_check.argtypes = [P, SZ, P]
+    lib.mamba_set_scan_spin_limit.restype = None
+    lib.mamba_set_scan_spin_limit.argtypes = [I32]
     _lib = lib
     return lib
 
@@ -174,6 +183,38 @@ def conv1d_silu(x, w, bias=None, out=None):
     return out
 
 
+_carry_checks = False
+
+
+def set_carry_checks(on: bool = True) -> None:
+    """After every scan and backward call, wait for the stream and check the
+    workspace's carry error word (raises MambaError with MAMBA_ERR_TIMEOUT).
+    Each check synchronizes, so this is for tests, not for timed runs."""
+    global _carry_checks
+    _carry_checks = bool(on)
+
+
+def selective_scan_check(workspace) -> None:
+    """Wait for the workspace's stream, then raise MambaError(MAMBA_ERR_TIMEOUT)
+    if a carry wait of the calls that last used it gave up (their affected
+    outputs are NaN)."""
+    st = load_library().mamba_selective_scan_check(_ptr(workspace), workspace.numel(),
+                                                   _stream(workspace.device))
+    _raise(st, "mamba_selective_scan_check")
+
+
+def set_scan_spin_limit(polls: int) -> None:
+    """Diagnostic: polls before a carry wait of later scans gives up (< 0: the
+    default).  0 makes any wait not met at once give up, for failure-path tests."""
+    load_library().mamba_set_scan_spin_limit(int(polls))
+
+
+def _after_scan(workspace, need):
+    # a check synchronizes, which a stream under graph capture cannot do
+    if _carry_checks and need >= 256 and not _torch().cuda.is_current_stream_capturing():
+        selective_scan_check(workspace)
+
+
 def selective_scan_fwd_workspace_size(B, D, L, N, dtype=None) -> int:
     io = MAMBA_F32 if dtype is None else _io_dtype(_torch().empty(0, dtype=dtype))
     return int(load_library().mamba_selective_scan_fwd_workspace_size(B, D, L, N, io))
@@ -225,6 +266,7 @@ def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=No
             _ptr(h0), _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N,
             io, _stream(dev))
         _raise(st, "mamba_selective_scan_fwd")
+    _after_scan(workspace, need)
     if return_last_state:
         return out, h_last
     return out
@@ -277,6 +319,7 @@ def conv1d_selective_scan_fwd(x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None, conv
         _ptr(out), _ptr(h_last), _ptr(workspace), workspace.numel(), B, D, L, N, io,
         _stream(dev))
     _raise(st, "mamba_conv1d_selective_scan_fwd")
+    _after_scan(workspace, need)
     res = [out]
     if return_last_state:
         res.append(h_last)
@@ -412,6 +455,7 @@ def selective_scan_bwd(x, dt, A, Bm, Cm, dout, dt_bias=None, Dskip=None, z=None,
         _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
         _ptr(g["dh0"]), _ptr(workspace), workspace.numel(), B, D, L, N, io, _stream(dev))
     _raise(st, "mamba_selective_scan_bwd")
+    _after_scan(workspace, need)
     return g
 
 

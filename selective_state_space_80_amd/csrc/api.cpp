@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <atomic>
 #include <mutex>
 
 #include "internal.h"
@@ -22,6 +23,7 @@ constexpr int64_t kMaxGrid = int64_t(1) << 31;
 
 thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
+std::atomic<int> g_spin_limit{mamba::kDefaultSpinLimit};
 
 bool valid_dtype(int dt) { return dt == MAMBA_F32 || dt == MAMBA_BF16; }
 size_t esize(mamba_dtype dt) { return dt == MAMBA_BF16 ? 2 : 4; }
@@ -98,11 +100,38 @@ const char *mamba_status_string(int status)
     case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MAMBA_ERR_LAUNCH: return "MAMBA_ERR_LAUNCH: HIP failed to launch a kernel";
     case MAMBA_ERR_DEVICE: return "MAMBA_ERR_DEVICE: no gfx950 HIP device is current";
+    case MAMBA_ERR_TIMEOUT: return "MAMBA_ERR_TIMEOUT: a carry wait of the scan gave up (outputs poisoned with NaN)";
     default: return "unknown mamba_status";
     }
 }
 
 int mamba_abi_version(void) { return MAMBA_AMD_ABI_VERSION; }
+
+void mamba_set_scan_spin_limit(int polls)
+{
+    g_spin_limit.store(polls < 0 ? mamba::kDefaultSpinLimit : polls);
+}
+
+mamba_status mamba_selective_scan_check(const void *workspace, size_t workspace_bytes,
+                                        void *stream)
+{
+    if (!workspace || workspace_bytes < 256 || !aligned(workspace, 256))
+        return MAMBA_ERR_WORKSPACE;
+    mamba_status st = device_ok();
+    if (st != MAMBA_OK)
+        return st;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)stream, &cap) != hipSuccess ||
+        cap != hipStreamCaptureStatusNone)
+        return MAMBA_ERR_LAUNCH;  // a stream under graph capture cannot be waited for
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return MAMBA_ERR_LAUNCH;
+    uint32_t word = 0;
+    if (hipMemcpy(&word, (const unsigned char *)workspace + mamba::kScanErrorWordOffset,
+                  sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        return MAMBA_ERR_LAUNCH;
+    return word ? MAMBA_ERR_TIMEOUT : MAMBA_OK;
+}
 
 void mamba_set_scan_timing_events(void *start, void *stop)
 {
@@ -284,6 +313,7 @@ mamba_status scan_entry(const void *x, int64_t conv_K, const float *conv_w,
     a.accumulate = (flags & MAMBA_SCAN_ACCUMULATE) != 0;
     a.ev_start = g_ev_start;
     a.ev_stop = g_ev_stop;
+    a.spin_limit = g_spin_limit.load();
     return launched(mamba::launch_selective_scan(a, (hipStream_t)stream));
 }
 
@@ -567,6 +597,7 @@ mamba_status mamba_selective_scan_bwd(
     a.bf16 = io == MAMBA_BF16;
     a.ev_start = g_ev_start;
     a.ev_stop = g_ev_stop;
+    a.spin_limit = g_spin_limit.load();
     return launched(mamba::launch_selective_scan_bwd(a, (hipStream_t)stream));
 }
 

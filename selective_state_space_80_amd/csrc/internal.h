@@ -37,6 +37,14 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L);
 constexpr uint32_t kPathStructured = 0u;
 constexpr uint32_t kPathGeneral = 1u;
 
+// Byte offset of the scan workspace's error word (bit 0: a carry wait timed
+// out); the header starts the workspace, also inside the backward's.
+constexpr size_t kScanErrorWordOffset = 4;
+
+// Polls (each followed by a short sleep) before a carry wait of the scan
+// gives up: far beyond any real wait, so only a fault makes it happen.
+constexpr int kDefaultSpinLimit = 1 << 22;
+
 // Fused causal conv1d front end of the scan: at most this many taps.
 constexpr int kFusedConvTaps = 4;
 
@@ -64,6 +72,10 @@ struct ScanArgs {
     // its start state in scan order, [groups][n_seg*4][16][64] floats
     bool adjoint = false;
     float *chunk_states = nullptr;
+    // the workspace's error word keeps an earlier scan's timeout (the second
+    // scan of a backward call) instead of starting from zero
+    bool keep_error = false;
+    int spin_limit = kDefaultSpinLimit;  // polls before a carry wait gives up
     hipEvent_t ev_start, ev_stop;  // optional timing of the main kernel
 };
 hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s);
@@ -87,6 +99,7 @@ struct BwdArgsHost {
     int N;
     bool bf16;
     hipEvent_t ev_start, ev_stop;  // optional timing of the chunk-gradient kernel
+    int spin_limit = kDefaultSpinLimit;  // of the two scans' carry waits
 };
 hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s);
 

@@ -596,6 +596,8 @@ hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s)
     f.accumulate = false;
     f.adjoint = false;
     f.chunk_states = hsave;
+    f.keep_error = false;
+    f.spin_limit = a.spin_limit;
     f.ev_start = f.ev_stop = nullptr;
     hipError_t e = launch_selective_scan(f, s);
     if (e != hipSuccess)
@@ -610,6 +612,7 @@ hipError_t launch_selective_scan_bwd(const BwdArgsHost &a, hipStream_t s)
     r.reverse = true;
     r.adjoint = true;
     r.chunk_states = nusave;
+    r.keep_error = true;  // the forward scan's timeout, if any, stays reported
     e = launch_selective_scan(r, s);
     if (e != hipSuccess)
         return e;

@@ -46,6 +46,8 @@
 //   general     any A: per state exp and the ZOH input coefficient
 //               (exp(ΔA_n) - 1)/A_n, by series near ΔA_n = 0 (which includes the
 //               A_n = 0 limit Δ).  Slower, exact form.
+#include <cstddef>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -55,14 +57,14 @@ namespace {
 
 struct WsHeader {
     uint32_t ticket;
-    uint32_t error;
+    uint32_t error;  // bit 0: a carry wait timed out (read by mamba_selective_scan_check)
     uint32_t epoch;  // call counter (never 0): tag of this call's inclusive records
     uint32_t pad[61];
 };
+static_assert(offsetof(WsHeader, error) == kScanErrorWordOffset, "error word of the header");
 
 constexpr uint32_t kFlagAgg = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
-constexpr int kSpinLimit = 1 << 22;
 // segments per superblock of the carry (16 or 32 measured 1-8% slower on the
 // three forward workloads, 4 or 6 within 1%)
 constexpr int64_t kSuperSeg = 8;
@@ -79,7 +81,8 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(const float *__restrict_
                                                         unsigned char *__restrict__ ws,
                                                         ScanWsLayout lay, int64_t D, int N,
                                                         int64_t n_flags, int64_t classify_base,
-                                                        int64_t clear_base, int64_t n_clear16)
+                                                        int64_t clear_base, int64_t n_clear16,
+                                                        int keep_error)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= clear_base) {
@@ -95,7 +98,8 @@ __global__ void __launch_bounds__(256) scan_prep_kernel(const float *__restrict_
         if (i == 0) {
             WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + lay.off_header);
             hdr->ticket = 0u;
-            hdr->error = 0u;
+            if (!keep_error)
+                hdr->error = 0u;
             const uint32_t e = hdr->epoch + 1u;
             hdr->epoch = e ? e : 1u;
         }
@@ -309,20 +313,22 @@ __device__ __forceinline__ void publish_flag(uint32_t *p, uint32_t v, int lane)
 }
 
 // Spin (with sleeps) until the flag at `p` reaches `want` in every lane that
-// wants one (want = 0: nothing to wait for).  Bounded: a timeout is recorded
-// in the workspace header and the kernel carries on, so it always ends.
-__device__ __forceinline__ void wait_flags(const uint32_t *p, uint32_t want, WsHeader *hdr,
-                                           int lane)
+// wants one (want = 0: nothing to wait for).  Bounded by `limit` polls: a
+// timeout is recorded in the workspace header, the caller poisons what it
+// computes from the unfinished data (NaN), and the kernel carries on, so it
+// always ends.  Returns false on a timeout.
+__device__ __forceinline__ bool wait_flags(const uint32_t *p, uint32_t want, WsHeader *hdr,
+                                           int lane, int limit)
 {
     int spins = 0;
     for (;;) {
         const uint32_t f = want ? load_flag(p) : 0u;
         if (__ballot(f < want) == 0ull)
-            return;
-        if (++spins > kSpinLimit) {  // never expected
+            return true;
+        if (++spins > limit) {  // not expected with the default limit
             if (lane == 0)
                 atomicOr(&hdr->error, kErrSpinTimeout);
-            return;
+            return false;
         }
         __builtin_amdgcn_s_sleep(1);
     }
@@ -346,6 +352,7 @@ struct ScanKArgs {
     int accumulate;       // y += result instead of y = result
     float *chunk_states;  // per 32-step chunk its start state, or NULL (see launch)
     int64_t n_cslots;     // chunk slots per group in chunk_states
+    int spin_limit;       // polls before a carry wait gives up
 };
 
 // Fused front end: the chunk's scan inputs SiLU(bias + sum_k w_k x_(t-K+1+k))
@@ -527,7 +534,8 @@ __device__ __forceinline__ void scan_segment(
     const ScanKArgs &p, uint32_t *__restrict__ flags, float *__restrict__ agg,
     uint64_t *__restrict__ incl, uint32_t epoch,
     WsHeader *hdr, int64_t seg, int64_t g, int w, int lane, float (*s_agg)[kAggFields][kWave],
-    float (*s_part)[kAggFields][kWave], float (*s_bc)[kSegT][kMaxN], float (*s_A)[kWave])
+    float (*s_part)[kAggFields][kWave], float (*s_bc)[kSegT][kMaxN], float (*s_A)[kWave],
+    volatile uint32_t *s_timeout)
 {
     float(*s_hin)[kWave] = reinterpret_cast<float(*)[kWave]>(&s_bc[0][0][0]);
     const ScanWsLayout &lay = p.lay;
@@ -781,7 +789,10 @@ __device__ __forceinline__ void scan_segment(
             // watches segment seg-1-j (the inclusive state of sI is awaited
             // later, after the fold, so that the superblock-to-superblock chain
             // only carries one map application per hop)
-            wait_flags(flags + (seg - 1 - lane) * G + g, lane < depth ? kFlagAgg : 0u, hdr, lane);
+            const bool ok = wait_flags(flags + (seg - 1 - lane) * G + g,
+                                       lane < depth ? kFlagAgg : 0u, hdr, lane, p.spin_limit);
+            if (!ok && lane == 0)
+                *s_timeout = 1u;
         }
     }
     __syncthreads();
@@ -840,13 +851,22 @@ __device__ __forceinline__ void scan_segment(
                     }
                     if (__ballot(!ok) == 0ull)
                         break;
-                    if (spins >= kSpinLimit) {  // never expected
+                    if (spins >= p.spin_limit) {  // not expected with the default limit
                         if (lane == 0)
                             atomicOr(&hdr->error, kErrSpinTimeout);
+                        if (lane == 0)
+                            *s_timeout = 1u;
                         break;
                     }
                     __builtin_amdgcn_s_sleep(1);
                 }
+            }
+            // a carry wait that gave up: this segment's start state (and so its
+            // outputs, its end state and every later segment's) is NaN
+            if (*s_timeout) {
+#pragma unroll
+                for (int n = 0; n < kMaxN; ++n)
+                    hin[n] = __builtin_nanf("");
             }
             // wave 0's own partial is still in registers; then waves 1..3
             apply_map<STRUCT>(pf, [&](int n) { return ps[n]; }, Ar, hin);
@@ -970,6 +990,7 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, kScanWavesPerSimd) scan_m
     // every wave has finished its chunk scan the B half holds the start states
     __shared__ __attribute__((aligned(16))) float s_bc[2][kSegT][kMaxN];
     __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_timeout;  // a carry wait of this workgroup gave up
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(p.ws + p.lay.off_header);
     uint32_t *flags = reinterpret_cast<uint32_t *>(p.ws + p.lay.off_flags);
@@ -977,8 +998,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, kScanWavesPerSimd) scan_m
     uint64_t *incl = reinterpret_cast<uint64_t *>(p.ws + p.lay.off_incl);
     const uint32_t epoch = __builtin_amdgcn_readfirstlane(hdr->epoch);
 
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         s_ticket = atomicAdd(&hdr->ticket, 1u);
+        s_timeout = 0u;
+    }
     __syncthreads();
     const int64_t item = (int64_t)__builtin_amdgcn_readfirstlane(s_ticket);
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -989,10 +1012,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, kScanWavesPerSimd) scan_m
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
         scan_segment<BF16, true, CONV, REV, ADJ>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
-                                       s_part, s_bc, s_A);
+                                       s_part, s_bc, s_A, &s_timeout);
     else
         scan_segment<BF16, false, CONV, REV, ADJ>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
-                                        s_part, s_bc, s_A);
+                                        s_part, s_bc, s_A, &s_timeout);
 }
 
 // Writes h_last = h0 (or zeros) for an empty sequence (L == 0).
@@ -1094,7 +1117,8 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     const int64_t n_clear16 = (n_sb - 1) * lay.groups * kInclFields * kWave * 8 / 16;
     const int64_t total = clear_base + n_clear16;
     hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       a.A, a.ws, lay, a.D, a.N, n_flags, classify_base, clear_base, n_clear16);
+                       a.A, a.ws, lay, a.D, a.N, n_flags, classify_base, clear_base, n_clear16,
+                       a.keep_error ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -1124,6 +1148,7 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     k.accumulate = a.accumulate ? 1 : 0;
     k.chunk_states = a.chunk_states;
     k.n_cslots = lay.n_seg * kWavesPerSeg;
+    k.spin_limit = a.spin_limit;
     const size_t esz = a.bf16 ? 2 : 4;
     const uintptr_t amask = (uintptr_t)a.x | (uintptr_t)a.dt | (uintptr_t)a.y |
                             (uintptr_t)(a.z ? a.z : a.x);

@@ -17,3 +17,13 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.get()
+
+
+@pytest.fixture(autouse=True, scope="session")
+def _carry_checks():
+    """Every scan and backward call of the GPU tests checks its workspace's
+    carry error word afterwards (a timed-out carry wait fails the test)."""
+    import selective_state_space_80_amd as mamba
+    mamba.set_carry_checks(True)
+    yield
+    mamba.set_carry_checks(False)

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mamba_amd.h")
 
 F32, BF16 = mamba.MAMBA_F32, mamba.MAMBA_BF16
-OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EALIAS, EWS, ELAUNCH, EDEV = range(10)
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EALIGN, EALIAS, EWS, ELAUNCH, EDEV, ETIMEOUT = range(11)
 
 
 def _gpu_visible():
@@ -46,8 +46,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 6
-    for st in range(10):
+    assert lib.mamba_abi_version() == 7
+    for st in range(11):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
     assert "unknown" in lib.mamba_status_string(99).decode()
@@ -347,3 +347,19 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mamba.load_library(str(tmp_path / "missing.so"))
     finally:
         mamba._lib = saved
+
+
+def test_scan_check_rejects_bad_workspace_before_any_hip_call(lib):
+    """mamba_selective_scan_check validates its workspace first (no stream is
+    touched for a NULL, misaligned or too small one)."""
+    buf = ctypes.create_string_buffer(1024)
+    base = ctypes.addressof(buf)
+    aligned = (base + 255) // 256 * 256
+    assert lib.mamba_selective_scan_check(None, 4096, None) == EWS
+    assert lib.mamba_selective_scan_check(ctypes.c_void_p(aligned), 255, None) == EWS
+    assert lib.mamba_selective_scan_check(ctypes.c_void_p(aligned + 16), 512, None) == EWS
+
+
+def test_spin_limit_hook_accepts_values(lib):
+    lib.mamba_set_scan_spin_limit(0)
+    lib.mamba_set_scan_spin_limit(-1)  # back to the default

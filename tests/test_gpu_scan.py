@@ -151,6 +151,53 @@ def test_scan_workspace_reuse_and_no_error_flag():
         assert_within(host(y), yo, TOL["f32"], f"reuse {B}x{D}x{L}")
 
 
+def test_carry_timeout_poisons_outputs_and_is_reported():
+    """A carry wait that gives up must not leave silently wrong outputs: with
+    the diagnostic spin limit at 0 (every wait not met at its first poll gives
+    up; each kernel still ends normally) the affected segments are NaN and the
+    workspace reports MAMBA_ERR_TIMEOUT; the next call on the same workspace
+    starts clean and matches the oracle.  The same holds for the backward,
+    whose forward-scan timeout stays reported through its adjoint scan."""
+    import torch
+    import selective_state_space_80_amd as mamba
+    from scan_check import dev
+    say("scan carry timeout path")
+    B, D, L, N = 1, 256, 128 * 64, 16  # 4 groups x 64 segments
+    p = W.make_scan_inputs(B, D, L, N, "f32", seed=77)
+    ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
+                     device="cuda")
+    args = (dev(p["x"]), dev(p["dt"]), dev(p["A"]), dev(p["Bm"]), dev(p["Cm"]))
+    kw = dict(dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]), z=dev(p["z"]), workspace=ws)
+    mamba.set_carry_checks(False)
+    try:
+        mamba.set_scan_spin_limit(0)
+        y = mamba.selective_scan_fwd(*args, **kw)
+        with pytest.raises(mamba.MambaError) as ei:
+            mamba.selective_scan_check(ws)
+        assert ei.value.status == 10  # MAMBA_ERR_TIMEOUT
+        nan = torch.isnan(y)
+        say(f"  {int(nan.sum())} of {nan.numel()} outputs poisoned")
+        assert bool(nan.any())
+        # the backward's two scans share the workspace; the first one's
+        # timeout must survive the second one's prep
+        q = W.make_scan_inputs(1, 64, 128 * 32, N, "f32", seed=78)
+        dout = dev(np.random.default_rng(3).standard_normal(q["x"].shape).astype(np.float32))
+        wsb = torch.empty(mamba.selective_scan_bwd_workspace_size(1, 64, 128 * 32, N),
+                          dtype=torch.uint8, device="cuda")
+        mamba.selective_scan_bwd(dev(q["x"]), dev(q["dt"]), dev(q["A"]), dev(q["Bm"]),
+                                 dev(q["Cm"]), dout, dev(q["dt_bias"]), dev(q["Dskip"]),
+                                 dev(q["z"]), workspace=wsb)
+        with pytest.raises(mamba.MambaError):
+            mamba.selective_scan_check(wsb)
+    finally:
+        mamba.set_scan_spin_limit(-1)
+        mamba.set_carry_checks(True)
+    y = mamba.selective_scan_fwd(*args, **kw)  # checked by the carry-check hook
+    yo, _ = oracle.selective_scan(p["x"], p["dt"], p["A"], p["Bm"], p["Cm"], p["dt_bias"],
+                                  p["Dskip"], p["z"], nthreads=8)
+    assert_within(host(y), yo, TOL["f32"], "scan after a timed-out call")
+
+
 @pytest.mark.parametrize("shift", [256, 512, 768])
 def test_scan_workspace_carved_over_an_earlier_one(shift):
     """Two workspaces carved from one buffer, the second `shift` bytes after
