@@ -56,10 +56,12 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 7
+#define MAMBA_AMD_ABI_VERSION 8
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
+/* Scratch that mamba_selective_scan_fwd_noalloc uses in place of a workspace. */
+#define MAMBA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_dtype;
 
@@ -133,6 +135,31 @@ mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float
                                       void *y, float *h_last, void *workspace,
                                       size_t workspace_bytes, int64_t B, int64_t D, int64_t L,
                                       int64_t N, mamba_dtype io, void *stream);
+
+/*
+ * mamba_selective_scan_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, the same arguments without the workspace.
+ * The library's own scratch, MAMBA_NOALLOC_SCRATCH_BYTES (64 MiB) of device
+ * memory that each GPU it runs on holds until the process ends, takes the
+ * workspace's place; the call allocates nothing (no hipMalloc, no allocating
+ * library routine).  Shapes whose workspace
+ * (mamba_selective_scan_fwd_workspace_size) exceeds the scratch return
+ * MAMBA_ERR_WORKSPACE before any HIP call: B=2 D=1536 L=8192 needs 16.5 MB and
+ * B=8 D=5120 L=2048 55 MB; B=1 D=1536 L=131072 (132 MB) does not fit.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap in
+ * time on one GPU (two streams, or two host threads) race and must not be
+ * made; calls ordered on one stream are fine (each call initialises what it
+ * reads of the scratch).  The first call on a device looks up that device's
+ * copy of the scratch (MAMBA_ERR_DEVICE if that fails).
+ */
+mamba_status mamba_selective_scan_fwd_noalloc(const void *x, const void *dt,
+                                              const float *dt_bias, const float *A,
+                                              const void *Bm, const void *Cm,
+                                              const float *Dskip, const void *z,
+                                              const float *h0, void *y, float *h_last,
+                                              int64_t B, int64_t D, int64_t L, int64_t N,
+                                              mamba_dtype io, void *stream);
 
 /*
  * Single-token decode step (the recurrent, fixed-size-state mode used at

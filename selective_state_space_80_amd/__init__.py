@@ -20,6 +20,7 @@ Entry points (same names as the C ABI, without the ``mamba_`` prefix):
   selective_scan_bwd_workspace_size(B, D, L, N, dtype)
   ssd_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
                return_last_state=False, out=None, h_last=None)
+  selective_scan_fwd_noalloc(x, dt, A, Bm, Cm, ..., out=None, h_last=None)
   selective_scan_check(workspace)        the carry's error word (after a sync)
   set_scan_spin_limit(polls)             diagnostic bound of the carry waits
 Test helper: set_carry_checks(True) checks the carry after every scan call.
@@ -31,7 +32,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmamba_amd.so")
-ABI_VERSION = 7  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
+ABI_VERSION = 8  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
 
 MAMBA_F32 = 0
 MAMBA_BF16 = 1
@@ -51,7 +52,8 @@ EXPORTED = ["mamba_status_string", "mamba_abi_version", "mamba_conv1d_silu",
             "mamba_conv1d_update", "mamba_set_scan_timing_events",
             "mamba_selective_scan_bwd_workspace_size", "mamba_selective_scan_bwd",
             "mamba_ssd_scan_fwd", "mamba_conv1d_selective_state_update",
-            "mamba_selective_scan_check", "mamba_set_scan_spin_limit"]
+            "mamba_selective_scan_check", "mamba_set_scan_spin_limit",
+            "mamba_selective_scan_fwd_noalloc"]
 
 _lib = None
 
@@ -107,6 +109,8 @@ def load_library(path: str = LIBRARY):
     lib.mamba_ssd_scan_fwd.argtypes = [P] * 11 + [I64] * 6 + [I32, P]
     lib.mamba_set_scan_timing_events.restype = None
     lib.mamba_set_scan_timing_events.argtypes = [P, P]
+    lib.mamba_selective_scan_fwd_noalloc.restype = I32
+    lib.mamba_selective_scan_fwd_noalloc.argtypes = [P] * 11 + [I64, I64, I64, I64, I32, P]
     lib.mamba_selective_scan_check.restype = I32
     lib.mamba_selective_scan_check.argtypes = [P, SZ, P]
     lib.mamba_set_scan_spin_limit.restype = None
@@ -270,6 +274,41 @@ def selective_scan_fwd(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=No
     if return_last_state:
         return out, h_last
     return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MAMBA_NOALLOC_SCRATCH_BYTES of include/mamba_amd.h
+
+
+def selective_scan_fwd_noalloc(x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, h0=None,
+                               out=None, h_last=None):
+    """mamba_selective_scan_fwd_noalloc: the scan with the library's own scratch
+    in place of a workspace (the C call allocates nothing; `out` / `h_last`
+    given by the caller keep this wrapper allocation-free too).  Shapes whose
+    workspace exceeds NOALLOC_SCRATCH_BYTES raise MAMBA_ERR_WORKSPACE.
+    Returns out, or (out, h_last) when h_last is given."""
+    torch = _torch()
+    lib = load_library()
+    B, D, L = x.shape
+    N = A.shape[1]
+    dev, io_t = x.device, x.dtype
+    _check(x, "x", (B, D, L), io_t, dev)
+    _check(dt, "dt", (B, D, L), io_t, dev)
+    _check(z, "z", (B, D, L), io_t, dev, optional=True)
+    _check(Bm, "Bm", (B, L, N), io_t, dev)
+    _check(Cm, "Cm", (B, L, N), io_t, dev)
+    _check(A, "A", (D, N), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (D,), torch.float32, dev, optional=True)
+    _check(Dskip, "Dskip", (D,), torch.float32, dev, optional=True)
+    _check(h0, "h0", (B, D, N), torch.float32, dev, optional=True)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (B, D, L), io_t, dev)
+    _check(h_last, "h_last", (B, D, N), torch.float32, dev, optional=True)
+    st = lib.mamba_selective_scan_fwd_noalloc(
+        _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+        _ptr(h0), _ptr(out), _ptr(h_last), B, D, L, N, _io_dtype(x), _stream(dev))
+    _raise(st, "mamba_selective_scan_fwd_noalloc")
+    return (out, h_last) if h_last is not None else out
 
 
 def conv1d_selective_scan_fwd(x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None, conv_state_in=None,

@@ -373,9 +373,63 @@ mamba_status step_entry(float *h, void *conv_state, const void *x, int64_t conv_
     return launched(mamba::launch_state_update(a, (hipStream_t)stream));
 }
 
+// ---- scratch of the entry point that allocates nothing ----------------------
+// The workspace of mamba_selective_scan_fwd_noalloc: a file-scope device array
+// that every GPU the library runs on holds until the process ends.  In host
+// code its name is only a stand-in, not a device address: the address of each
+// device's copy comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MAMBA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// This device's copy of `scratch` (NULL if its address cannot be had).
+void *scratch_of_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+mamba_status mamba_selective_scan_fwd_noalloc(const void *x, const void *dt,
+                                              const float *dt_bias, const float *A,
+                                              const void *Bm, const void *Cm,
+                                              const float *Dskip, const void *z,
+                                              const float *h0, void *y, float *h_last,
+                                              int64_t B, int64_t D, int64_t L, int64_t N,
+                                              mamba_dtype io, void *stream)
+{
+    // the shape's workspace must fit the scratch (0 = nothing to scan)
+    if (sizes_ok(B, D, L) && N >= 1 && N <= kMaxN && B * D * L > 0 &&
+        mamba::scan_ws_layout(B, D, L).total > (size_t)MAMBA_NOALLOC_SCRATCH_BYTES)
+        return MAMBA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (sizes_ok(B, D, L) && B * D * L > 0) {
+        const mamba_status st = device_ok();
+        if (st != MAMBA_OK)
+            return st;
+        ws = scratch_of_current_device();
+        if (!ws)
+            return MAMBA_ERR_DEVICE;
+    }
+    return scan_entry(x, 0, nullptr, nullptr, nullptr, nullptr, dt, dt_bias, A, Bm, Cm, Dskip,
+                      z, h0, y, h_last, ws, ws ? (size_t)MAMBA_NOALLOC_SCRATCH_BYTES : 0, B, D,
+                      L, N, io, 0u, stream);
+}
 
 mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float *dt_bias,
                                       const float *A, const void *Bm, const void *Cm,

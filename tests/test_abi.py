@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 7
+    assert lib.mamba_abi_version() == 8
     for st in range(11):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -363,3 +363,19 @@ def test_scan_check_rejects_bad_workspace_before_any_hip_call(lib):
 def test_spin_limit_hook_accepts_values(lib):
     lib.mamba_set_scan_spin_limit(0)
     lib.mamba_set_scan_spin_limit(-1)  # back to the default
+
+
+def test_noalloc_scan_rejects_shapes_beyond_its_scratch(lib):
+    """The entry point that allocates nothing refuses, before any HIP call, a
+    shape whose workspace is larger than its 64 MiB scratch."""
+    f = lib.mamba_selective_scan_fwd_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_void_p]
+    fake = ctypes.c_void_p(4096)
+    need = lib.mamba_selective_scan_fwd_workspace_size(1, 1536, 131072, 16, BF16)
+    assert need > mamba.NOALLOC_SCRATCH_BYTES
+    args = [fake, fake, None, fake, fake, fake, None, None, None, ctypes.c_void_p(1 << 40),
+            None, 1, 1536, 131072, 16, BF16, None]
+    assert f(*args) == EWS
+    fits = lib.mamba_selective_scan_fwd_workspace_size(8, 5120, 2048, 16, BF16)
+    assert fits <= mamba.NOALLOC_SCRATCH_BYTES
