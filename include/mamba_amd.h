@@ -146,7 +146,7 @@ mamba_status mamba_selective_scan_fwd(const void *x, const void *dt, const float
  * library routine).  Shapes whose workspace
  * (mamba_selective_scan_fwd_workspace_size) exceeds the scratch return
  * MAMBA_ERR_WORKSPACE before any HIP call: B=2 D=1536 L=8192 needs 16.5 MB and
- * B=8 D=5120 L=2048 55 MB; B=1 D=1536 L=131072 (132 MB) does not fit.
+ * B=8 D=5120 L=2048 45 MB; B=1 D=1536 L=131072 (132 MB) does not fit.
  * Every call on one GPU shares that GPU's scratch, so calls that overlap in
  * time on one GPU (two streams, or two host threads) race and must not be
  * made; calls ordered on one stream are fine (each call initialises what it

@@ -26,6 +26,7 @@ struct ScanWsLayout {
     int64_t groups = 0;    // B * n_dtiles
     int64_t n_seg = 0;     // ceil(L / kSegT)
     int64_t n_items = 0;   // groups * n_seg
+    int64_t superseg = 0;  // segments per superblock of the carry (1: a chain)
     size_t off_header = 0, off_flags = 0, off_tiles = 0, off_agg = 0, off_incl = 0, total = 0;
 };
 ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L);

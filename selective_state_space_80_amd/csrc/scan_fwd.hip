@@ -65,9 +65,13 @@ static_assert(offsetof(WsHeader, error) == kScanErrorWordOffset, "error word of 
 
 constexpr uint32_t kFlagAgg = 1u;
 constexpr uint32_t kErrSpinTimeout = 1u;
-// segments per superblock of the carry (16 or 32 measured 1-8% slower on the
-// three forward workloads, 4 or 6 within 1%)
+// Segments per superblock of the carry when a problem has few 64-channel
+// groups (16 or 32 measured 1-8% slower on the three forward workloads, 4 or 6
+// within 1%).  With at least kChainGroups groups, consecutive segments of a
+// group are about one round of resident workgroups apart, so each segment
+// reads only its predecessor's end state (a chain, superblocks of one).
 constexpr int64_t kSuperSeg = 8;
+constexpr int64_t kChainGroups = 384;
 // waves per SIMD the register budget is held to (158-167 VGPRs)
 constexpr int kScanWavesPerSimd = 3;
 
@@ -747,7 +751,9 @@ __device__ __forceinline__ void scan_segment(
     // Fixed association order, independent of scheduling: a segment folds the
     // aggregates of the earlier segments of its superblock, in order, onto the
     // inclusive state that ends the previous superblock (-1 = h0).
-    const int64_t sI = (seg / kSuperSeg) * kSuperSeg - 1;
+    const int64_t SB = lay.superseg;
+    const bool chain = SB == 1;  // each segment takes its predecessor's end state
+    const int64_t sI = (seg / SB) * SB - 1;
     const int64_t depth = seg - 1 - sI;
     // Step-4 partials of waves 1..3: waves 1, 2 in s_part[1], s_part[2]; the
     // last wave's in s_agg's last slot, which nothing reads after step 3 (the
@@ -773,7 +779,7 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
             s_part[0][1 + n][lane] = Sg[n];
-        if (seg + 1 < lay.n_seg) {
+        if (seg + 1 < lay.n_seg && !chain) {
             // successors in this superblock fold this segment's aggregate
             float *rec = agg + item * (kAggFields * kWave);
             store_rec(rec + lane, F);
@@ -837,10 +843,20 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
                 for (int n = 0; n < kMaxN; ++n)
                     hin[n] = (p.h0 && n < p.N) ? p.h0[(b * p.D + dc) * p.N + n] : 0.f;
+            } else if (chain) {
+                // the previous segment's end state: its flag, then its record
+                const bool ok = wait_flags(flags + sI * G + g, lane == 0 ? kFlagAgg : 0u, hdr,
+                                           lane, p.spin_limit);
+                if (!ok && lane == 0)
+                    *s_timeout = 1u;
+                const float *rec = agg + (sI * G + g) * (kAggFields * kWave) + lane;
+#pragma unroll
+                for (int n = 0; n < kMaxN; ++n)
+                    hin[n] = load_rec(rec + (1 + n) * kWave);
             } else {
                 // the previous superblock's end state: poll its tagged record
                 const uint64_t *rec =
-                    incl + ((sI / kSuperSeg) * G + g) * (kInclFields * kWave) + lane;
+                    incl + ((sI / SB) * G + g) * (kInclFields * kWave) + lane;
                 for (int spins = 0;; ++spins) {
                     bool ok = true;
 #pragma unroll
@@ -879,15 +895,22 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
             for (int n = 0; n < kMaxN; ++n)
                 s_hin[n][lane] = hin[n];
-            const bool publish = seg + 1 < lay.n_seg && (seg + 1) % kSuperSeg == 0;
+            const bool publish = seg + 1 < lay.n_seg && (seg + 1) % SB == 0;
             const bool last = seg + 1 == lay.n_seg;
             if (publish || (last && p.h_last)) {
                 // state at the end of the segment
                 apply_map<STRUCT>(s_part[0][0][lane],
                                   [&](int n) { return s_part[0][1 + n][lane]; }, Ar, hin);
-                if (publish) {
+                if (publish && chain) {
+                    // in the segment's own record slot, then its flag
+                    float *rec = agg + item * (kAggFields * kWave) + lane;
+#pragma unroll
+                    for (int n = 0; n < kMaxN; ++n)
+                        store_rec(rec + (1 + n) * kWave, hin[n]);
+                    publish_flag(flags + item, kFlagAgg, lane);
+                } else if (publish) {
                     uint64_t *rec =
-                        incl + ((seg / kSuperSeg) * G + g) * (kInclFields * kWave) + lane;
+                        incl + ((seg / SB) * G + g) * (kInclFields * kWave) + lane;
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n)
                         store_tagged(rec + n * kWave, hin[n], epoch);
@@ -1068,10 +1091,12 @@ ScanWsLayout scan_ws_layout(int64_t B, int64_t D, int64_t L)
     off = round_up(off + (size_t)l.n_dtiles * 4, 256);
     l.off_agg = off;
     off = round_up(off + (size_t)l.n_items * kAggFields * kWave * 4, 256);
-    l.off_incl = off;  // one tagged record per superblock and group
-    off = round_up(off + (size_t)(((l.n_seg + kSuperSeg - 1) / kSuperSeg) * l.groups) *
-                             kInclFields * kWave * 8,
-                   256);
+    l.superseg = l.groups >= kChainGroups ? 1 : kSuperSeg;
+    l.off_incl = off;  // superblocks: one tagged record per superblock and group
+    if (l.superseg > 1)
+        off = round_up(off + (size_t)(((l.n_seg + l.superseg - 1) / l.superseg) * l.groups) *
+                                 kInclFields * kWave * 8,
+                       256);
     l.total = off;
     return l;
 }
@@ -1113,8 +1138,9 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     const int64_t n_flags = lay.n_items;
     const int64_t classify_base = (n_flags + kWave - 1) / kWave * kWave;
     const int64_t clear_base = classify_base + lay.n_dtiles * kWave;
-    const int64_t n_sb = (lay.n_seg + kSuperSeg - 1) / kSuperSeg;
-    const int64_t n_clear16 = (n_sb - 1) * lay.groups * kInclFields * kWave * 8 / 16;
+    const int64_t n_sb = (lay.n_seg + lay.superseg - 1) / lay.superseg;
+    const int64_t n_clear16 =
+        lay.superseg > 1 ? (n_sb - 1) * lay.groups * kInclFields * kWave * 8 / 16 : 0;
     const int64_t total = clear_base + n_clear16;
     hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        a.A, a.ws, lay, a.D, a.N, n_flags, classify_base, clear_base, n_clear16,

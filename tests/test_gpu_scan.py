@@ -29,6 +29,9 @@ SHAPES = [
     (2, 64, 33, 16, "bf16"),
     (1, 64, 4097, 16, "bf16"),
     (2, 192, 2000, 16, "bf16"),
+    # 384 or more 64-channel groups: the carry runs as a chain of segments
+    (8, 3072, 300, 16, "bf16"),
+    (8, 3100, 257, 16, "f32"),
 ]
 
 
@@ -151,7 +154,9 @@ def test_scan_workspace_reuse_and_no_error_flag():
         assert_within(host(y), yo, TOL["f32"], f"reuse {B}x{D}x{L}")
 
 
-def test_carry_timeout_poisons_outputs_and_is_reported():
+@pytest.mark.parametrize("shape", [(1, 256, 128 * 64), (8, 3072, 128 * 4)],
+                         ids=["superblocks", "chain"])
+def test_carry_timeout_poisons_outputs_and_is_reported(shape):
     """A carry wait that gives up must not leave silently wrong outputs: with
     the diagnostic spin limit at 0 (every wait not met at its first poll gives
     up; each kernel still ends normally) the affected segments are NaN and the
@@ -161,8 +166,9 @@ def test_carry_timeout_poisons_outputs_and_is_reported():
     import torch
     import selective_state_space_80_amd as mamba
     from scan_check import dev
-    say("scan carry timeout path")
-    B, D, L, N = 1, 256, 128 * 64, 16  # 4 groups x 64 segments
+    B, D, L = shape  # 4 groups x 64 segments, or 384 groups x 4 segments
+    N = 16
+    say(f"scan carry timeout path B={B} D={D} L={L}")
     p = W.make_scan_inputs(B, D, L, N, "f32", seed=77)
     ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
                      device="cuda")
