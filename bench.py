@@ -732,7 +732,8 @@ def run_bwd(args, torch, mamba, W):
             "roofline": {"bound": "alu", "achieved": round(30 * elems * N / (k_ms * 1e-3) / 1e12, 2),
                          "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(30 * elems * N / (k_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "scan_bwd_chunk_kernel<fp32>",
+                         "traffic": traffic_bytes(traffic_record(f"scan_bwd_b{B}_d{D}_l{L}_n{N}_f32")),
+                         "kernel": "scan_bwd_chunk_kernel<fp32>",
                          "kernel_ms": round(k_ms, 4), "algorithmic_flops": 30 * elems * N},
             "kernels": {"chunk_grad_ms": quantiles(k_all),
                         "chunk_grad_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)},
@@ -794,7 +795,8 @@ def run_ssd(args, torch, mamba, W):
                        "head_dim": wl.P, "groups": wl.G, "d_state": wl.N,
                        "step": "ssd_scan_fwd (chunked Mamba-2 form, bf16 MFMA)"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_bytes(traffic_record(wl.name)),
                          "kernel": f"ssd_fwd_kernel<N={wl.N}, Q={Q}>", "kernel_ms": round(k_ms, 4),
                          "algorithmic_bytes": nbytes},
             "mfma": {"achieved_tflops": round(flops / (k_ms * 1e-3) / 1e12, 2),

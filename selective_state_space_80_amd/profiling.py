@@ -6,6 +6,8 @@
         --copy-bytes N --kernel KERNEL --source SRC [--sq SQ.db] [--variant WORKLOAD] \
         --out profiles/traffic.json
 
+(``traffic`` also takes the text that ``counters`` prints in place of each database.)
+
 ``trace`` prints per-kernel call counts and average durations in microseconds (from
 ``rocprofv3 --kernel-trace --stats``); ``counters`` prints per-kernel averages of
 every counter collected with ``--pmc`` (summed over the per-XCD/SE rows of a
@@ -45,8 +47,32 @@ def kernel_trace(db: str):
     return [(short_name(n), int(c), float(t), float(a), float(p)) for n, c, t, a, p in rows]
 
 
+def counters_text(path: str):
+    """The same dictionary, read back from the text that ``counters`` prints
+    (several passes may follow each other in one file: a kernel's counters are
+    merged; lines starting with '#' are comments)."""
+    out, cur = {}, None
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        if line.startswith(" "):
+            parts = line.split()
+            if len(parts) == 2 and cur is not None:
+                try:
+                    out[cur][parts[0]] = float(parts[1].replace(",", ""))
+                except ValueError:
+                    pass
+        elif not line.startswith(("traffic", "{", "}")):
+            cur = line.strip()
+            out.setdefault(cur, {})
+    return out
+
+
 def counters(db: str):
-    """{kernel: {counter: mean over dispatches of the per-dispatch total}}"""
+    """{kernel: {counter: mean over dispatches of the per-dispatch total}}
+    from a rocprofv3 database, or from a ``counters`` text summary (.txt)."""
+    if db.endswith(".txt"):
+        return counters_text(db)
     con = sqlite3.connect(db)
     rows = con.execute("select dispatch_id, kernel_name, counter_name, value "
                        "from counters_collection").fetchall()
