@@ -309,3 +309,20 @@ def test_fused_decode_step_many_rows():
     assert_within(host(y), yo, TOL["bf16"], "fused decode y")
     assert_within(host(h), ho, STATE_TOL, "fused decode h")
     assert np.array_equal(host(cs), cs_or), "conv window"
+
+
+@pytest.mark.parametrize("shape", [(8, 3072, 300, 16), (1, 6080, 8320, 16)],
+                         ids=["chain", "superblocks"])
+def test_fused_f32_carry_modes_every_element(shape):
+    """fp32 fused front end with 384 groups (the chain carry) and with 95
+    groups x 65 segments (superblocks, a ragged last tile): every element
+    against the oracle."""
+    B, D, L, N = shape
+    K = 4
+    say(f"fused fp32 shape={shape}: drawing inputs")
+    p = make_inputs(B, D, L, N, K, "f32", seed=L + D, with_state=True, with_bias=True)
+    y, hl, cs = run_fused(p, "f32")
+    say("  oracle conv and scan over every channel")
+    xc, cs_want = oracle_conv_front(p["x_raw"], p["conv_w"], p["conv_b"], p["conv_state"])
+    check_scan_full(y, hl, p, "f32", x=xc, label="fused fp32")
+    assert np.array_equal(host(cs), cs_want), "conv state out is not the last K-1 raw inputs"

@@ -154,9 +154,9 @@ def test_scan_workspace_reuse_and_no_error_flag():
         assert_within(host(y), yo, TOL["f32"], f"reuse {B}x{D}x{L}")
 
 
-@pytest.mark.parametrize("shape", [(1, 256, 128 * 64), (8, 3072, 128 * 4)],
+@pytest.mark.parametrize("shape,io", [((1, 256, 128 * 64), "bf16"), ((8, 3072, 128 * 4), "f32")],
                          ids=["superblocks", "chain"])
-def test_carry_timeout_poisons_outputs_and_is_reported(shape):
+def test_carry_timeout_poisons_outputs_and_is_reported(shape, io):
     """A carry wait that gives up must not leave silently wrong outputs: with
     the diagnostic spin limit at 0 (every wait not met at its first poll gives
     up; each kernel still ends normally) the affected segments are NaN and the
@@ -166,14 +166,16 @@ def test_carry_timeout_poisons_outputs_and_is_reported(shape):
     import torch
     import selective_state_space_80_amd as mamba
     from scan_check import dev
-    B, D, L = shape  # 4 groups x 64 segments, or 384 groups x 4 segments
+    # 4 groups x 64 segments (superblocks), or 384 groups x 4 segments (a chain)
+    B, D, L = shape
     N = 16
-    say(f"scan carry timeout path B={B} D={D} L={L}")
-    p = W.make_scan_inputs(B, D, L, N, "f32", seed=77)
-    ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N), dtype=torch.uint8,
-                     device="cuda")
-    args = (dev(p["x"]), dev(p["dt"]), dev(p["A"]), dev(p["Bm"]), dev(p["Cm"]))
-    kw = dict(dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]), z=dev(p["z"]), workspace=ws)
+    say(f"scan carry timeout path B={B} D={D} L={L} io={io}")
+    p = W.make_scan_inputs(B, D, L, N, io, seed=77)
+    wdt = torch.bfloat16 if io == "bf16" else None
+    ws = torch.empty(mamba.selective_scan_fwd_workspace_size(B, D, L, N, wdt),
+                     dtype=torch.uint8, device="cuda")
+    args = (dev(p["x"], io), dev(p["dt"], io), dev(p["A"]), dev(p["Bm"], io), dev(p["Cm"], io))
+    kw = dict(dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]), z=dev(p["z"], io), workspace=ws)
     mamba.set_carry_checks(False)
     try:
         mamba.set_scan_spin_limit(0)
@@ -201,7 +203,7 @@ def test_carry_timeout_poisons_outputs_and_is_reported(shape):
     y = mamba.selective_scan_fwd(*args, **kw)  # checked by the carry-check hook
     yo, _ = oracle.selective_scan(p["x"], p["dt"], p["A"], p["Bm"], p["Cm"], p["dt_bias"],
                                   p["Dskip"], p["z"], nthreads=8)
-    assert_within(host(y), yo, TOL["f32"], "scan after a timed-out call")
+    assert_within(host(y), yo, TOL[io], "scan after a timed-out call")
 
 
 @pytest.mark.parametrize("shift", [256, 512, 768])
@@ -216,20 +218,20 @@ def test_scan_workspace_carved_over_an_earlier_one(shift):
     from scan_check import dev
     say(f"scan carved workspace shift={shift}")
     B, D, L, N = 1, 64, 3072, 16  # 24 segments: three superblocks, two polled records
-    need = mamba.selective_scan_fwd_workspace_size(B, D, L, N)
+    need = mamba.selective_scan_fwd_workspace_size(B, D, L, N, torch.bfloat16)
     buf = torch.zeros(need + shift, dtype=torch.uint8, device="cuda")
     outs = []
     for k, off in enumerate((0, shift)):
-        p = W.make_scan_inputs(B, D, L, N, "f32", seed=900 + k)
-        y = mamba.selective_scan_fwd(dev(p["x"]), dev(p["dt"]), dev(p["A"]), dev(p["Bm"]),
-                                     dev(p["Cm"]), dt_bias=dev(p["dt_bias"]),
-                                     Dskip=dev(p["Dskip"]), z=dev(p["z"]),
-                                     workspace=buf[off:off + need])
+        p = W.make_scan_inputs(B, D, L, N, "bf16", seed=900 + k)
+        y = mamba.selective_scan_fwd(dev(p["x"], "bf16"), dev(p["dt"], "bf16"), dev(p["A"]),
+                                     dev(p["Bm"], "bf16"), dev(p["Cm"], "bf16"),
+                                     dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]),
+                                     z=dev(p["z"], "bf16"), workspace=buf[off:off + need])
         outs.append((y, p))
     for k, (y, p) in enumerate(outs):
         yo, _ = oracle.selective_scan(p["x"], p["dt"], p["A"], p["Bm"], p["Cm"], p["dt_bias"],
                                       p["Dskip"], p["z"], nthreads=8)
-        assert_within(host(y), yo, TOL["f32"], f"call {k} of the carved workspaces")
+        assert_within(host(y), yo, TOL["bf16"], f"call {k} of the carved workspaces")
 
 
 @pytest.mark.parametrize("idx", [2, 3])
@@ -247,3 +249,15 @@ def test_scan_full_size_workload_every_element(idx):
     assert bool(torch.isfinite(y.float()).all())
     say("  oracle over every channel")
     check_scan_full(y, hl, p, wl.io, label=wl.name)
+
+
+def test_scan_f32_superblocks_many_groups_every_element():
+    """An fp32 forward scan with 95 groups x 65 segments (a ragged last tile,
+    superblock carry), every element against the oracle."""
+    B, D, L, N = 1, 6080, 8320, 16
+    say(f"fp32 superblocks B={B} D={D} L={L}: drawing inputs")
+    p = W.make_scan_inputs(B, D, L, N, "f32", seed=4242)
+    say("  running GPU")
+    y, hl = run_scan_gpu(p, "f32")
+    say("  oracle over every channel")
+    check_scan_full(y, hl, p, "f32", label="fp32 superblocks, 95 groups")
