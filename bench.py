@@ -400,10 +400,12 @@ def measure_scan(torch, mamba, W, idx, steps, warmup, settle_s, cpu_s, no_cpu=Fa
 
 def measure_decode(torch, mamba, W, steps, warmup, settle_s, n_sets, with_conv=False,
                    unfused=False):
-    """Decode steps of the [256, 5120, 16] workload, warm and cold.  Warm: one
-    state buffer (84 MB, resident in the 256 MB MALL between steps).  Cold:
-    n_sets state buffers (and conv windows) used in turn, more bytes than the
-    MALL holds, so every step reads its state from HBM."""
+    """Decode steps of the [256, 5120, 16] workload, warm and cold, each with the
+    state loaded and stored plainly and with the streaming hint
+    (MAMBA_STEP_STREAM_STATE).  Warm: one state buffer (84 MB, resident in the
+    256 MB MALL between steps).  Cold: n_sets state buffers (and conv windows)
+    used in turn, more bytes than the MALL holds, so every step reads its state
+    from HBM, as a model whose layers each step their own state does."""
     wl = W.WORKLOADS[4]
     dev = torch.device("cuda:0")
     init = W.decode_initial(wl)
@@ -423,18 +425,19 @@ def measure_decode(torch, mamba, W, steps, warmup, settle_s, n_sets, with_conv=F
         cstates = [T(ci["conv_state"], torch.bfloat16) for _ in range(n_sets)]
         xc = torch.empty((wl.B, wl.D), dtype=torch.bfloat16, device=dev)
 
-    def step(i, k):
+    def step(i, k, stream=False):
         t = toks[i % len(toks)]
         x, h = t["x"], hs[k]
         if with_conv and not unfused:  # conv front end and state update in one kernel
             mamba.conv1d_selective_state_update(h, cstates[k], x, cw, t["dt"], A, t["Bm"],
                                                 t["Cm"], dt_bias=bias, Dskip=Dk, z=t["z"],
-                                                out=y)
+                                                out=y, stream_state=stream)
             return
         if with_conv:
             mamba.conv1d_update(cstates[k], x, cw, None, out=xc)
             x = xc
-        mamba.selective_state_update(h, x, t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"], out=y)
+        mamba.selective_state_update(h, x, t["dt"], A, t["Bm"], t["Cm"], bias, Dk, t["z"], out=y,
+                                     stream_state=stream)
 
     nbytes = wl.B * wl.D * (2 * wl.N * 4 + 4 * 2) + wl.B * 2 * wl.N * 2 + wl.D * (wl.N + 2) * 4
     if with_conv:  # window read and written (the state update above counts the raw input's
@@ -442,21 +445,23 @@ def measure_decode(torch, mamba, W, steps, warmup, settle_s, n_sets, with_conv=F
         nbytes += wl.B * wl.D * 2 * (K - 1) * 2 + wl.D * K * 4
     settle = settle_clocks(lambda: step(0, 0), torch, settle_s)
     res = {}
-    for mode, sets in (("warm", 1), ("cold", n_sets)):
+    for mode, sets, stream in (("warm", 1, False), ("cold", n_sets, False),
+                               ("warm_stream", 1, True), ("cold_stream", n_sets, True)):
         for i in range(warmup):
-            step(i, i % sets)
+            step(i, i % sets, stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
-            step(i, i % sets)
+            step(i, i % sets, stream)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
         gbs = nbytes / (ms * 1e-3) / 1e9
         res[mode] = {"ms_per_step": round(ms, 5), "GBps": round(gbs, 1),
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "state_sets": sets, "state_set_bytes": hs[0].numel() * 4}
+                     "state_sets": sets, "state_set_bytes": hs[0].numel() * 4,
+                     "stream_state": stream}
     res["clock_settle"] = settle
     res["algorithmic_bytes_per_step"] = nbytes
     res["toks_np"], res["init"] = toks_np, init
@@ -591,10 +596,11 @@ def other_workloads(args, torch, mamba, W):
     d = measure_decode(torch, mamba, W, steps=200, warmup=20,
                        settle_s=min(args.settle_seconds, 0.5), n_sets=args.decode_sets)
     toks_np, init = d.pop("toks_np"), d.pop("init")
-    d["roofline"] = {"bound": "hbm", "achieved": d["cold"]["GBps"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": d["cold"]["frac"],
+    d["roofline"] = {"bound": "hbm", "achieved": d["cold_stream"]["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": d["cold_stream"]["frac"],
                      "traffic": traffic_bytes(traffic_record(wl.name)),
-                     "kernel": "state update (cold: state read from HBM every step)"}
+                     "kernel": "state update (cold: state read from HBM every step; "
+                               "streaming hint)"}
     if not args.no_cpu:
         d["cpu_baseline"] = cpu_baseline_decode(wl, init, toks_np,
                                                 d["algorithmic_bytes_per_step"], target_s=4.0)
@@ -814,7 +820,9 @@ def run_decode(args, torch, mamba, W):
                        args.decode_sets, with_conv=args.with_conv, unfused=args.unfused)
     toks_np, init = d.pop("toks_np"), d.pop("init")
     nbytes = d["algorithmic_bytes_per_step"]
-    cold = d["cold"]
+    # the serving setting: every step's state comes from HBM (a model's layers
+    # each step their own state), stepped with the streaming hint
+    cold = d["cold_stream"]
     metric = ("decode step (conv update + state update) GB/s" if args.with_conv else
               "decode state update GB/s")
     key = wl.name + ("_conv" if args.with_conv else "")
@@ -823,7 +831,7 @@ def run_decode(args, torch, mamba, W):
             "ms_per_step": cold["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16-io/f32", "data": "synthetic",
             "config": {"workload": wl.name, "batch": wl.B, "d_inner": wl.D, "d_state": wl.N,
-                       "state_sets": args.decode_sets,
+                       "state_sets": args.decode_sets, "state_hint": "stream",
                        **({"d_conv": K,
                            "step": ("conv1d_update, then selective_state_update" if args.unfused
                                     else "conv1d_selective_state_update (one kernel)")}
@@ -833,8 +841,10 @@ def run_decode(args, torch, mamba, W):
                          "traffic": traffic_bytes(traffic_record(key)),
                          "note": (f"cold: {args.decode_sets} state sets of "
                                   f"{cold['state_set_bytes'] / 1e6:.0f} MB used in turn, more "
-                                  "than the 256 MB MALL holds")},
-            "warm": d["warm"], "cold": cold, "clock_settle": d["clock_settle"],
+                                  "than the 256 MB MALL holds; h loaded and stored with "
+                                  "MAMBA_STEP_STREAM_STATE")},
+            "warm": d["warm"], "cold": d["cold"], "warm_stream": d["warm_stream"],
+            "cold_stream": cold, "clock_settle": d["clock_settle"],
             "algorithmic_bytes_per_step": nbytes,
             **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_decode(
                 wl, init, toks_np, nbytes, W.decode_conv_initial(wl, K) if args.with_conv

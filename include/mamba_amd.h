@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MAMBA_AMD_ABI_VERSION 8
+#define MAMBA_AMD_ABI_VERSION 9
 #define MAMBA_MAX_STATE 16
 #define MAMBA_MAX_CONV_TAPS 8
 #define MAMBA_MAX_FUSED_CONV_TAPS 4
@@ -170,13 +170,26 @@ mamba_status mamba_selective_scan_fwd_noalloc(const void *x, const void *dt,
  *   x, dt, z, y : [B, D] of `io`  (z NULL = no gate)
  *   Bm, Cm      : [B, N] of `io`
  *   A [D, N], dt_bias [D] or NULL, Dskip [D] or NULL : float
- * y must not overlap h or any input.
+ *   flags       : 0, or MAMBA_STEP_STREAM_STATE
+ * y must not overlap h or any input.  Unknown flags return
+ * MAMBA_ERR_UNSUPPORTED.
  */
 mamba_status mamba_selective_state_update(float *h, const void *x, const void *dt,
                                           const float *dt_bias, const float *A,
                                           const void *Bm, const void *Cm, const float *Dskip,
                                           const void *z, void *y, int64_t B, int64_t D,
-                                          int64_t N, mamba_dtype io, void *stream);
+                                          int64_t N, mamba_dtype io, unsigned flags,
+                                          void *stream);
+
+/* Flag of the decode steps (mamba_selective_state_update,
+ * mamba_conv1d_selective_state_update): a cache hint only, the results are
+ * the same bits.  The state h is loaded and stored with nontemporal hints, so
+ * it streams through the caches instead of being kept in them.  For callers
+ * whose state will not be read again before other traffic evicts it, as in a
+ * model whose layers each advance their own state once per token: there it
+ * raises the step's bandwidth; a state that stays cached from one call to the
+ * next (the same state stepped again at once) is slower with it. */
+#define MAMBA_STEP_STREAM_STATE 1u
 
 /* Flags of mamba_selective_scan_fwd_ex. */
 #define MAMBA_SCAN_REVERSE 1u    /* scan from step L-1 down to step 0 */
@@ -268,7 +281,7 @@ mamba_status mamba_conv1d_selective_state_update(
     float *h, void *conv_state, const void *x_raw, const float *conv_w, const float *conv_bias,
     int64_t K, const void *dt, const float *dt_bias, const float *A, const void *Bm,
     const void *Cm, const float *Dskip, const void *z, void *y, int64_t B, int64_t D, int64_t N,
-    mamba_dtype io, void *stream);
+    mamba_dtype io, unsigned flags, void *stream);
 
 /*
  * Backward pass of the selective scan ("Mamba状态空间模型深度解析：挑战

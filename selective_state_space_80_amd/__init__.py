@@ -32,7 +32,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmamba_amd.so")
-ABI_VERSION = 8  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
+ABI_VERSION = 9  # MAMBA_AMD_ABI_VERSION of include/mamba_amd.h that this binding follows
 
 MAMBA_F32 = 0
 MAMBA_BF16 = 1
@@ -89,7 +89,7 @@ def load_library(path: str = LIBRARY):
     lib.mamba_selective_scan_fwd.restype = I32
     lib.mamba_selective_scan_fwd.argtypes = [P] * 12 + [SZ, I64, I64, I64, I64, I32, P]
     lib.mamba_selective_state_update.restype = I32
-    lib.mamba_selective_state_update.argtypes = [P] * 10 + [I64, I64, I64, I32, P]
+    lib.mamba_selective_state_update.argtypes = [P] * 10 + [I64, I64, I64, I32, ctypes.c_uint, P]
     lib.mamba_selective_scan_fwd_ex.restype = I32
     lib.mamba_selective_scan_fwd_ex.argtypes = ([P] * 12 + [SZ, I64, I64, I64, I64, I32,
                                                              ctypes.c_uint, P])
@@ -99,8 +99,8 @@ def load_library(path: str = LIBRARY):
     lib.mamba_conv1d_update.restype = I32
     lib.mamba_conv1d_update.argtypes = [P] * 5 + [I64, I64, I64, I32, P]
     lib.mamba_conv1d_selective_state_update.restype = I32
-    lib.mamba_conv1d_selective_state_update.argtypes = [P] * 5 + [I64] + [P] * 8 + [I64, I64, I64,
-                                                                                  I32, P]
+    lib.mamba_conv1d_selective_state_update.argtypes = ([P] * 5 + [I64] + [P] * 8 +
+                                                        [I64, I64, I64, I32, ctypes.c_uint, P])
     lib.mamba_selective_scan_bwd_workspace_size.restype = SZ
     lib.mamba_selective_scan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I32]
     lib.mamba_selective_scan_bwd.restype = I32
@@ -389,9 +389,19 @@ def conv1d_update(state, x, w, bias=None, out=None):
     return out
 
 
-def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, out=None):
+STEP_STREAM_STATE = 1  # MAMBA_STEP_STREAM_STATE
+
+
+def _step_flags(stream_state):
+    return STEP_STREAM_STATE if stream_state else 0
+
+
+def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None, out=None,
+                           stream_state=False):
     """One decode step.  h [B,D,N] f32 is updated in place; x, dt, z [B,D] and
-    Bm, Cm [B,N] share one dtype (f32/bf16).  Returns y [B,D] of that dtype."""
+    Bm, Cm [B,N] share one dtype (f32/bf16).  Returns y [B,D] of that dtype.
+    stream_state: h is loaded and stored with nontemporal hints (the same
+    results), for a state that leaves the caches before its next step anyway."""
     torch = _torch()
     lib = load_library()
     B, D, N = h.shape
@@ -410,13 +420,13 @@ def selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=None, Dskip=None, z=None
     _check(out, "out", (B, D), io_t, dev)
     st = lib.mamba_selective_state_update(
         _ptr(h), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
-        _ptr(z), _ptr(out), B, D, N, _io_dtype(x), _stream(dev))
+        _ptr(z), _ptr(out), B, D, N, _io_dtype(x), _step_flags(stream_state), _stream(dev))
     _raise(st, "mamba_selective_state_update")
     return out
 
 
 def conv1d_selective_state_update(h, conv_state, x_raw, conv_w, dt, A, Bm, Cm, conv_bias=None,
-                                  dt_bias=None, Dskip=None, z=None, out=None):
+                                  dt_bias=None, Dskip=None, z=None, out=None, stream_state=False):
     """The block's decode step in one kernel: the conv front end's step on the
     raw input x_raw [B,D] (conv_state [B,D,K-1] of x_raw's dtype, updated in
     place; conv_w [D,K] f32 with K <= 4, conv_bias [D] f32), feeding the state
@@ -445,7 +455,7 @@ def conv1d_selective_state_update(h, conv_state, x_raw, conv_w, dt, A, Bm, Cm, c
     st = lib.mamba_conv1d_selective_state_update(
         _ptr(h), _ptr(conv_state), _ptr(x_raw), _ptr(conv_w), _ptr(conv_bias), K, _ptr(dt),
         _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(out), B, D, N,
-        _io_dtype(x_raw), _stream(dev))
+        _io_dtype(x_raw), _step_flags(stream_state), _stream(dev))
     _raise(st, "mamba_conv1d_selective_state_update")
     return out
 

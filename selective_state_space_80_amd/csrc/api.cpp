@@ -324,13 +324,15 @@ mamba_status step_entry(float *h, void *conv_state, const void *x, int64_t conv_
                         const float *conv_w, const float *conv_b, const void *dt,
                         const float *dt_bias, const float *A, const void *Bm, const void *Cm,
                         const float *Dskip, const void *z, void *y, int64_t B, int64_t D,
-                        int64_t N, mamba_dtype io, void *stream)
+                        int64_t N, mamba_dtype io, unsigned flags, void *stream)
 {
     if (!valid_dtype(io))
         return MAMBA_ERR_DTYPE;
     if (!sizes_ok(B, D, 1) || N < 0 || conv_K < 0)
         return MAMBA_ERR_SHAPE;
     if (N < 1 || N > kMaxN || conv_K > mamba::kFusedConvTaps)
+        return MAMBA_ERR_UNSUPPORTED;
+    if ((flags & ~(unsigned)MAMBA_STEP_STREAM_STATE) != 0)
         return MAMBA_ERR_UNSUPPORTED;
     if (B * D >= kMaxGrid)  // launch grid: up to two lanes per channel in a row's dimension
         return MAMBA_ERR_SHAPE;
@@ -370,6 +372,7 @@ mamba_status step_entry(float *h, void *conv_state, const void *x, int64_t conv_
     a.conv_state = conv_state;
     a.conv_w = conv_w;
     a.conv_b = conv_b;
+    a.stream_state = (flags & MAMBA_STEP_STREAM_STATE) != 0;
     return launched(mamba::launch_state_update(a, (hipStream_t)stream));
 }
 
@@ -511,24 +514,25 @@ mamba_status mamba_selective_state_update(float *h, const void *x, const void *d
                                           const float *dt_bias, const float *A,
                                           const void *Bm, const void *Cm, const float *Dskip,
                                           const void *z, void *y, int64_t B, int64_t D,
-                                          int64_t N, mamba_dtype io, void *stream)
+                                          int64_t N, mamba_dtype io, unsigned flags,
+                                          void *stream)
 {
     return step_entry(h, nullptr, x, 0, nullptr, nullptr, dt, dt_bias, A, Bm, Cm, Dskip, z, y, B,
-                      D, N, io, stream);
+                      D, N, io, flags, stream);
 }
 
 mamba_status mamba_conv1d_selective_state_update(
     float *h, void *conv_state, const void *x_raw, const float *conv_w, const float *conv_bias,
     int64_t K, const void *dt, const float *dt_bias, const float *A, const void *Bm,
     const void *Cm, const float *Dskip, const void *z, void *y, int64_t B, int64_t D, int64_t N,
-    mamba_dtype io, void *stream)
+    mamba_dtype io, unsigned flags, void *stream)
 {
     if (K < 0)
         return valid_dtype(io) ? MAMBA_ERR_SHAPE : MAMBA_ERR_DTYPE;
     if (K == 0)
         return valid_dtype(io) ? MAMBA_ERR_UNSUPPORTED : MAMBA_ERR_DTYPE;
     return step_entry(h, conv_state, x_raw, K, conv_w, conv_bias, dt, dt_bias, A, Bm, Cm, Dskip,
-                      z, y, B, D, N, io, stream);
+                      z, y, B, D, N, io, flags, stream);
 }
 
 size_t mamba_selective_scan_bwd_workspace_size(int64_t B, int64_t D, int64_t L, int64_t N,

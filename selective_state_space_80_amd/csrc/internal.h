@@ -151,6 +151,8 @@ struct StepArgs {
     int conv_K = 0;
     void *conv_state = nullptr;
     const float *conv_w = nullptr, *conv_b = nullptr;
+    // h loaded and stored with nontemporal hints (MAMBA_STEP_STREAM_STATE)
+    bool stream_state = false;
 };
 hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
 

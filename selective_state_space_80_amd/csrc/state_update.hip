@@ -6,7 +6,9 @@
 // ("Mamba架构与SSM模型：高效序列建模技术解析" §2), then
 // y = (sum_n C_n h_n + D x) * SiLU(z).
 // Bound by memory: the fp32 state (N*4 bytes read and written per channel)
-// dominates the traffic.  With N = 16 and aligned rows, four lanes share a
+// dominates the traffic.  NT: the state is loaded and stored with nontemporal
+// hints, for callers whose state leaves the caches between two steps anyway
+// (a model's layers each touch their own state once per token).  With N = 16 and aligned rows, four lanes share a
 // channel, one 16-byte quarter of its state each, so every load and store of
 // a wave covers one contiguous 1 KB run; the readout is summed over the four
 // lanes with two DPP quad permutes.  Other N: one lane per channel.
@@ -25,6 +27,53 @@ constexpr int kThreads = 256;
 // channel quads per lane: two, 64 quads apart, keep twice the bytes in flight
 // per lane (one measured 2-6% slower, four slower still: fewer waves fit)
 constexpr int kQuadsPerLane = 2;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Quarter i4 of the state (16 bytes), plain or nontemporal.
+template <bool NT>
+__device__ __forceinline__ void load_state4(const float *h, int64_t i4, float (&v)[4])
+{
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(h) + i4;
+    f32x4 t;
+    if constexpr (NT)
+        t = __builtin_nontemporal_load(p);
+    else
+        t = *p;
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_state4(float *h, int64_t i4, const float (&v)[4])
+{
+    const f32x4 t = {v[0], v[1], v[2], v[3]};
+    f32x4 *p = reinterpret_cast<f32x4 *>(h) + i4;
+    if constexpr (NT)
+        __builtin_nontemporal_store(t, p);
+    else
+        *p = t;
+}
+
+template <bool NT>
+__device__ __forceinline__ float load_state(const float *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_state(float *p, float v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
 
 template <bool BF16>
 __device__ __forceinline__ void load4(const void *base, int64_t i4, float (&v)[4])
@@ -92,7 +141,7 @@ struct ConvStep {
 // slot q, or the raw input for the last tap; lanes past the taps weigh 0):
 // one 2-byte and one 4-byte load per lane, the weighted taps summed over the
 // quad like the readout, and lane q in 1..KC-1 writes its tap to slot q - 1.
-template <bool BF16, int QPT, int KC>
+template <bool BF16, int QPT, int KC, bool NT>
 __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
@@ -133,7 +182,7 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
             dq[k] = rqc >> 2;
             cq[k] = b * D + dq[k];
             gq[k] = b * row_quads + rqc;
-            load4<false>(h, gq[k], hs[k]);
+            load_state4<NT>(h, gq[k], hs[k]);
             load4<false>(A, dq[k] * 4 + q, a[k]);
             xv[k] = E::load(reinterpret_cast<const T *>(x_) + cq[k]);
             dtv[k] = E::load(reinterpret_cast<const T *>(dt_) + cq[k]);
@@ -182,14 +231,13 @@ __global__ void __launch_bounds__(kThreads) state_update_quad_kernel(
                 if (q >= 1 && q < KC)
                     E::store(reinterpret_cast<T *>(conv_state) + cq[k] * (KC - 1) + (q - 1), tu[k]);
             }
-            reinterpret_cast<float4 *>(h)[gq[k]] =
-                make_float4(hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
+            store_state4<NT>(h, gq[k], hs[k]);
         }
     }
 }
 
 // Any N <= 16: one lane per channel.
-template <bool BF16, int KC>
+template <bool BF16, int KC, bool NT>
 __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float *__restrict__ h, const void *__restrict__ x_, const void *__restrict__ dt_,
     const float *__restrict__ dt_bias, const float *__restrict__ A, const void *__restrict__ Bm_,
@@ -223,8 +271,8 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
         const float an = A[d * N + n];
         const float en = hw_exp2(an * l);
         const float coef = zoh_input_coef(an, delta, en);
-        const float hn = fmaf(en, h[c * N + n], coef * (E::load(Bm + n) * xv));
-        h[c * N + n] = hn;
+        const float hn = fmaf(en, load_state<NT>(h + c * N + n), coef * (E::load(Bm + n) * xv));
+        store_state<NT>(h + c * N + n, hn);
         acc = fmaf(E::load(Cm + n), hn, acc);
     }
     float yv = acc + (Dskip ? Dskip[d] : 0.f) * xv;
@@ -233,7 +281,7 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     E::store(reinterpret_cast<T *>(y_) + c, yv);
 }
 
-template <int KC>
+template <int KC, bool NT>
 hipError_t launch_state_update_k(const StepArgs &a, hipStream_t s)
 {
     const int64_t n_ch = a.B * a.D;
@@ -247,11 +295,11 @@ hipError_t launch_state_update_k(const StepArgs &a, hipStream_t s)
             const dim3 grid((unsigned)((4 * a.D + per_block - 1) / per_block),
                             (unsigned)min(a.B - b0, (int64_t)65535));
             if (a.bf16)
-                hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT, KC>), grid, dim3(kThreads),
+                hipLaunchKernelGGL((state_update_quad_kernel<true, kQPT, KC, NT>), grid, dim3(kThreads),
                                    0, s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z,
                                    a.y, b0, a.D, a.conv_state, a.conv_w, a.conv_b);
             else
-                hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT, KC>), grid,
+                hipLaunchKernelGGL((state_update_quad_kernel<false, kQPT, KC, NT>), grid,
                                    dim3(kThreads), 0, s, a.h, a.x, a.dt, a.dt_bias, a.A, a.Bm,
                                    a.Cm, a.Dskip, a.z, a.y, b0, a.D, a.conv_state, a.conv_w,
                                    a.conv_b);
@@ -259,11 +307,11 @@ hipError_t launch_state_update_k(const StepArgs &a, hipStream_t s)
     } else {
         const dim3 grid((unsigned)((n_ch + kThreads - 1) / kThreads));
         if (a.bf16)
-            hipLaunchKernelGGL((state_update_kernel<true, KC>), grid, dim3(kThreads), 0, s, a.h,
+            hipLaunchKernelGGL((state_update_kernel<true, KC, NT>), grid, dim3(kThreads), 0, s, a.h,
                                a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
                                n_ch, a.conv_state, a.conv_w, a.conv_b);
         else
-            hipLaunchKernelGGL((state_update_kernel<false, KC>), grid, dim3(kThreads), 0, s, a.h,
+            hipLaunchKernelGGL((state_update_kernel<false, KC, NT>), grid, dim3(kThreads), 0, s, a.h,
                                a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm, a.Dskip, a.z, a.y, a.D, a.N,
                                n_ch, a.conv_state, a.conv_w, a.conv_b);
     }
@@ -276,12 +324,22 @@ hipError_t launch_state_update(const StepArgs &a, hipStream_t s)
 {
     if (a.B * a.D == 0)
         return hipSuccess;
+    if (a.stream_state) {
+        switch (a.conv_K) {
+        case 0: return launch_state_update_k<0, true>(a, s);
+        case 1: return launch_state_update_k<1, true>(a, s);
+        case 2: return launch_state_update_k<2, true>(a, s);
+        case 3: return launch_state_update_k<3, true>(a, s);
+        case 4: return launch_state_update_k<4, true>(a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.conv_K) {
-    case 0: return launch_state_update_k<0>(a, s);
-    case 1: return launch_state_update_k<1>(a, s);
-    case 2: return launch_state_update_k<2>(a, s);
-    case 3: return launch_state_update_k<3>(a, s);
-    case 4: return launch_state_update_k<4>(a, s);
+    case 0: return launch_state_update_k<0, false>(a, s);
+    case 1: return launch_state_update_k<1, false>(a, s);
+    case 2: return launch_state_update_k<2, false>(a, s);
+    case 3: return launch_state_update_k<3, false>(a, s);
+    case 4: return launch_state_update_k<4, false>(a, s);
     default: return hipErrorInvalidValue;
     }
 }

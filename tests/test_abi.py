@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert lib.mamba_abi_version() == 8
+    assert lib.mamba_abi_version() == mamba.ABI_VERSION == 9
     for st in range(11):
         s = lib.mamba_status_string(st).decode()
         assert s.startswith(mamba.STATUS_NAMES[st])
@@ -135,15 +135,18 @@ def test_conv_rejects(lib):
 def test_state_update_rejects(lib):
     f = lib.mamba_selective_state_update
     args = [P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8), P(9), P(10)]
-    assert f(*args, 4, 64, 17, F32, None) == EUNSUP
-    assert f(*args, 4, 64, 16, 5, None) == EDTYPE
+    assert f(*args, 4, 64, 17, F32, 0, None) == EUNSUP
+    assert f(*args, 4, 64, 16, 5, 0, None) == EDTYPE
+    assert f(*args, 4, 64, 16, F32, 2, None) == EUNSUP  # unknown flag
+    assert f(*args, 4, 64, 16, F32, 1 | 4, None) == EUNSUP
     bad = list(args)
     bad[9] = P(1)  # y on top of h
-    assert f(*bad, 4, 64, 16, F32, None) == EALIAS
+    assert f(*bad, 4, 64, 16, F32, 0, None) == EALIAS
     bad = list(args)
     bad[0] = None
-    assert f(*bad, 4, 64, 16, F32, None) == ENULL
-    assert f(*args, 0, 64, 16, F32, None) == OK
+    assert f(*bad, 4, 64, 16, F32, 1, None) == ENULL
+    assert f(*args, 0, 64, 16, F32, 0, None) == OK
+    assert f(*args, 0, 64, 16, F32, mamba.STEP_STREAM_STATE, None) == OK
 
 
 def fused(lib, **kw):
@@ -178,11 +181,11 @@ def test_fused_scan_empty_is_ok(lib):
 
 def fused_step(lib, **kw):
     a = dict(h=P(1), cs=P(11), x=P(2), w=P(12), cb=P(13), K=4, dt=P(3), dt_bias=P(4), A=P(5),
-             Bm=P(6), Cm=P(7), Dskip=P(8), z=P(9), y=P(10), B=4, D=64, N=16, io=F32)
+             Bm=P(6), Cm=P(7), Dskip=P(8), z=P(9), y=P(10), B=4, D=64, N=16, io=F32, flags=0)
     a.update(kw)
     return lib.mamba_conv1d_selective_state_update(
         a["h"], a["cs"], a["x"], a["w"], a["cb"], a["K"], a["dt"], a["dt_bias"], a["A"], a["Bm"],
-        a["Cm"], a["Dskip"], a["z"], a["y"], a["B"], a["D"], a["N"], a["io"], None)
+        a["Cm"], a["Dskip"], a["z"], a["y"], a["B"], a["D"], a["N"], a["io"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -193,6 +196,7 @@ def fused_step(lib, **kw):
     (dict(io=BF16, cs=ctypes.c_void_p(0xB0000000001)), EALIGN),
     (dict(cs=P(2)), EALIAS), (dict(cs=P(1)), EALIAS), (dict(cs=P(10)), EALIAS),
     (dict(cs=P(12)), EALIAS), (dict(y=P(13)), EALIAS), (dict(h=P(12)), EALIAS),
+    (dict(flags=2), EUNSUP), (dict(flags=0x80000001), EUNSUP),
 ])
 def test_fused_step_rejects(lib, kw, want):
     assert fused_step(lib, **kw) == want
@@ -307,7 +311,7 @@ def test_launch_grid_limits(lib):
     assert lib.mamba_conv1d_silu(P(1), P(2), None, P(3), 1, 1 << 20, 1 << 13, 4, F32,
                                  None) == ESHAPE
     assert lib.mamba_selective_state_update(*[P(k) for k in range(1, 11)], big["B"], big["D"],
-                                            16, F32, None) == ESHAPE
+                                            16, F32, 0, None) == ESHAPE
     assert fused_step(lib, **big) == ESHAPE
     assert lib.mamba_conv1d_update(P(1), P(2), P(3), None, P(4), big["B"], big["D"], 4, F32,
                                    None) == ESHAPE
@@ -331,10 +335,13 @@ def test_valid_arguments_without_gpu_report_device(lib):
     assert scan(lib) == EDEV
     assert lib.mamba_conv1d_silu(P(1), P(2), None, P(3), 2, 8, 32, 4, F32, None) == EDEV
     assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
-                                            P(9), P(10), 4, 64, 16, F32, None) == EDEV
+                                            P(9), P(10), 4, 64, 16, F32, 0, None) == EDEV
+    assert lib.mamba_selective_state_update(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8),
+                                            P(9), P(10), 4, 64, 16, F32, 1, None) == EDEV
     assert bwd(lib) == EDEV
     assert fused_step(lib) == EDEV
     assert fused_step(lib, K=1, cs=None) == EDEV  # one tap: no window to carry
+    assert fused_step(lib, flags=1) == EDEV
     assert ssd(lib) == EDEV
     assert ssd(lib, L=0, x=None, y=None, dt=None, Bm=None, Cm=None) == EDEV  # h_last = h0
 

@@ -86,9 +86,10 @@ def test_block_workload_every_element():
 @pytest.mark.parametrize("N", [16, 5])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("A_kind", ["structured", "general"])
-def test_state_update_matches_oracle(N, io, A_kind):
+@pytest.mark.parametrize("stream", [False, True], ids=["plain", "stream_state"])
+def test_state_update_matches_oracle(N, io, A_kind, stream):
     import selective_state_space_80_amd as mamba
-    say(f"decode step N={N} io={io} A={A_kind}")
+    say(f"decode step N={N} io={io} A={A_kind} stream_state={stream}")
     rng = np.random.default_rng(N + len(io))
     B, D = 3, 300
     wl = W.DecodeWorkload("t", B, D, N, io, 3, 1, 77)
@@ -104,7 +105,7 @@ def test_state_update_matches_oracle(N, io, A_kind):
         y = mamba.selective_state_update(h, dev(s["x"], io), dev(s["dt"], io), dev(init["A"]),
                                          dev(s["Bm"], io), dev(s["Cm"], io),
                                          dt_bias=dev(init["dt_bias"]), Dskip=dev(init["Dskip"]),
-                                         z=dev(s["z"], io))
+                                         z=dev(s["z"], io), stream_state=stream)
         yo, h_or = oracle.state_update(h_or, s["x"], s["dt"], init["A"], s["Bm"], s["Cm"],
                                        dt_bias=init["dt_bias"], Dskip=init["Dskip"], z=s["z"])
         assert_within(host(y), yo, TOL[io], f"decode y step {step}")
@@ -195,3 +196,41 @@ def test_decode_workload_1024_steps():
                     f"{h.numel()} states); max rel err y {e1:.2e} h {e2:.2e}")
     say(f"  decode: max rel err y {worst_y:.3e} (tol {TOL['bf16']}) h {worst_h:.3e} "
         f"(tol {STATE_TOL})")
+
+
+@pytest.mark.parametrize("conv", [False, True], ids=["state_update", "with_conv"])
+def test_stream_state_hint_gives_the_same_bits(conv):
+    """MAMBA_STEP_STREAM_STATE is a cache hint: on the full decode workload
+    (B=256, D=5120, N=16, bf16 tokens) two steps with it leave the same bits in
+    y, h (and the conv window) as two steps without it."""
+    import selective_state_space_80_amd as mamba
+    wl = W.WORKLOADS[4]
+    say(f"stream_state hint, {wl.name}, conv={conv}")
+    init = W.decode_initial(wl)
+    K = 4
+    ci = W.decode_conv_initial(wl, K) if conv else None
+    A, bias, Dk = dev(init["A"]), dev(init["dt_bias"]), dev(init["Dskip"])
+    outs = {}
+    for stream in (False, True):
+        h = dev(init["h0"])
+        cs = dev(ci["conv_state"], "bf16") if conv else None
+        ys = []
+        for t in range(2):
+            s = W.decode_step_inputs(wl, t)
+            x, dt, Bm, Cm, z = (dev(s[k], "bf16") for k in ("x", "dt", "Bm", "Cm", "z"))
+            if conv:
+                y = mamba.conv1d_selective_state_update(h, cs, x, dev(ci["conv_w"]), dt, A, Bm,
+                                                        Cm, dt_bias=bias, Dskip=Dk, z=z,
+                                                        stream_state=stream)
+            else:
+                y = mamba.selective_state_update(h, x, dt, A, Bm, Cm, dt_bias=bias, Dskip=Dk,
+                                                 z=z, stream_state=stream)
+            ys.append(host(y))
+        outs[stream] = (ys, host(h), host(cs) if conv else None)
+    (y0, h0, c0), (y1, h1, c1) = outs[False], outs[True]
+    for t in range(2):
+        assert np.array_equal(y0[t], y1[t]), f"y step {t}"
+    assert np.array_equal(h0, h1), "h"
+    if conv:
+        assert np.array_equal(c0, c1), "conv window"
+    say("  y, h" + (", window" if conv else "") + " bit-identical with and without the hint")

@@ -235,11 +235,22 @@ def test_block_workload_fused_every_element():
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_fused_decode_step_matches_oracle(N, K, io):
+    _fused_decode_vs_oracle(N, K, io, stream=False)
+
+
+@pytest.mark.parametrize("N", [16, 5])
+@pytest.mark.parametrize("K", [1, 4])
+def test_fused_decode_step_stream_state_matches_oracle(N, K):
+    """The same with the streaming hint on the state (bf16)."""
+    _fused_decode_vs_oracle(N, K, "bf16", stream=True)
+
+
+def _fused_decode_vs_oracle(N, K, io, stream):
     """mamba_conv1d_selective_state_update over several tokens against the
     oracle's conv step followed by its state update (conv output in fp64, not
     rounded), with the window checked bit for bit after every token."""
     import selective_state_space_80_amd as mamba
-    say(f"fused decode step N={N} K={K} io={io}")
+    say(f"fused decode step N={N} K={K} io={io} stream_state={stream}")
     B, D, T = 3, 300, 4
     wl = W.DecodeWorkload("t", B, D, N, io, T, 1, 90 + K)
     init = W.decode_initial(wl)
@@ -257,7 +268,7 @@ def test_fused_decode_step_matches_oracle(N, K, io):
             dev(s["Bm"], io), dev(s["Cm"], io), conv_bias=dev(cb),
             dt_bias=dev(init["dt_bias"]) if with_opt else None,
             Dskip=dev(init["Dskip"]) if with_opt else None,
-            z=dev(s["z"], io) if with_opt else None)
+            z=dev(s["z"], io) if with_opt else None, stream_state=stream)
         xc, cs_or = oracle.conv1d_update(cs_or, s["x"], ci["conv_w"], cb)
         yo, h_or = oracle.state_update(h_or, xc, s["dt"], init["A"], s["Bm"], s["Cm"],
                                        dt_bias=init["dt_bias"] if with_opt else None,
