@@ -37,7 +37,9 @@ constexpr int kNSub = kBT / kSub;    // sub-chunks per chunk, each from its own 
 constexpr int kBThreads = 256;       // 64 channels x 4 lanes (4 states each)
 constexpr int kCh = kBThreads / 4;   // channels per workgroup (one tile)
 constexpr int kPad = kBT + 1;        // LDS row stride of the per-channel arrays
-constexpr int kTStride = 2 * kMaxN + 4;  // row of dB then dC values, 16-byte aligned
+// row of sT: dB then dC of two steps (32 floats each) and two float4s of room
+// for the odd channels' shift
+constexpr int kTStride = 4 * kMaxN + 8;
 
 // dβ/dA for β(A) = (e^(ΔA) - 1)/A, u = ΔA, e = e^u:  Δ² ψ(u) with
 // ψ(u) = (u e^u - e^u + 1)/u² = Σ_m (m+1) u^m / (m+2)!, by its series through
@@ -80,12 +82,17 @@ struct BwdSmem {
     float sDel[kCh][kPad], sX[kCh][kPad], sDY[kCh][kPad];
     // dB, dC of two steps per wave, channel-major, summed over the wave's 16
     // channels by reading them back transposed; the wave sums of a sub-chunk go
-    // to sRed (two buffers: sub-chunks alternate)
-    float sT[kBThreads / 64][2][16][kTStride];
+    // to sRed (two buffers: sub-chunks alternate).  A row is 18 float4s, so
+    // consecutive channels start 2 float4s (8 banks) apart; odd channels store
+    // 2 float4s further on, so that the 8 lanes of each 16-byte-store cycle (two
+    // channels x four quarters) hit 32 different banks.
+    float sT[kBThreads / 64][16][kTStride];
     float sRed[2][kBThreads / 64][kSub][2 * kMaxN];
 };
 static_assert(offsetof(BwdSmem, sC) % 16 == 0 && offsetof(BwdSmem, sT) % 16 == 0,
               "rows read and written as float4");
+// 54016 bytes (sT rows of 20 float4s) measured at two workgroups per CU
+static_assert(sizeof(BwdSmem) <= 52 * 1024, "three workgroups per CU");
 
 // The whole chunk computation for one class of A (STRUCT: the structured form,
 // whose recompute takes the decays of a step's states as powers of one
@@ -290,17 +297,21 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs &p, BwdSmem &sm)
             dxp = quad_sum(dxp);
             ddel = quad_sum(ddel);
             yp = quad_sum(yp);
-            // every lane of the quad holds the sums: all four store the same
-            // values, no branch.  Δ, x and dy of step r are not read again.
+            // every lane of the quad holds the sums; lane 0 stores them (all
+            // four storing the same words measured 2% slower).  Δ, x and dy of
+            // step r are not read again.
             dDacc = fmaf(dy, xv, dDacc);     // padded steps have dy = x = 0
-            sDel[ch][r] = ddel;              // dΔ (times σ at the output)
-            sX[ch][r] = fmaf(Dd, dy, dxp);   // dx
-            sDY[ch][r] = fmaf(Dd, xv, yp);   // y + D x, for dz
+            if (q == 0) {
+                sDel[ch][r] = ddel;              // dΔ (times σ at the output)
+                sX[ch][r] = fmaf(Dd, dy, dxp);   // dx
+                sDY[ch][r] = fmaf(Dd, xv, yp);   // y + D x, for dz
+            }
             // dB, dC: sums over the wave's 16 channels.  Two steps at a time: the
             // lanes store their values channel-major, then lane l adds up the
             // 16 channels of entry l (step j + l/32, value l%32) in order.
             const int s2 = j & 1;
-            float4 *row = reinterpret_cast<float4 *>(&sT[wave][s2][(tid & 63) >> 2][0]);
+            const int wc = (tid & 63) >> 2;  // the lane's channel within the wave
+            float4 *row = reinterpret_cast<float4 *>(&sT[wave][wc][(wc & 1) * 8 + s2 * 2 * kMaxN]);
             row[q] = make_float4(dBv[0], dBv[1], dBv[2], dBv[3]);
             row[4 + q] = make_float4(dCv[0], dCv[1], dCv[2], dCv[3]);
             if (s2 == 0) {
@@ -309,7 +320,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs &p, BwdSmem &sm)
                 float acc = 0.f;
 #pragma unroll
                 for (int cw = 0; cw < 16; ++cw)
-                    acc += sT[wave][so][cw][kn];
+                    acc += sT[wave][cw][(cw & 1) * 8 + l];
                 red[wave][j + so][kn] = acc;
                 __builtin_amdgcn_wave_barrier();
             }
