@@ -35,7 +35,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kP = kSsdHeadDim;  // channels per head
 constexpr int kT = 256;       // threads per workgroup
-constexpr int kYP = kP + 1;   // row of the fp32 output tile
+// row of the fp32 output tile: 16-byte rows whose stride (68 words) puts the
+// two 16-lane halves of a store of step 6 on different banks
+constexpr int kYP = kP + 4;
 
 // MFMA lane layouts (64 lanes, l16 = lane % 16, g4 = lane / 16), D = A B:
 //   16x16x16 bf16: A[l16][4 g4 + j], B[4 g4 + j][l16], j < 4
@@ -110,7 +112,7 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
     __shared__ __align__(16) uint16_t sX[kQ * (kP + 8)];   // x[s][p]
     __shared__ __align__(16) uint16_t sXt[kP * kQP];       // x^T[p][s]
     __shared__ __align__(16) uint16_t sXw[2][kP * kQP];    // (w x)^T[p][s], hi and lo
-    __shared__ float sY[kQ * kYP];                         // output tile Y[t][p]
+    __shared__ __align__(16) float sY[kQ * kYP];           // output tile Y[t][p]
     __shared__ __align__(16) uint16_t sM[kTiles][2][64 * 4];  // M tiles, hi and lo, A layout
     // per step of a chunk: Λ, β, w = e^(Λ_end - Λ) β, e^Λ, and the chunk's
     // e^Λ_end; two buffers, chunks alternate (see step 4)
@@ -426,11 +428,19 @@ __global__ void __launch_bounds__(kT, (Q == 32 && N <= 64) ? 3 : 2) ssd_fwd_kern
                 const uint32_t xw[4] = {cX[k].x, cX[k].y, cX[k].z, cX[k].w};
                 const uint32_t zw[4] = {cZ[k].x, cZ[k].y, cZ[k].z, cZ[k].w};
                 uint32_t out[4];
+                // the thread's 8 values as two 16-byte reads; threads with
+                // xc >= 32 read their upper half first, so that each read's 8
+                // lanes (one row) hit 32 different banks
+                const float *yrow = sY + xr * kYP + xc + 8 * k;
+                const int sw = (xc >> 5) & 1;
+                const float4 fa = *reinterpret_cast<const float4 *>(yrow + 4 * sw);
+                const float4 fb = *reinterpret_cast<const float4 *>(yrow + 4 * (sw ^ 1));
+                const float4 lo = sw ? fb : fa, hi = sw ? fa : fb;
+                const float yv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float *yr = sY + xr * kYP + xc + 8 * k + 2 * j;
-                    float v0 = fmaf(Dv, __uint_as_float(xw[j] << 16), yr[0]);
-                    float v1 = fmaf(Dv, __uint_as_float(xw[j] & 0xffff0000u), yr[1]);
+                    float v0 = fmaf(Dv, __uint_as_float(xw[j] << 16), yv[2 * j]);
+                    float v1 = fmaf(Dv, __uint_as_float(xw[j] & 0xffff0000u), yv[2 * j + 1]);
                     if (p.z) {
                         v0 *= silu_hw(__uint_as_float(zw[j] << 16));
                         v1 *= silu_hw(__uint_as_float(zw[j] & 0xffff0000u));
