@@ -33,6 +33,14 @@
 //   * Once a chunk knows its true start state h_in, each kept output gets the
 //     missing term sum_n C_tn * (prod_(s<=t) Ā_sn) * h_in,n added, then the
 //     gate, then one store.  Every input element is read once, y written once.
+//   * Every global load a wave needs before its scan is issued before the
+//     first of them is waited for: the small ones (conv taps, B/C rows) first,
+//     then the chunk's x and dt, so that waiting for the small ones (the wait
+//     counter is in order) leaves the chunk's loads in flight.  A branch
+//     around a load works against this: at the join the compiler may reuse a
+//     register an in-flight load still targets and so wait for every load.
+//     fp32 problems of whole segments with aligned rows therefore take a FULL
+//     instantiation with no ragged-chunk path at all.
 //
 // Two arithmetic paths, chosen per 64-channel tile by the prep kernel:
 //   structured  A_dn = (n+1) A_d0 exactly with A_d0 < 0 (the S4D-real form).
@@ -359,42 +367,61 @@ struct ScanKArgs {
     int spin_limit;       // polls before a carry wait gives up
 };
 
+// The fused front end's per-lane inputs besides the chunk itself: the taps,
+// the bias and the raw inputs of the three steps before the chunk (from x, or
+// from the carried conv state before t = 0).
+template <bool BF16>
+struct ConvPre {
+    float wk[kFusedConvTaps], cb;
+    float vx[kFusedConvTaps - 1], vs[kFusedConvTaps - 1];
+    bool in_x[kFusedConvTaps - 1], in_cs[kFusedConvTaps - 1];
+    // every load from an index that is always valid, with no branch around
+    // any of them; the values are selected where they are used
+    __device__ __forceinline__ void load(const ScanKArgs &p, int64_t bd, int64_t dc, int64_t t0,
+                                         int64_t row_off)
+    {
+        using E = Elem<BF16>;
+        using T = typename E::T;
+        const int K = p.conv_K;
+#pragma unroll
+        for (int s = 0; s < kFusedConvTaps; ++s) {
+            const int k = s - (kFusedConvTaps - K);
+            wk[s] = p.conv_w[dc * K + (k >= 0 ? k : 0)];
+        }
+        cb = (p.conv_b ? p.conv_b : p.conv_w)[dc];  // conv_w has >= D entries
+        const T *xs = reinterpret_cast<const T *>(p.x);
+        const T *cs = reinterpret_cast<const T *>(p.conv_state_in ? p.conv_state_in : p.x);
+#pragma unroll
+        for (int i = 0; i < kFusedConvTaps - 1; ++i) {
+            const int64_t t = t0 - (kFusedConvTaps - 1) + i;
+            const int64_t si = (int64_t)(K - 1) + t;  // slot of the carried raw inputs (t < 0)
+            in_x[i] = t >= 0 && t < p.L;
+            in_cs[i] = t < 0 && p.conv_state_in && si >= 0;
+            vx[i] = E::load(xs + (in_x[i] ? row_off - (kFusedConvTaps - 1) + i : 0));
+            vs[i] = E::load(cs + (in_cs[i] ? bd * (K - 1) + si : 0));
+        }
+    }
+};
+
 // Fused front end: the chunk's scan inputs SiLU(bias + sum_k w_k x_(t-K+1+k))
-// from the raw inputs of the chunk (already in `xin`) and of the three steps
-// before it.  Taps are right-aligned in kFusedConvTaps slots (zero weights in
+// from the raw inputs of the chunk (in `xin`) and of the three steps before it
+// (in `cp`).  Taps are right-aligned in kFusedConvTaps slots (zero weights in
 // front for K < 4).  Computed from the last step down, so each raw value is
 // still available when the outputs that need it are formed.  Steps at or past
 // the end of the sequence get the identity input 0.
 template <bool BF16>
-__device__ __forceinline__ void conv_chunk(const ScanKArgs &p, const InChunk<BF16> &xin,
-                                           int64_t bd, int64_t dc, int64_t t0, int64_t row_off,
-                                           int nt, float (&xc)[kChunkT])
+__device__ __forceinline__ void conv_chunk(const ScanKArgs &p, const ConvPre<BF16> &cp,
+                                           const InChunk<BF16> &xin, int nt, float (&xc)[kChunkT])
 {
-    using E = Elem<BF16>;
-    using T = typename E::T;
     const int K = p.conv_K;
-    float wk[kFusedConvTaps];
+    float wk[kFusedConvTaps], hm[kFusedConvTaps - 1];
 #pragma unroll
-    for (int s = 0; s < kFusedConvTaps; ++s) {
-        const int k = s - (kFusedConvTaps - K);
-        wk[s] = (k >= 0) ? p.conv_w[dc * K + k] : 0.f;
-    }
-    const float cb = p.conv_b ? p.conv_b[dc] : 0.f;
-    float hm[kFusedConvTaps - 1];  // raw x at t0-3, t0-2, t0-1
+    for (int s = 0; s < kFusedConvTaps; ++s)
+        wk[s] = s - (kFusedConvTaps - K) >= 0 ? cp.wk[s] : 0.f;
+    const float cb = p.conv_b ? cp.cb : 0.f;
 #pragma unroll
-    for (int i = 0; i < kFusedConvTaps - 1; ++i) {
-        const int64_t t = t0 - (kFusedConvTaps - 1) + i;
-        if (t >= p.L) {
-            hm[i] = 0.f;  // a wave past the end of the sequence (nt = 0) reads nothing
-        } else if (t >= 0) {
-            hm[i] = E::load(reinterpret_cast<const T *>(p.x) + row_off - (kFusedConvTaps - 1) + i);
-        } else {
-            const int64_t si = (int64_t)(K - 1) + t;  // slot of the carried raw inputs
-            hm[i] = (p.conv_state_in && si >= 0)
-                        ? E::load(reinterpret_cast<const T *>(p.conv_state_in) + bd * (K - 1) + si)
-                        : 0.f;
-        }
-    }
+    for (int i = 0; i < kFusedConvTaps - 1; ++i)
+        hm[i] = cp.in_x[i] ? cp.vx[i] : (cp.in_cs[i] ? cp.vs[i] : 0.f);
     auto raw = [&](int i) -> float { return i >= 0 ? xin.get(i) : hm[kFusedConvTaps - 1 + i]; };
 #pragma unroll
     for (int j = kChunkT - 1; j >= 0; --j) {
@@ -484,6 +511,45 @@ __device__ __forceinline__ void stage_bc(const ScanKArgs &p, float (*s_bc)[kSegT
     }
 }
 
+// B/C of a whole segment with N = 16 and aligned rows, fp32: loaded into
+// registers first, stored to LDS once the chunk's own loads are issued.
+template <bool STRUCT, bool REV, bool ADJ>
+struct BcPre {
+    static constexpr int kPer = kSegT * kMaxN / 4 / (kWave * kWavesPerSeg);
+    float4 v[2][kPer];
+    __device__ __forceinline__ void load(const ScanKArgs &p, int64_t b, int64_t seg, int64_t Ls,
+                                         int tid)
+    {
+        const int64_t t0s = seg * kSegT;
+        const int64_t run0 = REV ? Ls - t0s - kSegT : t0s;
+        const float *Bb = reinterpret_cast<const float *>(ADJ ? p.Cm : p.Bm) + b * p.L * p.N;
+        const float *Cb = reinterpret_cast<const float *>(p.Cm) + b * p.L * p.N;
+        const float *src[2] = {Bb + run0 * p.N, Cb + run0 * p.N};
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+                v[m][i] = reinterpret_cast<const float4 *>(src[m])[tid + i * (kWave * kWavesPerSeg)];
+    }
+    __device__ __forceinline__ void store(float (*s_bc)[kSegT][kMaxN], int tid) const
+    {
+        auto lrow = [](int pr) { return REV ? kSegT - 1 - pr : pr; };
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int q = tid + i * (kWave * kWavesPerSeg);
+                const int row = lrow(q >> 2), n4 = (q & 3) * 4;
+                float4 x = v[m][i];
+                if (m == 1 && STRUCT)
+                    x = make_float4(x.x * hw_rcp((float)(n4 + 1)), x.y * hw_rcp((float)(n4 + 2)),
+                                    x.z * hw_rcp((float)(n4 + 3)), x.w * hw_rcp((float)(n4 + 4)));
+                *reinterpret_cast<float4 *>(&s_bc[m][row][n4]) = x;
+            }
+        }
+    }
+};
+
 // One LDS row of kMaxN floats into registers (four 128-bit broadcast reads).
 __device__ __forceinline__ void lds_row(const float *row, float (&v)[kMaxN])
 {
@@ -533,7 +599,7 @@ __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 }
 
 // The whole per-workgroup body for one arithmetic path.
-template <bool BF16, bool STRUCT, bool CONV, bool REV, bool ADJ>
+template <bool BF16, bool STRUCT, bool CONV, bool REV, bool ADJ, bool FULL>
 __device__ __forceinline__ void scan_segment(
     const ScanKArgs &p, uint32_t *__restrict__ flags, float *__restrict__ agg,
     uint64_t *__restrict__ incl, uint32_t epoch,
@@ -566,7 +632,7 @@ __device__ __forceinline__ void scan_segment(
     const int khi = __builtin_amdgcn_readfirstlane(
         REV ? (nt > 0 ? (int)min((int64_t)kChunkT, p.L - p0) : 0) : nt);
     const int klo = 0;
-    const bool vec = p.vec && khi == kChunkT;
+    const bool vec = FULL || (p.vec && khi == kChunkT);
     const int64_t row_off = (b * p.D + dc) * p.L + p0;
     const int64_t chunk_slot = REV ? Ls / kChunkT - 1 - t0 / kChunkT : t0 / kChunkT;
     auto slot = [](int j) { return REV ? kChunkT - 1 - j : j; };
@@ -610,12 +676,24 @@ __device__ __forceinline__ void scan_segment(
     float hs[kMaxN];
     float summ;
     {
+        // the small loads first (conv taps, B/C rows of a whole fp32 segment),
+        // then the chunk's x and dt: a wait for the early ones then leaves the
+        // chunk's loads in flight
+        ConvPre<BF16> cpre;
+        if constexpr (CONV)
+            cpre.load(p, b * p.D + dc, dc, t0, row_off);
+        constexpr bool kBcPre = FULL && !BF16;
+        BcPre<STRUCT, REV, ADJ> bpre;
+        if constexpr (kBcPre)
+            bpre.load(p, b, seg, Ls, w * kWave + lane);
         InChunk<BF16> xin, din;
         xin.load(p.x, row_off, klo, khi, vec, 0.f);
         din.load(p.dt, row_off, klo, khi, vec, -__builtin_huge_valf());
+        if constexpr (kBcPre)
+            bpre.store(s_bc, w * kWave + lane);
         float xc[kChunkT];  // scan inputs of the fused front end (CONV only)
         if constexpr (CONV)
-            conv_chunk<BF16>(p, xin, b * p.D + dc, dc, t0, row_off, nt, xc);
+            conv_chunk<BF16>(p, cpre, xin, nt, xc);
         // adjoint scan: the input is dy = dout * SiLU(z) (x holds dout)
         InChunk<BF16> zadj;
         if (ADJ && p.z)
@@ -628,7 +706,8 @@ __device__ __forceinline__ void scan_segment(
             else
                 return xin.get(slot(j));
         };
-        stage_bc<BF16, STRUCT, REV, ADJ>(p, s_bc, b, seg, Ls, w * kWave + lane);
+        if constexpr (!kBcPre)
+            stage_bc<BF16, STRUCT, REV, ADJ>(p, s_bc, b, seg, Ls, w * kWave + lane);
         __syncthreads();
         // Step decays of the whole chunk first (independent chains, out of
         // the serial loop): er[j] = exp(Δ_j A_0) (structured) or Δ_j/ln2.
@@ -1002,7 +1081,11 @@ __device__ __forceinline__ void scan_segment(
                           [&](int k) { return yl[slot(k)]; });
 }
 
-template <bool BF16, bool CONV, bool REV, bool ADJ>
+// FULL: every chunk of the problem is whole and its rows are 16-byte aligned
+// (L a multiple of kSegT, aligned x, dt, z, y; N = 16 with aligned B, C), so
+// the inputs take 128-bit loads with no bounds checks and B/C go through
+// registers ahead of the chunk's own loads.
+template <bool BF16, bool CONV, bool REV, bool ADJ, bool FULL>
 __global__ void __launch_bounds__(kWave *kWavesPerSeg, kScanWavesPerSimd) scan_main_kernel(
     ScanKArgs p, const uint32_t *__restrict__ tiles)
 {
@@ -1034,10 +1117,10 @@ __global__ void __launch_bounds__(kWave *kWavesPerSeg, kScanWavesPerSimd) scan_m
     const int64_t dtile = g % p.lay.n_dtiles;
     const uint32_t path = __builtin_amdgcn_readfirstlane(tiles[dtile]);
     if (path == kPathStructured)
-        scan_segment<BF16, true, CONV, REV, ADJ>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, true, CONV, REV, ADJ, FULL>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
                                        s_part, s_bc, s_A, &s_timeout);
     else
-        scan_segment<BF16, false, CONV, REV, ADJ>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
+        scan_segment<BF16, false, CONV, REV, ADJ, FULL>(p, flags, agg, incl, epoch, hdr, seg, g, w, lane, s_agg,
                                         s_part, s_bc, s_A, &s_timeout);
 }
 
@@ -1184,27 +1267,39 @@ hipError_t launch_selective_scan(const ScanArgs &a, hipStream_t s)
     if (a.ev_start)
         (void)hipEventRecord(a.ev_start, s);
     const dim3 grid((unsigned)lay.n_items), block(kWave * kWavesPerSeg);
-#define MAMBA_SCAN_LAUNCH(BF, CV, RV, AJ) \
-    hipLaunchKernelGGL((scan_main_kernel<BF, CV, RV, AJ>), grid, block, 0, s, k, tiles)
+    // fp32 problems of whole segments with aligned rows take the FULL kernel
+    // (no ragged chunk, so no branch around any input load); bf16 ones do not
+    // need it (their loads already leave together) and would spill with it
+    const bool full = !a.bf16 && k.vec && k.bc_vec && a.L % kSegT == 0;
+#define MAMBA_SCAN_LAUNCH(BF, CV, RV, AJ, FL) \
+    hipLaunchKernelGGL((scan_main_kernel<BF, CV, RV, AJ, FL>), grid, block, 0, s, k, tiles)
+#define MAMBA_SCAN_LAUNCH_F32(CV, RV, AJ)                 \
+    do {                                                  \
+        if (full)                                         \
+            MAMBA_SCAN_LAUNCH(false, CV, RV, AJ, true);   \
+        else                                              \
+            MAMBA_SCAN_LAUNCH(false, CV, RV, AJ, false);  \
+    } while (0)
     if (a.bf16) {
         if (a.conv_K)
-            MAMBA_SCAN_LAUNCH(true, true, false, false);
+            MAMBA_SCAN_LAUNCH(true, true, false, false, false);
         else if (a.adjoint)
-            MAMBA_SCAN_LAUNCH(true, false, true, true);
+            MAMBA_SCAN_LAUNCH(true, false, true, true, false);
         else if (a.reverse)
-            MAMBA_SCAN_LAUNCH(true, false, true, false);
+            MAMBA_SCAN_LAUNCH(true, false, true, false, false);
         else
-            MAMBA_SCAN_LAUNCH(true, false, false, false);
+            MAMBA_SCAN_LAUNCH(true, false, false, false, false);
     } else {
         if (a.conv_K)
-            MAMBA_SCAN_LAUNCH(false, true, false, false);
+            MAMBA_SCAN_LAUNCH_F32(true, false, false);
         else if (a.adjoint)
-            MAMBA_SCAN_LAUNCH(false, false, true, true);
+            MAMBA_SCAN_LAUNCH_F32(false, true, true);
         else if (a.reverse)
-            MAMBA_SCAN_LAUNCH(false, false, true, false);
+            MAMBA_SCAN_LAUNCH_F32(false, true, false);
         else
-            MAMBA_SCAN_LAUNCH(false, false, false, false);
+            MAMBA_SCAN_LAUNCH_F32(false, false, false);
     }
+#undef MAMBA_SCAN_LAUNCH_F32
 #undef MAMBA_SCAN_LAUNCH
     e = hipGetLastError();
     if (a.ev_stop)

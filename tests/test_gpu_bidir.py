@@ -11,7 +11,7 @@ from selective_state_space_80_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 64, 256, 16), (2, 100, 300, 16), (1, 37, 33, 7), (1, 64, 1, 16),
-          (1, 64, 129, 5), (1, 130, 2100, 16), (1, 64, 4096, 16)]
+          (1, 64, 129, 5), (1, 130, 2100, 16), (1, 64, 4096, 16), (2, 100, 512, 16)]
 
 
 def run(p, io, h0=None, reverse=False, accumulate=False, out=None):

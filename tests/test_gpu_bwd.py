@@ -11,7 +11,7 @@ from selective_state_space_80_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 64, 256, 16), (2, 100, 300, 16), (1, 37, 33, 7), (1, 64, 1, 16),
-          (1, 64, 129, 5), (1, 130, 2100, 16), (2, 64, 31, 16)]
+          (1, 64, 129, 5), (1, 130, 2100, 16), (2, 64, 31, 16), (2, 100, 256, 16)]
 KEYS_IO = ("dx", "ddt", "dz")                       # I/O dtype, rounded once
 KEYS_F32 = ("dA", "dB", "dC", "dD", "ddt_bias", "dh0")
 

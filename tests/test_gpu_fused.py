@@ -48,7 +48,7 @@ def run_fused(p, io, h0=None, conv_state_in="from_p", **kw):
 
 
 SHAPES = [(1, 64, 256, 16), (2, 100, 300, 16), (1, 37, 33, 7), (2, 64, 129, 16),
-          (1, 130, 2100, 16), (1, 64, 3, 16), (1, 64, 1, 4)]
+          (1, 130, 2100, 16), (1, 64, 3, 16), (1, 64, 1, 4), (2, 100, 384, 16)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))

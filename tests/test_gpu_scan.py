@@ -23,6 +23,7 @@ SHAPES = [
     (1, 64, 127, 16, "f32"),
     (1, 64, 129, 16, "f32"),
     (1, 64, 4096, 16, "f32"),
+    (2, 100, 512, 16, "f32"),  # whole fp32 segments, a ragged tile: the FULL kernel
     (3, 64, 517, 16, "bf16"),
     (2, 130, 1000, 4, "bf16"),
     (2, 64, 31, 16, "bf16"),
@@ -81,10 +82,11 @@ def test_scan_workload0_exact_config():
 
 @pytest.mark.parametrize("kind", ["negative_random", "with_zero_and_positive", "mixed_tiles"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_scan_general_A(kind, io):
+@pytest.mark.parametrize("L", [700, 768])  # 768: whole segments (fp32: the FULL kernel)
+def test_scan_general_A(kind, io, L):
     """Tiles whose A is not the structured (n+1)*A_0 form take the general path."""
-    say(f"scan general A {kind} {io}")
-    B, D, L, N = 2, 192, 700, 16
+    say(f"scan general A {kind} {io} L={L}")
+    B, D, N = 2, 192, 16
     p = W.make_scan_inputs(B, D, L, N, io, seed=17)
     rng = np.random.default_rng(3)
     if kind == "negative_random":
