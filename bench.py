@@ -31,7 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (packed fp32)
+# Without packed fp32 (the v_pk_*_f32 forms are switched off in every build here)
+# a CU issues one wave64 fp32 VALU instruction per clock: 4 SIMDs x 16 lanes, a
+# wave64 instruction occupying a SIMD for 4 clocks.  256 CUs at 2.4 GHz:
+VALU_ISSUE_PEAK = 256 * 2.4e9    # wave64 VALU instructions per second
+FP32_NOPACK_PEAK_TFLOPS = VALU_ISSUE_PEAK * 64 * 2 / 1e12  # 78.6: fma = 2 flops
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -256,18 +261,61 @@ def quantiles(ms):
 
 
 def valu_record(tr, elems, kernel_ms):
-    """VALU issue utilisation of the main scan kernel: wave-level VALU
-    instructions per launch (rocprofv3 SQ_INSTS_VALU on the same kernel source)
-    over the time of one launch, against the published fp32 vector peak in
-    wave64 instructions: 157.3 TFLOP/s / 2 flops per fma / 64 lanes, i.e. two
-    wave64 fp32 instructions per clock per CU (256 CUs at 2.4 GHz)."""
+    """Measured VALU issue of a kernel: wave64 VALU instructions per launch
+    (rocprofv3 SQ_INSTS_VALU, taken on the same kernel source) over the time of
+    one launch, against one wave64 instruction per clock per CU; and the VALU
+    busy cycles (SQ_ACTIVE_INST_VALU: a transcendental counts two, and they
+    partly overlap other VALU work, so this may exceed 1 on exp-heavy kernels)."""
     if tr is None or "valu_insts" not in tr:
         return None
-    peak = FP32_VECTOR_PEAK_TFLOPS * 1e12 / 2 / 64
     per_s = tr["valu_insts"] / (kernel_ms * 1e-3)
-    return {"wave_instr_per_launch": int(tr["valu_insts"]),
-            "wave_instr_per_elem": round(tr["valu_insts"] * 64 / elems, 1),
-            "issue_peak_per_s": peak, "frac": round(per_s / peak, 4)}
+    rec = {"wave_instr_per_launch": int(tr["valu_insts"]),
+           "wave_instr_per_elem": round(tr["valu_insts"] * 64 / elems, 1),
+           "issue_peak_per_s": VALU_ISSUE_PEAK, "frac": round(per_s / VALU_ISSUE_PEAK, 4)}
+    if "valu_active" in tr:
+        rec["busy_frac"] = round(tr["valu_active"] / (kernel_ms * 1e-3) / VALU_ISSUE_PEAK, 4)
+    return rec
+
+
+def scan_valu_per_elem(io, conv=False):
+    """Algorithmic VALU instructions per scanned element of the forward scan
+    (structured A, N = 16, with dt_bias, D and the gate): the arithmetic the
+    chunked two-level scan performs, without loads, stores, addressing,
+    register moves or waits.  A transcendental counts one instruction.
+      chunk scan per step: Δ = softplus (fma, exp2, add, log2, compare,
+        select: 6), the step decay (mul, exp2: 2), e - 1 (1), 16 states x 3
+        minus the first power (47), readout (16), cumulative decay (1),
+        skip and scale (2)                                              75
+      fix-up: 16 products C_n/(n+1) * carried state, 16 Horner fmas, 2  34
+      gate: SiLU(z) (mul, exp2, add, rcp, mul) and the product          6
+      carry: chunk and segment maps, start states (~136 per 32 steps)  4.25
+      bf16 I/O: unpack x, dt, z; pack y                                 3.5
+      fused conv1d, 4 taps: 4 fma + SiLU                                9"""
+    n = 75 + 34 + 6 + 4.25
+    if io == "bf16":
+        n += 3.5
+    if conv:
+        n += 9
+    return n
+
+
+def scan_roofline(kernel, io, conv, elems, kernel_ms, alg_bytes, tr):
+    """Roofline of a forward scan kernel.  Its binding roof is VALU issue: the
+    counted instructions need more time at one wave64 instruction per clock per
+    CU than its bytes need at 8 TB/s.  `achieved` is the algorithmic VALU
+    instruction rate (scan_valu_per_elem x elements / kernel time); `hbm` is the
+    metric's own figure, algorithmic bytes over kernel time against 8 TB/s."""
+    per_elem = scan_valu_per_elem(io, conv)
+    alg_instr = per_elem * elems / 64
+    achieved = alg_instr / (kernel_ms * 1e-3)
+    gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    return {"bound": "alu", "achieved": round(achieved / 1e9, 1),
+            "peak": round(VALU_ISSUE_PEAK / 1e9, 1), "unit": "G VALU instr/s (wave64)",
+            "frac": round(achieved / VALU_ISSUE_PEAK, 4), "traffic": traffic_bytes(tr),
+            "kernel": kernel, "kernel_ms": round(kernel_ms, 4),
+            "algorithmic_instr_per_elem": per_elem, "algorithmic_instr": int(alg_instr),
+            "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_bytes}}
 
 
 
@@ -378,16 +426,18 @@ def measure_scan(torch, mamba, W, idx, steps, warmup, settle_s, cpu_s, no_cpu=Fa
            "step_gelem_s": round(elems / (ms_step * 1e-3) / 1e9, 3),
            "ms_per_step": round(ms_step, 4), "steps": steps, "warmup": warmup,
            "clock_settle": settle,
-           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": traffic_bytes(tr), "kernel": f"main scan kernel ({wl.io})",
-                        "kernel_ms": round(k_ms, 4), "algorithmic_bytes": sb},
+           "roofline": scan_roofline(f"main scan kernel ({wl.io})", wl.io, False, elems, k_ms,
+                                     sb, tr),
            "valu": valu_record(tr, elems, k_ms),
            "kernels": {"scan_ms": quantiles(k_all),
                        "scan_gelem_s": round(elems / (k_ms * 1e-3) / 1e9, 2)}}
     if idx == 0:
-        out["roofline"]["note"] = ("0.3 MB problem: cache-resident and launch-latency bound, "
-                                   "reported for completeness")
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": None, "kernel": f"main scan kernel ({wl.io})",
+                           "kernel_ms": round(k_ms, 4), "algorithmic_bytes": sb,
+                           "note": "0.3 MB problem: cache-resident and launch-latency bound, "
+                                   "reported for completeness"}
     if not no_cpu:
         ch = min(D, 64)
         y_rows = y[0:1, :ch].float().cpu().numpy().astype(np.float64)
@@ -562,11 +612,7 @@ def run_block(args, torch, mamba, W):
                    "d_state": N, "d_conv": K, "io": "f32", "state": "f32",
                    "step": ("conv1d_silu, then selective_scan_fwd" if args.unfused else
                             "conv1d_selective_scan_fwd (conv1d+SiLU fused into the scan)")},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": kname,
-                     "kernel_ms": round(scan_ms, 4),
-                     "algorithmic_bytes": sb},
+        "roofline": scan_roofline(kname, "f32", not args.unfused, elems, scan_ms, sb, tr),
         "valu": valu_record(tr, elems, scan_ms),
         "kernels": kernels,
         "clock_settle": settle,
@@ -734,10 +780,11 @@ def run_bwd(args, torch, mamba, W):
                        "step": "forward recompute, adjoint scan, chunk gradients, reductions"},
             # the chunk-gradient kernel is bound by fp32 arithmetic: 30 flops of the
             # formulas per (element, state) (recompute 7, gradients 23; an fma counts
-            # 2, exp and reciprocal 1), against the fp32 vector peak
+            # 2, exp and reciprocal 1), against the fp32 vector peak without packed
+            # math (one wave64 fma per clock per CU: 78.6 TFLOP/s)
             "roofline": {"bound": "alu", "achieved": round(30 * elems * N / (k_ms * 1e-3) / 1e12, 2),
-                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(30 * elems * N / (k_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "peak": round(FP32_NOPACK_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                         "frac": round(30 * elems * N / (k_ms * 1e-3) / 1e12 / FP32_NOPACK_PEAK_TFLOPS, 4),
                          "traffic": traffic_bytes(traffic_record(f"scan_bwd_b{B}_d{D}_l{L}_n{N}_f32")),
                          "kernel": "scan_bwd_chunk_kernel<fp32>",
                          "kernel_ms": round(k_ms, 4), "algorithmic_flops": 30 * elems * N},

@@ -110,6 +110,10 @@ def traffic(fetch_db, write_db, copy_bytes, kernel, source=None, sq_db=None):
         sq = _find(counters(sq_db), kernel)
         out["valu_insts"] = sq["SQ_INSTS_VALU"]
         out["waves"] = sq["SQ_WAVES"]
+        # VALU busy time in wave64 issue cycles of a CU (one fp32 operation
+        # per cycle, two for a transcendental)
+        if "SQ_ACTIVE_INST_VALU" in sq:
+            out["valu_active"] = sq["SQ_ACTIVE_INST_VALU"]
     if source:
         out["source"] = os.path.relpath(source, os.path.dirname(os.path.dirname(
             os.path.abspath(__file__))))
@@ -131,7 +135,8 @@ def main(argv=None):
     tr.add_argument("--copy-bytes", type=int, required=True)
     tr.add_argument("--kernel", default="scan_main_kernel")
     tr.add_argument("--source", default=None, help="kernel source to fingerprint")
-    tr.add_argument("--sq", default=None, help="run with SQ_INSTS_VALU and SQ_WAVES")
+    tr.add_argument("--sq", default=None,
+                    help="run with SQ_INSTS_VALU, SQ_WAVES (and SQ_ACTIVE_INST_VALU)")
     tr.add_argument("--variant", default="block_fused",
                     help="key of the record in --out: the workload it was taken on")
     tr.add_argument("--out", default=None)
