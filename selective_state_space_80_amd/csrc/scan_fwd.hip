@@ -729,6 +729,7 @@ __device__ __forceinline__ void scan_segment(
             lds_row(s_bc[0][w * kChunkT], Bc);
 #pragma unroll
         for (int j = 0; j < kChunkT; ++j) {
+            const float ej = er[j];  // the step's decay (structured path)
             if (j < nt) {  // one basic block per step
                 const float xv = xget(j);
                 const float *Bj = s_bc[0][w * kChunkT + j];  // B (LDS broadcast)
@@ -763,7 +764,7 @@ __device__ __forceinline__ void scan_segment(
                     // built as (e_n - 1) = e (e_(n-1) - 1) + (e - 1)
                     float Cr[kMaxN];
                     lds_row(Cj, Cr);
-                    const float e1 = er[j];
+                    const float e1 = ej;
                     const float em0 = e1 - 1.f;  // exact (Sterbenz)
                     float em = em0;
 #pragma unroll
@@ -778,9 +779,7 @@ __device__ __forceinline__ void scan_segment(
 #pragma unroll
                     for (int n = 0; n < kMaxN; ++n)
                         acc = fmaf(Cr[n], hs[n], acc);
-                    E *= e1;
                     yl[j] = fmaf(acc, inva0, Dd * xv);
-                    er[j] = E;
                 } else {
                     const float l = er[j];
                     const float delta = l * kLn2;
@@ -797,9 +796,14 @@ __device__ __forceinline__ void scan_segment(
                     er[j] = cumL;
                 }
             }
+            // structured forward: er[j] becomes the cumulative decay E_j, formed
+            // on every step (a padding step's decay is exactly 1), so that no
+            // running product has to be carried beside the kept values
+            if constexpr (STRUCT && !ADJ)
+                er[j] = j ? er[j - 1] * ej : ej;
         }
         if constexpr (STRUCT) {
-            summ = E;
+            summ = ADJ ? E : er[kChunkT - 1];
             // back to true units: h_n = ĥ_n / A_n (the adjoint is unscaled)
             if constexpr (!ADJ) {
 #pragma unroll
@@ -1045,9 +1049,11 @@ __device__ __forceinline__ void scan_segment(
                 if (j < ntf) {
                     const float *cs = s_bc[1][w * kChunkT + j];  // C/(n+1)
                     const float Ej = er[j];
-                    float qh = 0.f;
+                    // Horner from the last state (starting from 0 would cost an
+                    // fma with 0, which the compiler keeps)
+                    float qh = cs[kMaxN - 1] * hsc[kMaxN - 1];
 #pragma unroll
-                    for (int n = kMaxN - 1; n >= 0; --n)
+                    for (int n = kMaxN - 2; n >= 0; --n)
                         qh = fmaf(qh, Ej, cs[n] * hsc[n]);
                     yl[j] = fmaf(qh * Ej, inva0, yl[j]);
                 }
