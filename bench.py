@@ -286,12 +286,12 @@ def scan_valu_per_elem(io, conv=False):
         select: 6), the step decay (mul, exp2: 2), e - 1 (1), 16 states x 3
         minus the first power (47), readout (16), cumulative decay (1),
         skip and scale (2)                                              75
-      fix-up: 16 products C_n/(n+1) * carried state, 16 Horner fmas, 2  34
+      fix-up: 16 products C_n/(n+1) * carried state, 15 Horner fmas, 2  33
       gate: SiLU(z) (mul, exp2, add, rcp, mul) and the product          6
       carry: chunk and segment maps, start states (~136 per 32 steps)  4.25
       bf16 I/O: unpack x, dt, z; pack y                                 3.5
       fused conv1d, 4 taps: 4 fma + SiLU                                9"""
-    n = 75 + 34 + 6 + 4.25
+    n = 75 + 33 + 6 + 4.25
     if io == "bf16":
         n += 3.5
     if conv:
