@@ -898,6 +898,53 @@ def run_decode(args, torch, mamba, W):
                 else None)})}
 
 
+PROBE_LIBRARY = os.path.join(ROOT, "selective_state_space_80_amd", "libmamba_probe.so")
+PROBE_MODES = ((0, "8 independent fma chains", 8),
+               (1, "8 chains of exp2 then mul", 16),
+               (2, "1 exp2 chain and 7 fma chains", 8))
+
+
+def run_probe_valu(torch):
+    """The VALU issue-rate probe behind the roofline's peak: independent chains
+    per lane (libmamba_probe.so, built without packed fp32 like the kernels) at
+    2, 3, 4 and 8 waves per SIMD, timed with events on the launch stream.
+    Reports wave64 VALU instructions per clock per CU at the 2.4 GHz peak clock,
+    and the clocks one round of 8 chain steps takes per CU."""
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.mamba_probe_valu_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for mode, what, instr_per_round in PROBE_MODES:
+        for wgs in (2, 3, 4, 8):
+            grid = n_cu * wgs * 8  # eight workgroups per resident slot
+            out = torch.empty(grid * 256, dtype=torch.float32, device="cuda:0")
+            if lib.mamba_probe_valu_launch(out.data_ptr(), mode, grid, wgs, 200, stream) != 0:
+                raise RuntimeError("probe launch failed")
+            times = []
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if lib.mamba_probe_valu_launch(out.data_ptr(), mode, grid, wgs, iters,
+                                               stream) != 0:
+                    raise RuntimeError("probe launch failed")
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = min(times)
+            rounds = grid * 4 * iters * 16  # wave-level rounds of 8 chain steps
+            clocks = ms * 1e-3 * 2.4e9 * n_cu
+            rows.append({"mode": what, "waves_per_simd": wgs, "ms": round(ms, 3),
+                         "instr_per_clock_per_cu": round(rounds * instr_per_round / clocks, 3),
+                         "clocks_per_round_per_cu": round(clocks / rounds, 2)})
+            del out
+    return {"metric": "VALU issue probe", "unit": "wave64 VALU instructions per clock per CU "
+            "at 2.4 GHz", "n_cu": n_cu, "packed_fp32": False, "results": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -924,6 +971,9 @@ def main():
                     help="untimed back-to-back steps before the warm-up, for steady clocks")
     ap.add_argument("--decode-sets", type=int, default=8,
                     help="decode: state buffers used in turn for the cold figure (8 x 84 MB)")
+    ap.add_argument("--probe-valu", action="store_true",
+                    help="instead of a workload, run the VALU issue-rate probe that the "
+                         "roofline's peak rests on (libmamba_probe.so)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one elementwise kernel that reads and writes "
                          "this many MiB (known traffic for scaling rocprofv3 byte counters)")
@@ -938,6 +988,9 @@ def main():
     from selective_state_space_80_amd import workloads as W
 
     mamba.load_library()
+    if args.probe_valu:
+        print(json.dumps(run_probe_valu(torch)), flush=True)
+        return
     if args.copy_calibration_mib:
         # one plain streaming kernel (torch's elementwise multiply) that reads
         # and writes exactly this many bytes with ordinary loads and stores

@@ -15,6 +15,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libmamba_amd.so")
+# VALU issue-rate probe (measurement aid for the roofline; not part of the C ABI)
+PROBE_SOURCE = "valu_probe.hip"
+PROBE_LIBRARY = os.path.join(HERE, "libmamba_probe.so")
 SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bwd.hip", "ssd_fwd.hip", "conv1d_silu.hip", "state_update.hip"]
 ARCH = "gfx950"
 
@@ -52,8 +55,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIBRARY)
+    probe_obj = _compile(PROBE_SOURCE)
+    tmp = PROBE_LIBRARY + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, probe_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIBRARY)
     if verbose:
-        print("built", LIBRARY)
+        print("built", LIBRARY, "and", PROBE_LIBRARY)
     return LIBRARY
 
 

@@ -115,3 +115,13 @@ def test_scan_roofline_is_the_alu_roof_with_hbm_beside_it():
     assert v["wave_instr_per_elem"] == pytest.approx(140.0)
     assert v["frac"] == pytest.approx(140e6 / 0.25e-3 / 614.4e9, abs=1e-4)
     assert v["busy_frac"] == pytest.approx(146e6 / 0.25e-3 / 614.4e9, abs=1e-4)
+
+
+def test_probe_library_exports_its_launch():
+    """The issue-rate probe is built beside the library (build() links it) and
+    exports its one launch function; no GPU call here."""
+    import ctypes
+    if not os.path.exists(bench.PROBE_LIBRARY):
+        pytest.skip("libmamba_probe.so not built")
+    lib = ctypes.CDLL(bench.PROBE_LIBRARY)
+    assert hasattr(lib, "mamba_probe_valu_launch")
