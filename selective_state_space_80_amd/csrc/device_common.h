@@ -52,12 +52,20 @@ __device__ __forceinline__ float silu_hw(float z) {
     return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));
 }
 
-// softplus(v) in log2 units: log2(1 + 2^v2) for v2 = v * log2(e).  Above
-// v2 = 25 the 1 no longer changes 1 + 2^v2 in fp32, so the value is v2 itself;
-// taking it directly also keeps 2^v2 from overflowing to +inf for v2 >= 128.
+// softplus(v) in log2 units: log2(1 + t), t = 2^v2, for v2 = v * log2(e).
+// Above v2 = 25 the 1 no longer changes 1 + t in fp32, so the value is v2
+// itself; taking it directly also keeps t from overflowing to +inf for
+// v2 >= 128.  Below v2 = -6 (t < 1/64) the value is small and
+// v_log_f32(1 + t) would carry its error near 1, an absolute one, which is a
+// large relative error in a small Δ (1.6e-3 in the outputs of a scan with Δ
+// near 1e-5): there it is the series log2(e) (t - t^2/2 + t^3/3), whose
+// truncation stays below 6e-7 relative.
 __device__ __forceinline__ float softplus_log2(float v2) {
-    const float l = hw_log2(1.0f + hw_exp2(v2));
-    return v2 > 25.0f ? v2 : l;
+    const float t = hw_exp2(v2);
+    const float l = hw_log2(1.0f + t);
+    constexpr float c1 = 1.44269504088896341f, c2 = -c1 / 2.f, c3 = c1 / 3.f;
+    const float small = t * fmaf(fmaf(c3, t, c2), t, c1);
+    return v2 > 25.0f ? v2 : (v2 < -6.0f ? small : l);
 }
 
 // Input coefficient of the exact ZOH step for one state, B̄_n / B_n =
