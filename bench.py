@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -29,6 +28,8 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+from selective_state_space_80_amd import profiling  # noqa: E402  (stdlib only)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (packed fp32)
@@ -88,11 +89,10 @@ def traffic_record(key):
         return None
     if not rec or "source" not in rec:
         return None
-    try:
-        sha = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
-    except OSError:
+    path = os.path.join(ROOT, rec["source"])
+    if not os.path.isfile(path):
         return None
-    return rec if rec.get("source_sha256") == sha else None
+    return rec if rec.get("source_digest") == profiling.source_digest(path) else None
 
 
 def traffic_bytes(tr):

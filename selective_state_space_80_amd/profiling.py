@@ -27,6 +27,31 @@ import re
 import sqlite3
 import sys
 
+_LOCAL_INCLUDE = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def source_digest(source):
+    """sha256 over a kernel source and the local headers it includes
+    (``#include "..."`` found beside it, recursively, each once, in the order
+    first met): counters describe the compiled kernel, so a change to a shared
+    device header makes them as stale as a change to the source itself."""
+    h = hashlib.sha256()
+    seen = set()
+
+    def add(path):
+        path = os.path.abspath(path)
+        if path in seen or not os.path.isfile(path):
+            return
+        seen.add(path)
+        text = open(path, "rb").read()
+        h.update(os.path.basename(path).encode() + b"\0" + text + b"\0")
+        for inc in _LOCAL_INCLUDE.findall(text.decode("utf-8", "replace")):
+            add(os.path.join(os.path.dirname(path), inc))
+
+    add(source)
+    return h.hexdigest()
+
+
 COPY_KERNEL = "MulFunctor"  # torch elementwise multiply: reads N bytes, writes N bytes
 
 
@@ -117,7 +142,7 @@ def traffic(fetch_db, write_db, copy_bytes, kernel, source=None, sq_db=None):
     if source:
         out["source"] = os.path.relpath(source, os.path.dirname(os.path.dirname(
             os.path.abspath(__file__))))
-        out["source_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
+        out["source_digest"] = source_digest(source)
     return out
 
 

@@ -2,7 +2,6 @@
 guard, the scaling of rocprofv3 byte counters by the copy calibration, and the
 rule that counter traffic is reported only for the kernel source it was taken
 on."""
-import hashlib
 import json
 import os
 import subprocess
@@ -67,16 +66,34 @@ def test_traffic_is_scaled_by_the_copy_kernel(tmp_path):
     assert rec["fetch_bytes"] == pytest.approx(45000 * 1024 * 2.0)
     assert rec["write_bytes"] == pytest.approx(84000 * 1024 * 1.0)
     assert rec["valu_insts"] == 10240000.0 and rec["waves"] == 40960.0
-    assert rec["source_sha256"] == hashlib.sha256(src.read_bytes()).hexdigest()
+    assert rec["source_digest"] == profiling.source_digest(str(src))
+
+
+def test_source_digest_follows_local_includes(tmp_path):
+    """The digest changes with the source and with a local header it includes,
+    directly or through another header, and not with an unrelated file."""
+    (tmp_path / "k.hip").write_text('#include "a.h"\n#include <hip/hip_runtime.h>\nk\n')
+    (tmp_path / "a.h").write_text('#include "b.h"\na\n')
+    (tmp_path / "b.h").write_text("b\n")
+    (tmp_path / "c.h").write_text("c\n")
+    k = str(tmp_path / "k.hip")
+    d0 = profiling.source_digest(k)
+    (tmp_path / "c.h").write_text("c changed\n")
+    assert profiling.source_digest(k) == d0
+    (tmp_path / "b.h").write_text("b changed\n")
+    d1 = profiling.source_digest(k)
+    assert d1 != d0
+    (tmp_path / "k.hip").write_text('#include "a.h"\n#include <hip/hip_runtime.h>\nk2\n')
+    assert profiling.source_digest(k) != d1
 
 
 def test_traffic_record_only_for_the_current_source(tmp_path, monkeypatch):
     src = os.path.join("selective_state_space_80_amd", "csrc", "state_update.hip")
-    sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    dig = profiling.source_digest(os.path.join(ROOT, src))
     rec = {"kernel": "k", "fetch_bytes": 100.4, "write_bytes": 50.2, "source": src}
     table = tmp_path / "traffic.json"
-    table.write_text(json.dumps({"cur": dict(rec, source_sha256=sha),
-                                 "old": dict(rec, source_sha256="0" * 64),
+    table.write_text(json.dumps({"cur": dict(rec, source_digest=dig),
+                                 "old": dict(rec, source_digest="0" * 64),
                                  "nosrc": {"kernel": "k", "fetch_bytes": 1.0,
                                            "write_bytes": 1.0}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(table))
