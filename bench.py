@@ -289,10 +289,11 @@ def scan_valu_per_elem(io, conv=False):
         skip and scale (2)                                              81
       fix-up: 16 products C_n/(n+1) * carried state, 15 Horner fmas, 2  33
       gate: SiLU(z) (mul, exp2, add, rcp, mul) and the product          6
-      carry: chunk and segment maps, start states (~136 per 32 steps)  4.25
+      carry: chunk and segment maps, start states: about 4.25 map
+        applications per 32 steps, each 16 x (exponent, exp2, fma)      6.375
       bf16 I/O: unpack x, dt, z; pack y                                 3.5
       fused conv1d, 4 taps: 4 fma + SiLU                                9"""
-    n = 81 + 33 + 6 + 4.25
+    n = 81 + 33 + 6 + 6.375
     if io == "bf16":
         n += 3.5
     if conv:

@@ -584,28 +584,27 @@ struct ARow {
     __device__ __forceinline__ float operator[](int n) const { return a[n][lane]; }
 };
 
+// Applies a span's map h <- P h + S to h.  The span's decay is carried as the
+// sum f of its steps' exponents: Σ Δ A_0 / ln2 on the structured path, whose
+// state n decays by P_n = 2^((n+1) f), and Σ Δ / ln2 on the general path,
+// P_n = 2^(A_n f).  One exponential per state keeps each P_n within about an ulp
+// however many steps the span holds; powers of the span's decay, formed by
+// products, would carry n+1 times its rounding into every later segment.
 template <bool STRUCT, typename GetS>
 __device__ __forceinline__ void apply_map(float f, GetS get, const ARow &Ar, float (&h)[kMaxN])
 {
-    float pw = f;
     const float fc = fminf(f, __FLT_MAX__);  // finite: A_n = 0 gives 2^0 = 1
 #pragma unroll
     for (int n = 0; n < kMaxN; ++n) {
-        float P;
-        if constexpr (STRUCT) {
-            P = pw;
-            pw *= f;
-        } else {
-            P = hw_exp2(Ar[n] * fc);
-        }
+        const float P = STRUCT ? hw_exp2(f * (float)(n + 1)) : hw_exp2(Ar[n] * fc);
         h[n] = fmaf(P, h[n], get(n));
     }
 }
 
-template <bool STRUCT>
+// The decay summary of two consecutive spans: exponent sums add.
 __device__ __forceinline__ float combine_summary(float f_early, float f_late)
 {
-    return STRUCT ? f_early * f_late : f_early + f_late;
+    return f_early + f_late;
 }
 
 // The whole per-workgroup body for one arithmetic path.
@@ -824,7 +823,7 @@ __device__ __forceinline__ void scan_segment(
                 er[j] = hw_exp2(cumW);
         }
         if constexpr (STRUCT) {
-            summ = hw_exp2(cumW);  // the chunk's decay (forward: er[kChunkT - 1])
+            summ = cumW;  // the chunk's decay, as its exponent sum
             // back to true units: h_n = ĥ_n / A_n (the adjoint is unscaled)
             if constexpr (!ADJ) {
 #pragma unroll
@@ -875,7 +874,7 @@ __device__ __forceinline__ void scan_segment(
         for (int k = 1; k < kWavesPerSeg; ++k) {
             const float fk = s_agg[k][0][lane];
             apply_map<STRUCT>(fk, [&](int n) { return s_agg[k][1 + n][lane]; }, Ar, Sg);
-            F = combine_summary<STRUCT>(F, fk);
+            F = combine_summary(F, fk);
         }
         // the segment map, for step 5 (slot 0 of s_part; wave 0 keeps its own
         // step-4 partial in registers)
@@ -910,7 +909,7 @@ __device__ __forceinline__ void scan_segment(
     {
         const int64_t per = (depth + kWavesPerSeg - 1) / kWavesPerSeg;
         const int64_t lo = min(depth, (int64_t)w * per), hi = min(depth, lo + per);
-        float pf = STRUCT ? 1.f : 0.f;  // identity map
+        float pf = 0.f;  // identity map
         float ps[kMaxN];
 #pragma unroll
         for (int n = 0; n < kMaxN; ++n)
@@ -926,10 +925,10 @@ __device__ __forceinline__ void scan_segment(
                 v1[k] = load_rec(r1 + k * kWave + lane);
             }
             apply_map<STRUCT>(v0[0], [&](int n) { return v0[1 + n]; }, Ar, ps);
-            pf = combine_summary<STRUCT>(pf, v0[0]);
+            pf = combine_summary(pf, v0[0]);
             if (two) {
                 apply_map<STRUCT>(v1[0], [&](int n) { return v1[1 + n]; }, Ar, ps);
-                pf = combine_summary<STRUCT>(pf, v1[0]);
+                pf = combine_summary(pf, v1[0]);
             }
         }
         if (w != 0) {
