@@ -135,6 +135,20 @@ def test_scan_structured_A_with_small_steps(io):
     say(f"  max rel err {e1:.2e}")
 
 
+def test_scan_structured_A_with_small_steps_long():
+    """The same small steps over 16384 steps (512 chunks, 128 segments): the
+    carry applies every earlier span's decay to each state, so rounding there
+    grows with the length. Powers of a chunk's decay formed by products had
+    put the error at 7.4e-5 by 4096 steps, rising almost linearly."""
+    say("scan structured A, small steps, L = 16384, f32")
+    B, D, L, N = 1, 64, 16384, 16
+    p = W.make_scan_inputs(B, D, L, N, "f32", seed=41)
+    u = np.exp(np.random.default_rng(8).uniform(np.log(1e-5), np.log(1e-4), size=D))
+    p["dt_bias"] = np.log(np.expm1(u)).astype(np.float32)
+    e1, _ = _full_check(p, "f32", _h0(B, D, N, 5))
+    say(f"  max rel err {e1:.2e}")
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_scan_general_A_with_small_steps(io):
     """The general path with step sizes Δ log-uniform in [1e-5, 1e-4] and a
