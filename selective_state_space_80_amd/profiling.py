@@ -109,7 +109,10 @@ def counters(db: str):
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for (did, cn), v in per_dispatch.items():
         acc[short_name(names[did])][cn].append(v)
-    return {k: {cn: sum(v) / len(v) for cn, v in d.items()} for k, d in acc.items()}
+    out = {k: {cn: sum(v) / len(v) for cn, v in d.items()} for k, d in acc.items()}
+    for k, d in acc.items():
+        out[k]["dispatches"] = float(max(len(v) for v in d.values()))
+    return out
 
 
 def _find(d, sub):
@@ -122,6 +125,12 @@ def _find(d, sub):
 def traffic(fetch_db, write_db, copy_bytes, kernel, source=None, sq_db=None):
     f = counters(fetch_db)
     w = counters(write_db)
+    for d in (f, w):
+        # the scale rests on one launch of known size: an average with other
+        # launches of the same kernel would scale by the wrong bytes
+        if _find(d, COPY_KERNEL).get("dispatches", 1.0) != 1.0:
+            raise ValueError("the calibration kernel %s was launched %d times in one pass"
+                             % (COPY_KERNEL, _find(d, COPY_KERNEL)["dispatches"]))
     copy_f = _find(f, COPY_KERNEL)["FETCH_SIZE"] * 1024.0
     copy_w = _find(w, COPY_KERNEL)["WRITE_SIZE"] * 1024.0
     kf = _find(f, kernel)["FETCH_SIZE"] * 1024.0

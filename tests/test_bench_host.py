@@ -51,6 +51,29 @@ def test_counter_text_is_read_back_per_kernel(tmp_path):
     assert k["SQ_INSTS_VALU"] == 10240000.0 and k["SQ_WAVES"] == 40960.0
 
 
+def test_traffic_refuses_a_calibration_kernel_launched_more_than_once(tmp_path):
+    """The counters of a database keep each kernel's dispatch count; a pass in
+    which the calibration kernel ran twice (another multiply beside the one of
+    known size) cannot scale bytes, and the traffic step says so."""
+    import sqlite3
+    db = tmp_path / "run_results.db"
+    con = sqlite3.connect(str(db))
+    con.execute("create table counters_collection (dispatch_id, kernel_name, counter_name, value)")
+    rows = [(1, "void at::native::elementwise<MulFunctor<float>>(int)", "FETCH_SIZE", 262144.0),
+            (2, "void at::native::elementwise<MulFunctor<float>>(int)", "FETCH_SIZE", 20000.0),
+            (3, "mamba::foo_kernel(int)", "FETCH_SIZE", 1000.0),
+            (3, "mamba::foo_kernel(int)", "FETCH_SIZE", 500.0)]  # two XCD rows: summed
+    con.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    d = profiling.counters(str(db))
+    assert d["calibration_MulFunctor"]["dispatches"] == 2.0
+    assert d["calibration_MulFunctor"]["FETCH_SIZE"] == pytest.approx(141072.0)
+    assert d["foo_kernel"] == {"FETCH_SIZE": 1500.0, "dispatches": 1.0}
+    with pytest.raises(ValueError, match="launched 2 times"):
+        profiling.traffic(str(db), str(db), 512 << 20, "foo_kernel")
+
+
 def test_traffic_is_scaled_by_the_copy_kernel(tmp_path):
     """A copy of 512 MiB that the counters see as 256 MiB fetched and 512 MiB
     written gives scales 2 and 1; the kernel's KiB are scaled alike, and the
