@@ -284,16 +284,17 @@ def scan_valu_per_elem(io, conv=False):
     register moves or waits.  A transcendental counts one instruction.
       chunk scan per step: Δ = softplus (fma, exp2, add, log2; the series
         near 0: fma, fma, mul; two compares, two selects: 11), the step decay
-        (mul, exp2: 2), e - 1 (1), 16 states x 3 minus the first power (47),
-        readout (16), cumulative decay (add to the exponent sum, exp2: 2),
-        skip and scale (2)                                              81
+        (mul, exp2: 2), e and e - 1 (the subtraction; the series near 0: fma,
+        fma, mul, compare, add, two selects: 8), 16 states x 3 minus the first
+        power (47), readout (16), cumulative decay (add to the exponent sum,
+        exp2: 2), skip and scale (2)                                     88
       fix-up: 16 products C_n/(n+1) * carried state, 15 Horner fmas, 2  33
       gate: SiLU(z) (mul, exp2, add, rcp, mul) and the product          6
       carry: chunk and segment maps, start states: about 4.25 map
         applications per 32 steps, each 16 x (exponent, exp2, fma)      6.375
       bf16 I/O: unpack x, dt, z; pack y                                 3.5
       fused conv1d, 4 taps: 4 fma + SiLU                                9"""
-    n = 81 + 33 + 6 + 6.375
+    n = 88 + 33 + 6 + 6.375
     if io == "bf16":
         n += 3.5
     if conv:

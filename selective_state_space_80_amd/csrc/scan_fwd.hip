@@ -577,6 +577,24 @@ __device__ __forceinline__ void lds_row(const float *row, float (&v)[kMaxN])
 //   structured: f = prod of e over the chunk, P_n = f^(n+1)
 //   general:    f = sum over the chunk of Δ/ln2, P_n = 2^(A_n f)   (A_n = 0 -> 1)
 // S_n is read through `get(n)` so it can come from registers, LDS or a record.
+// e = 2^w and e - 1 for a structured step's decay exponent w = Δ A_0 / ln2.
+// Near w = 0 the exponential carries about an ulp of 1, which in e - 1 formed
+// by subtraction is a relative error of ~6e-8 / |w ln2|; every state's
+// increment (e_n - 1)(ĥ + B x) inherits it, and along a sequence of small steps
+// it accumulates in the state.  So for |w ln2| < 1/64, e - 1 is the series
+// u + u^2/2 + u^3/6 (u = w ln2; truncation below 2e-7 relative) and e = 1 + that,
+// rounded once; beyond, e is the exponential and e - 1 its subtraction.
+__device__ __forceinline__ void step_decay(float w, float &e, float &em1)
+{
+    constexpr float c1 = 0.693147180559945309f;  // ln 2
+    constexpr float c2 = c1 * c1 / 2.f, c3 = c1 * c1 * c1 / 6.f;
+    const float x = hw_exp2(w);
+    const float sr = w * fmaf(fmaf(c3, w, c2), w, c1);
+    const bool small = fabsf(w) < (1.f / 64.f) * 1.44269504088896341f;
+    em1 = small ? sr : x - 1.f;
+    e = small ? 1.f + sr : x;
+}
+
 // One channel's row of A held in LDS ([n][lane] layout): Ar[n].
 struct ARow {
     const float (*a)[kWave];
@@ -743,8 +761,7 @@ __device__ __forceinline__ void scan_segment(
             // exponent w = Δ A_0 / ln2 kept in er[j]
             float ej = 0.f, emj = 0.f;
             if constexpr (STRUCT) {
-                ej = hw_exp2(er[j]);
-                emj = ej - 1.f;
+                step_decay(er[j], ej, emj);
                 cumW += er[j];
             }
             if (j < nt) {  // one basic block per step

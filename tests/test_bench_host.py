@@ -138,17 +138,17 @@ def test_valu_peak_is_one_wave64_instruction_per_clock_per_cu():
 
 def test_scan_roofline_is_the_alu_roof_with_hbm_beside_it():
     # design count per element: fp32 plain, bf16, fp32 with the fused conv
-    assert bench.scan_valu_per_elem("f32") == pytest.approx(126.375)
-    assert bench.scan_valu_per_elem("bf16") == pytest.approx(129.875)
-    assert bench.scan_valu_per_elem("f32", conv=True) == pytest.approx(135.375)
+    assert bench.scan_valu_per_elem("f32") == pytest.approx(133.375)
+    assert bench.scan_valu_per_elem("bf16") == pytest.approx(136.875)
+    assert bench.scan_valu_per_elem("f32", conv=True) == pytest.approx(142.375)
     elems, ms, nbytes = 64 * 1000 * 1000, 0.25, 8 * 64 * 10 ** 6
     tr = {"fetch_bytes": 600.0e6, "write_bytes": 200.0e6, "valu_insts": 140.0e6,
           "valu_active": 146.0e6}
     r = bench.scan_roofline("k", "bf16", False, elems, ms, nbytes, tr)
     assert r["bound"] == "alu"
-    # 129.875 instructions per element x 1e6 wave-steps in 0.25 ms
-    assert r["achieved"] == pytest.approx(129.875e6 / 0.25e-3 / 1e9, rel=1e-3)
-    assert r["frac"] == pytest.approx(129.875e6 / 0.25e-3 / 614.4e9, abs=1e-4)
+    # 136.875 instructions per element x 1e6 wave-steps in 0.25 ms
+    assert r["achieved"] == pytest.approx(136.875e6 / 0.25e-3 / 1e9, rel=1e-3)
+    assert r["frac"] == pytest.approx(136.875e6 / 0.25e-3 / 614.4e9, abs=1e-4)
     assert r["traffic"] == 800000000
     assert r["hbm"]["frac"] == pytest.approx(nbytes / 0.25e-3 / 8e12, abs=1e-4)
     v = bench.valu_record(tr, elems, ms)
