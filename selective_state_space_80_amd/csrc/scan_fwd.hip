@@ -833,9 +833,9 @@ __device__ __forceinline__ void scan_segment(
             // the chunk's start (a padding step adds 0 to the exponent).  It is
             // 2^(Σ w), not a product of the steps' decays: those sit within a
             // few ulp of 1 when Δ A_0 is small, and a product of many of them,
-            // raised to the power n+1 by the fix-up and the chunk maps, loses
-            // about (n+1) ulp per step (1.4e-3 in the outputs of a 4096-step fp32
-            // scan with Δ near 1e-5 and an initial state, against 7e-5 now)
+            // raised to the power n+1 by the fix-up, loses about (n+1) ulp per
+            // step (the products had put the outputs of a 4096-step fp32 scan
+            // with Δ near 1e-5 and an initial state 1.4e-3 off)
             if constexpr (STRUCT && !ADJ)
                 er[j] = hw_exp2(cumW);
         }
