@@ -161,6 +161,38 @@ def test_decode_steps_equal_scan():
     assert_within(host(h), host(h_scan), 5e-5, "decode vs scan state")
 
 
+@pytest.mark.parametrize("A_kind", ["structured", "general"])
+def test_decode_small_steps_1024(A_kind):
+    """1024 decode steps with step sizes Δ log-uniform in [1e-5, 1e-4] from a
+    given state, which then barely decays: any rounding of a small Δ (the
+    softplus near 0) or of a decay within an ulp of 1 accumulates in the state.
+    y is compared at every step and h at the end, fp32 I/O."""
+    import selective_state_space_80_amd as mamba
+    say(f"decode small steps, 1024 steps, A={A_kind}")
+    B, D, L, N = 2, 128, 1024, 16
+    p = W.make_scan_inputs(B, D, L, N, "f32", seed=43)
+    rng = np.random.default_rng(9)
+    u = np.exp(rng.uniform(np.log(1e-5), np.log(1e-4), size=D))
+    p["dt_bias"] = np.log(np.expm1(u)).astype(np.float32)
+    if A_kind == "general":
+        p["A"] = -rng.uniform(0.05, 8.0, size=(D, N)).astype(np.float32)
+    h0 = rng.standard_normal((B, D, N)).astype(np.float32)
+    h = dev(h0)
+    h_or = h0.astype(np.float64)
+    worst = 0.0
+    for t in range(L):
+        y = mamba.selective_state_update(
+            h, dev(p["x"][:, :, t]), dev(p["dt"][:, :, t]), dev(p["A"]),
+            dev(p["Bm"][:, t]), dev(p["Cm"][:, t]), dt_bias=dev(p["dt_bias"]),
+            Dskip=dev(p["Dskip"]), z=dev(p["z"][:, :, t]))
+        yo, h_or = oracle.state_update(h_or, p["x"][:, :, t], p["dt"][:, :, t], p["A"],
+                                       p["Bm"][:, t], p["Cm"][:, t], dt_bias=p["dt_bias"],
+                                       Dskip=p["Dskip"], z=p["z"][:, :, t])
+        worst = max(worst, assert_within(host(y), yo, TOL["f32"], f"decode y step {t}"))
+    eh = assert_within(host(h), h_or, STATE_TOL, "decode h after 1024 steps")
+    say(f"  max rel err y {worst:.2e}, h {eh:.2e}")
+
+
 def test_decode_workload_1024_steps():
     """Decode workload: 1024 steps on the [256, 5120, 16] fp32 state with fresh
     bf16 tokens; every 128 steps, every output and every state element is
